@@ -1,0 +1,203 @@
+"""Oracle building blocks: plain float64 definitions of each operation in the step.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The GPU path
+never calls it, and it shares no code with the GPU path.
+
+Each function is written from the definition the source pages give (or the
+textbook definition where the pages name the operation without spelling it
+out) and computes in float64 unless told otherwise. Rounding to a storage
+type happens only where the caller says the method stores a value.
+
+Page key used in citations:
+  [Serving Efficiency]  "Chapter 31 Serving Efficiency: Reuse, Kernels,
+                        Speculation, and Batching" (imbrooklyn.dev)
+  [Spending the Idle]   "Spending the Idle" (derivingsystems.com)
+  [Serving]             "Serving" (pradyotprakash.com, inference-serving)
+  [KV Cache]            "Inference at Scale: KV Cache, Prefill, and Decode"
+                        (blog.truongducdung.dev)
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+F64 = torch.float64
+
+_STORAGE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def storage_dtype(dt: str) -> torch.dtype:
+    return _STORAGE[dt]
+
+
+def round_to(x: torch.Tensor, dt: str) -> torch.Tensor:
+    """Round float64 values to a storage type (round to nearest even) and back to float64.
+
+    This is where the method stores a value in fp32 / fp16 / bf16; everything
+    between two such points is carried in float64.
+    """
+    return x.to(_STORAGE[dt]).to(F64)
+
+
+def linear(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """y = x W^T for a weight stored row-major as [out][in] (float64 product).
+
+    [KV Cache] section 02 ("Counting FLOPs and counting bytes"): every matrix
+    multiply reads the full weight once and uses it for every row passing
+    through; the rows share the read. The product itself is the library matmul.
+    """
+    return x.to(F64) @ w.to(F64).T
+
+
+def rmsnorm(x: torch.Tensor, gain: torch.Tensor, eps: float) -> torch.Tensor:
+    """Root-mean-square normalisation of the last axis, times a per-feature gain.
+
+    The pages name RMSNorm as a fused step of the decode path without
+    writing it out; this is the textbook definition
+    y_i = x_i / sqrt(mean_j(x_j^2) + eps) * g_i.
+    """
+    x = x.to(F64)
+    ms = (x * x).mean(dim=-1, keepdim=True)
+    return x / torch.sqrt(ms + eps) * gain.to(F64)
+
+
+def rope_angles(positions: torch.Tensor, head_dim: int, theta: float) -> torch.Tensor:
+    """Rotary angles pos * theta^(-2i/head_dim) for i in [0, head_dim/2), float64.
+
+    The pages name RoPE (fused with RMSNorm on the decode path, and as the
+    positional encoding MLA has to carry separately in [KV Cache] section 04)
+    without writing it out; this is the rotary definition with base theta.
+    """
+    half = head_dim // 2
+    i = torch.arange(half, dtype=F64)
+    inv_freq = theta ** (-2.0 * i / head_dim)
+    return positions.to(F64).unsqueeze(-1) * inv_freq
+
+
+def rope(x: torch.Tensor, positions: torch.Tensor, theta: float) -> torch.Tensor:
+    """Rotate pairs (x_i, x_{i+d/2}) of each head vector by the angle of its position.
+
+    x: [..., n_heads, head_dim] with the leading axes matching `positions`
+    (one position per row). Pairing is "rotate half": feature i is paired with
+    feature i + head_dim/2.
+    """
+    x = x.to(F64)
+    d = x.shape[-1]
+    half = d // 2
+    ang = rope_angles(positions, d, theta)  # [..., half]
+    cos = torch.cos(ang).unsqueeze(-2)  # broadcast over heads
+    sin = torch.sin(ang).unsqueeze(-2)
+    a, b = x[..., :half], x[..., half:]
+    return torch.cat([a * cos - b * sin, b * cos + a * sin], dim=-1)
+
+
+def attention_standard(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.Tensor | None = None,
+                       scale: float | None = None) -> torch.Tensor:
+    """softmax(q k^T * scale) v with the full score matrix materialised.
+
+    [KV Cache] section 07 ("Online softmax" and the standard attention it is
+    compared with): scores for every (query, key) pair are formed, masked
+    positions (a later key for a causal query) are set to -inf, and the
+    numerically stable softmax takes the row maximum first and then the sum of
+    exp(s - max). scale defaults to 1/sqrt(head_dim).
+
+    q: [..., n_q, d]; k, v: [..., n_k, d]; mask: bool [n_q, n_k], True = keep.
+    Computes in the dtype of its inputs (the step passes float64; the pages'
+    own comparison runs the same function in fp32 and fp64).
+    """
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    s = (q @ k.transpose(-1, -2)) * scale
+    if mask is not None:
+        s = s.masked_fill(~mask, float("-inf"))
+    m = s.amax(dim=-1, keepdim=True)
+    p = torch.exp(s - m)
+    return (p / p.sum(dim=-1, keepdim=True)) @ v
+
+
+def attention_online(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int, mask: torch.Tensor | None = None,
+                     scale: float | None = None) -> torch.Tensor:
+    """The same function computed block by block over the keys.
+
+    [KV Cache] section 07: walk K and V in blocks; for each block form its
+    scores, raise the running maximum m to m', rescale the running sum l and
+    output O by exp(m - m'), add exp(S - m') and its product with V_j, and
+    divide O by l at the end. Works in the dtype of q (the pages run it in fp32
+    and in fp64 to show both agree to rounding).
+    """
+    dt = q.dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    n_q, n_k = q.shape[-2], k.shape[-2]
+    m = torch.full(q.shape[:-1] + (1,), float("-inf"), dtype=dt)
+    l = torch.zeros(q.shape[:-1] + (1,), dtype=dt)
+    o = torch.zeros(q.shape[:-1] + (v.shape[-1],), dtype=dt)
+    for j in range(0, n_k, block):
+        kj, vj = k[..., j:j + block, :], v[..., j:j + block, :]
+        s = (q @ kj.transpose(-1, -2)) * scale
+        if mask is not None:
+            s = s.masked_fill(~mask[:, j:j + block], float("-inf"))
+        m_new = torch.maximum(m, s.amax(dim=-1, keepdim=True))
+        # a row whose keys in this block and before are all masked keeps m = -inf;
+        # exp(-inf - -inf) would be NaN, so those rows contribute nothing yet
+        safe = torch.where(torch.isinf(m_new), torch.zeros_like(m_new), m_new)
+        p = torch.exp(s - safe)
+        alpha = torch.exp(m - safe)
+        l = l * alpha + p.sum(dim=-1, keepdim=True)
+        o = o * alpha + p @ vj
+        m = m_new
+    return o / l
+
+
+def combine_partials(nums: torch.Tensor, dens: torch.Tensor, maxes: torch.Tensor | None = None) -> torch.Tensor:
+    """Merge per-tile softmax statistics into one normalised output.
+
+    [Serving Efficiency] section 31.4, Example 31.2: tiles are combined by
+    adding their numerators and their denominators, (sum num) / (sum den), not
+    by averaging the tiles' normalised outputs. With running maxima (the
+    Flash-Decoding merge of [KV Cache] section 07: each split stores its
+    log-sum-exp and the splits are merged with the online-softmax rescaling),
+    tile t's numerator and denominator were computed relative to exp(-m_t) and
+    are first brought to the common scale exp(-max_t m_t).
+
+    nums: [T, ...d]; dens: [T]; maxes: [T] or None.
+    """
+    nums, dens = nums.to(F64), dens.to(F64)
+    if maxes is not None:
+        maxes = maxes.to(F64)
+        mstar = maxes.max()
+        w = torch.exp(maxes - mstar)
+        nums = nums * w.reshape((-1,) + (1,) * (nums.dim() - 1))
+        dens = dens * w
+    return nums.sum(dim=0) / dens.sum(dim=0)
+
+
+def silu(x: torch.Tensor) -> torch.Tensor:
+    """x * sigmoid(x) = x / (1 + exp(-x)), float64."""
+    x = x.to(F64)
+    return x / (1.0 + torch.exp(-x))
+
+
+def swiglu(gate: torch.Tensor, up: torch.Tensor) -> torch.Tensor:
+    """Gated feed-forward activation silu(gate) * up (the SwiGLU MLP of a 7B Llama-style model)."""
+    return silu(gate) * up.to(F64)
+
+
+def argmax_lowest(logits: torch.Tensor) -> tuple[int, float]:
+    """Greedy token: index of the largest value, the lowest index on exact ties; and the
+    gap between the largest and the second-largest value (0 on a tie).
+
+    [KV Cache] section 08: with greedy decoding the verifier compares each
+    draft with the target's argmax. The gap is what decides whether a
+    reduction-order difference can flip that argmax (section 08's note on
+    near-ties between the top two tokens).
+    """
+    v = logits.to(F64).reshape(-1)
+    top = v.max()
+    idx = int(torch.nonzero(v == top)[0, 0])
+    if v.numel() < 2:
+        return idx, float("inf")
+    two = torch.topk(v, 2).values
+    return idx, float(two[0] - two[1])
