@@ -1,0 +1,300 @@
+"""Benchmark: 7B-shaped greedy decode at batch 1 on one MI355X.
+
+Workload: 32 layers, d_model 4096, 32 heads x 128 (MHA), SwiGLU 11008,
+vocab 32000, RMSNorm + RoPE, fp16 random-init weights N(0, 0.02) (13.2 GB
+streamed per step), one sequence whose 2048-token synthetic context sits in
+16-token pages scattered through the pool, K = 1, each step's input token is
+the previous step's argmax. One "step" is one decode_step over the whole
+path (embedding, 32 layers, LM head, argmax) plus the host's per-step page
+bookkeeping (kv_append) and the on-device token / length update.
+
+Prints one JSON line. `value` is decode tokens/s over the timed steps;
+`roofline` reports the gate/up product (the kernel that streams the most
+weight bytes) against the 8 TB/s HBM peak; `cpu_baseline` times the CPU
+oracle on one step of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s + achieved HBM TB/s vs peak, 7B-shaped, B=1..64, K=1/5"
+HBM_PEAK_GBPS = 8000.0
+CTX0 = 2048
+SEED_W, SEED_KV, SEED_TOK, SEED_PAGES = 2001, 2002, 2003, 2006
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles through libamdhip64 (for the per-kernel timer)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.start = (ctypes.c_void_p * n)()
+        self.stop = (ctypes.c_void_p * n)()
+        for i in range(n):
+            for arr in (self.start, self.stop):
+                e = ctypes.c_void_p()
+                assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+                arr[i] = e
+        self.n = n
+
+    def elapsed_ms(self, i):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.stop[i])
+        assert rc == 0, rc
+        return ms.value
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.start[i])
+            self.hip.hipEventDestroy(self.stop[i])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly instead of replaying a graph")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the step is one GPU's share; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import verify_step_amd as vs
+    from harness import GpuModel, GpuPool, SeqSpec, make_step
+    from synth import workloads as W
+    from verify_step_amd import build as vsbuild
+
+    if not os.path.exists(vs.LIB_PATH):
+        vsbuild.build()
+    vs.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    dims = W.LLAMA7B  # fp16
+    K, Wm = args.steps, args.warmup
+    total_len = CTX0 + Wm + K + 1
+
+    # ---- weights (generated on the host, one tensor at a time) ----
+    t0 = time.time()
+    keep_cpu = not args.no_cpu_baseline
+    w_cpu = {"layers": [dict() for _ in range(dims.n_layers)]} if keep_cpu else None
+
+    def items():
+        for name, layer, t in W.iter_weights(dims, SEED_W):
+            if keep_cpu:
+                (w_cpu if layer < 0 else w_cpu["layers"][layer])[name] = t
+            yield name, layer, t
+
+    model = GpuModel.__new__(GpuModel)
+    _load_model(model, dims, items(), dev)
+    log(f"weights ready in {time.time() - t0:.1f}s")
+
+    # ---- pool, scattered pages, synthetic 2048-token context ----
+    n_pages = -(-total_len // 16) + 8
+    pool = GpuPool(dims, n_pages)
+    ids = vs.kv_alloc(pool.handle, n_pages)
+    perm = synth.permutation(synth.key(SEED_PAGES), n_pages)
+    vs.kv_free(pool.handle, [ids[int(i)] for i in perm])
+    row = vs.kv_alloc(pool.handle, -(-CTX0 // 16))
+    kv0 = W.kv_block(dims, SEED_KV, 0, 0, CTX0)
+    pool.write(row, 0, kv0)
+    tok0 = W.token_ids(SEED_TOK, 0, 1, dims.vocab)
+    max_blocks = -(-total_len // 16)
+    row = vs.kv_append(pool.handle, row, max_blocks, CTX0, 1)
+    sb = make_step(model, pool, [SeqSpec(CTX0, tok0)], [row], max_blocks=max_blocks, want_logits_tensor=False)
+    # the graph is built for the longest context the run reaches
+    sb.desc.max_ctx = total_len
+    sb.ws_bytes = vs.decode_step_workspace_bytes(sb.desc, __import__("harness").model_desc(dims))
+    sb.ws = torch.empty(sb.ws_bytes, dtype=torch.uint8, device=dev)
+    bt_host = torch.zeros(max_blocks, dtype=torch.int32).pin_memory()
+    bt_host[:len(row)] = torch.tensor(row, dtype=torch.int32)
+    sb.block_tables[0].copy_(bt_host)
+    torch.cuda.synchronize()
+    log(f"context ready: {CTX0} tokens in {len(row)} pages, pool {n_pages} pages")
+
+    state = {"row": row, "len": CTX0}  # host view: positions [0, len) hold K/V after the step
+
+    def device_step():
+        vs.decode_step(sb.desc, sb.block_tables, model.w, sb.out, sb.ws, sb.ws_bytes,
+                       torch.cuda.current_stream().cuda_stream)
+        sb.tokens.copy_(sb.argmax[:1])
+        sb.ctx_len.add_(1)
+
+    def host_bookkeeping():
+        # the step about to run writes position len + 1's K/V next time; make room for it
+        cur = state["len"] + 1
+        r = vs.kv_append(pool.handle, state["row"], max_blocks, cur, 1)
+        if len(r) != len(state["row"]):
+            bt_host[len(r) - 1] = r[-1]
+            sb.block_tables[0, len(r) - 1:len(r)].copy_(bt_host[len(r) - 1:len(r)], non_blocking=True)
+        state["row"], state["len"] = r, cur
+
+    graph = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            device_step()  # one eager step before capture (position 2048)
+            host_bookkeeping()
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            device_step()
+        Wm_left = Wm - 1
+    else:
+        Wm_left = Wm
+
+    def one():
+        if graph is not None:
+            graph.replay()
+        else:
+            device_step()
+        host_bookkeeping()
+
+    for _ in range(Wm_left):
+        one()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tw0 = time.perf_counter()
+    ev0.record()
+    for _ in range(K):
+        one()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - tw0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / K
+    log(f"timed {K} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / K:.3f} ms/step)")
+
+    # ---- dominant kernel: gate/up product, timed launch by launch with HIP events ----
+    n_tk = 2 * dims.n_layers
+    ev = HipEvents(n_tk)
+    vs.vs_time_kernel(vs.VS_KERNEL["gateup"], ev.start, ev.stop, n_tk)
+    for _ in range(2):
+        device_step()
+        host_bookkeeping()
+    torch.cuda.synchronize()
+    n_done = vs.vs_timed_launches()
+    vs.vs_time_kernel(0, None, None, 0)
+    durs = [ev.elapsed_ms(i) for i in range(n_done)]
+    ev.close()
+    gu_ms = sum(durs) / len(durs)
+    gu_bytes = 2 * dims.ffn * dims.d_model * dims.elem_bytes  # W_gate + W_up, read once per launch
+    gu_gbps = gu_bytes / (gu_ms * 1e-3) / 1e9
+
+    # ---- byte accounting for the whole step ----
+    import oracle  # byte counts only (the step is not run here)
+
+    wbytes = oracle.streamed_weight_bytes(dims)
+    kvpt = oracle.kv_bytes_per_token(dims.n_layers, dims.n_kv_heads, dims.head_dim, dims.elem_bytes)
+    first = CTX0 + Wm + 1  # keys read by the first timed step
+    avg_keys = first + (K - 1) / 2.0
+    step_bytes = wbytes + avg_keys * kvpt + kvpt
+    result = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_step, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "7B-shaped greedy decode, B=1, K=1, fp16 weights+KV, context 2048 grown one token per step, "
+                        "16-token pages scattered in the pool",
+            "model_shape": dims.name,
+            "batch": 1,
+            "rows_per_seq": 1,
+            "ctx_first_timed_step": first - 1,
+            "graph_replay": graph is not None,
+        },
+        "hbm": {
+            "weight_bytes_per_step": wbytes,
+            "kv_bytes_per_step_avg": int(avg_keys * kvpt + kvpt),
+            "step_TBps": round(step_bytes / (ms_step * 1e-3) / 1e12, 4),
+            "step_frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "wall_ms_per_step": round(wall * 1e3 / K, 4),
+        },
+        "roofline": {
+            "kernel": "gate/up product + SwiGLU (gemm_skinny_kernel, EPI_SWIGLU)",
+            "bound": "hbm",
+            "achieved": round(gu_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": gu_bytes,
+            "avg_launch_us": round(gu_ms * 1e3, 3),
+            "launches_timed": n_done,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(dims, w_cpu, kv0, tok0)
+    print(json.dumps(result), flush=True)
+
+
+def _load_model(model, dims, items, dev):
+    """GpuModel built from a (name, layer, cpu tensor) stream."""
+    import torch
+
+    import verify_step_amd as vs
+    from harness import model_desc
+
+    model.dims = dims
+    model.t = {}
+    model.layer_structs = (vs.vs_layer_weights * dims.n_layers)()
+    for name, layer, cpu in items:
+        d = cpu.to(dev)
+        model.t[(name, layer)] = d
+        if layer >= 0:
+            setattr(model.layer_structs[layer], name, d.data_ptr())
+    model.w = vs.vs_weights(model_desc(dims), model.t[("embed", -1)].data_ptr(),
+                            model.t[("final_norm", -1)].data_ptr(), model.t[("lm_head", -1)].data_ptr(),
+                            ctypes.cast(model.layer_structs, ctypes.POINTER(vs.vs_layer_weights)))
+    torch.cuda.synchronize()
+
+
+def cpu_baseline(dims, w_cpu, kv0, tok0):
+    """The oracle, as it stands, on one step of the same workload (B=1, 2048-token context)."""
+    import torch
+
+    import oracle
+
+    log("cpu baseline: one oracle step of the same workload")
+    full = torch.zeros(dims.n_layers, 2, CTX0 + 1, dims.n_kv_heads, dims.head_dim, dtype=dims.torch_dtype)
+    full[:, :, :CTX0] = kv0
+    st = oracle.SeqState(full, CTX0, list(tok0))
+    t0 = time.perf_counter()
+    oracle.decode_step(dims, w_cpu, [st])
+    dt = time.perf_counter() - t0
+    return {"value": round(1.0 / dt, 5), "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"1 decode step, B=1, context {CTX0}, 7B shape fp16 (float64 PyTorch CPU oracle), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

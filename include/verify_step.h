@@ -1,0 +1,250 @@
+/*
+ * verify_step -- one batched, paged decode / speculative-verify step of a
+ * Llama-style decoder on an AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Plain pointers and sizes only. Device pointers are HIP device
+ * addresses on the current device; host pointers are ordinary process memory.
+ * Every call returns a vs_status; on failure vs_last_error() gives a message
+ * (thread-local, valid until the next call on the same thread). No C++
+ * exception crosses this interface.
+ *
+ * Sources (page titles; section numbers as printed on each page):
+ *   [Serving Efficiency] "Chapter 31 Serving Efficiency: Reuse, Kernels,
+ *                        Speculation, and Batching"
+ *   [Spending the Idle]  "Spending the Idle"
+ *   [Serving]            "Serving"
+ *   [KV Cache]           "Inference at Scale: KV Cache, Prefill, and Decode"
+ *
+ * Ownership. The caller owns every device buffer: the KV pool's memory, the
+ * weights, the batch arrays, the outputs and the workspace. The library owns
+ * only host-side pool metadata. Nothing on the step path allocates device
+ * memory, synchronises the device, or issues a memset, so decode_step and
+ * verify_accept may be captured into a HIP graph.
+ *
+ * Asynchrony. decode_step, verify_accept and the copy that kv_append may
+ * enqueue are asynchronous on the stream passed in; their inputs must stay
+ * valid until the stream reaches them. Argument errors are reported before
+ * anything is enqueued. A device fault surfaces as VS_ERR_HIP at a later
+ * checked call. The pool calls are not thread-safe (one scheduler thread).
+ */
+#ifndef VERIFY_STEP_H
+#define VERIFY_STEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t vs_status;
+#define VS_OK 0
+#define VS_ERR_INVALID (-1) /* bad argument, or a pool operation that would break its invariants */
+#define VS_ERR_OOM (-2)     /* the pool has too few free pages; state unchanged */
+#define VS_ERR_SHAPE (-3)   /* sizes the kernels do not support, or a workspace that is too small */
+#define VS_ERR_HIP (-4)     /* a HIP runtime call failed */
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* vs_last_error(void);
+
+/* Storage type of weights and KV cache. Arithmetic is fp32 throughout. */
+#define VS_F32 0
+#define VS_F16 1
+#define VS_BF16 2
+
+/* ------------------------------------------------------------------ model */
+
+/* A pre-norm decoder layer stack ([KV Cache] section 03: the 7B shape is
+ * Llama 2 7B's, multi-head attention with as many KV heads as query heads):
+ * RMSNorm, rotary q/k, causal softmax attention scaled by 1/sqrt(head_dim),
+ * output projection + residual, RMSNorm, SwiGLU MLP + residual; final RMSNorm
+ * and an untied LM head. */
+typedef struct vs_model_desc {
+    int32_t d_model;    /* = n_heads * head_dim */
+    int32_t n_heads;
+    int32_t n_kv_heads; /* divides n_heads (equal for multi-head attention) */
+    int32_t head_dim;   /* 64 or 128 */
+    int32_t ffn;        /* MLP hidden width */
+    int32_t vocab;
+    int32_t n_layers;
+    int32_t dtype;      /* VS_F32, VS_F16 or VS_BF16 */
+    float rope_theta;   /* rotary base, e.g. 10000 */
+    float eps;          /* RMSNorm epsilon, e.g. 1e-5 */
+} vs_model_desc;
+
+/* Device pointers to one layer's weights, all in the model dtype. Matrices are
+ * row-major [out][in] (a product reads row n to make output feature n). */
+typedef struct vs_layer_weights {
+    const void* attn_norm; /* [d_model] */
+    const void* wq;        /* [n_heads*head_dim][d_model] */
+    const void* wk;        /* [n_kv_heads*head_dim][d_model] */
+    const void* wv;        /* [n_kv_heads*head_dim][d_model] */
+    const void* wo;        /* [d_model][n_heads*head_dim] */
+    const void* ffn_norm;  /* [d_model] */
+    const void* wg;        /* [ffn][d_model] gate */
+    const void* wu;        /* [ffn][d_model] up */
+    const void* wd;        /* [d_model][ffn] down */
+} vs_layer_weights;
+
+typedef struct vs_weights {
+    vs_model_desc dims;
+    const void* embed;              /* device [vocab][d_model] */
+    const void* final_norm;         /* device [d_model] */
+    const void* lm_head;            /* device [vocab][d_model] */
+    const vs_layer_weights* layers; /* HOST array of n_layers entries (device pointers inside) */
+} vs_weights;
+
+/* ------------------------------------------------------------------ KV pool */
+
+/* Paged KV cache ([KV Cache] section 05 "The block table"): fixed blocks of
+ * page_tokens token slots; a per-sequence block table maps logical block i
+ * (positions [16i, 16i+16)) to a physical page anywhere in the pool.
+ *
+ * Page layout in device memory (one page holds every layer):
+ *   page p, layer l, K (0) or V (1), KV head h, slot s, dim e at element
+ *   ((((p*n_layers + l)*2 + kv)*n_kv_heads + h)*page_tokens + s)*head_dim + e
+ * so one (page, layer, K|V, head) block of page_tokens*head_dim values is
+ * contiguous (4 KiB for 16 x 128 fp16). */
+typedef struct vs_pool_desc {
+    int32_t num_pages;
+    int32_t page_tokens; /* 16 */
+    int32_t n_layers;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t dtype;
+} vs_pool_desc;
+
+typedef struct vs_pool vs_pool;
+
+/* Bytes of one page for this geometry. */
+size_t kv_page_bytes(const vs_pool_desc* desc);
+
+/* Create a pool over caller-owned device memory of at least
+ * num_pages * kv_page_bytes bytes (the region left after the weights,
+ * [KV Cache] section 03 "The memory budget of a GPU"). Every page starts free.
+ * kv_pool_destroy frees the host metadata only. */
+vs_status kv_pool_create(const vs_pool_desc* desc, void* dev_base, size_t dev_bytes, vs_pool** out);
+void kv_pool_destroy(vs_pool* pool);
+
+/* Take n free pages, all or nothing; each gets reference count 1. Writes the
+ * page ids to out_ids (host, n entries). VS_ERR_OOM leaves the pool unchanged. */
+vs_status kv_alloc(vs_pool* pool, int32_t n, int32_t* out_ids);
+
+/* Add one reference to each listed page (a fork, or a prefix shared between
+ * requests: [KV Cache] section 05 "Block sharing and copy-on-write").
+ * Every page must be in use; otherwise VS_ERR_INVALID and nothing changes. */
+vs_status kv_share(vs_pool* pool, const int32_t* ids, int32_t n);
+
+/* Drop one reference from each listed page (a page listed twice loses two);
+ * a page returns to the free list at zero. Dropping a reference that does not
+ * exist is VS_ERR_INVALID and nothing changes. */
+vs_status kv_free(vs_pool* pool, const int32_t* ids, int32_t n);
+
+/* Make room for positions [cur_len, cur_len + n_new) of one sequence.
+ * bt_row (host, capacity max_blocks) holds *n_blocks page ids, which must equal
+ * ceil(cur_len / page_tokens). A new page is taken only when the last one is
+ * full ([KV Cache] section 05). If the last page is partly filled and shared
+ * (reference count > 1), the sequence first gets a private copy of it:
+ * a fresh page is taken, one page-sized device copy is enqueued on `stream`,
+ * the shared page loses this sequence's reference and bt_row is rewritten
+ * (copy-on-write at block granularity, [KV Cache] section 05; [Serving
+ * Efficiency] section 31.3). All or nothing: VS_ERR_OOM leaves everything
+ * unchanged. *n_blocks is updated on success. */
+vs_status kv_append(vs_pool* pool, int32_t* bt_row, int32_t* n_blocks, int32_t max_blocks, int32_t cur_len,
+                    int32_t n_new, hipStream_t stream);
+
+int32_t kv_num_free(const vs_pool* pool);
+int32_t kv_refcount(const vs_pool* pool, int32_t page); /* -1 for an out-of-range id */
+/* Device address of the pool memory and the page geometry, for filling pages. */
+void* kv_pool_base(const vs_pool* pool);
+
+/* ------------------------------------------------------------------ step */
+
+/* One step's batch ([Serving] "Continuous batching"; [KV Cache] section 06:
+ * the batch is re-formed every iteration). Sequence b brings rows
+ * q_start[b] .. q_start[b+1]-1; row i of sequence b sits at position
+ * ctx_len[b] + i, where ctx_len[b] counts positions already in its cache.
+ * The step writes K/V of every row into the pages through the block table,
+ * and each row attends to positions 0 .. its own position of its own
+ * sequence ([KV Cache] sections 02 and 07). */
+typedef struct vs_batch_desc {
+    int32_t B;          /* sequences, >= 1 */
+    int32_t M;          /* rows = q_start[B] */
+    int32_t M_log;      /* rows that produce logits (length of logit_rows) */
+    int32_t max_rows;   /* >= rows of any one sequence */
+    int32_t max_ctx;    /* >= ctx_len[b] + rows of b, for every b */
+    int32_t max_blocks; /* row stride of block_tables; >= ceil(max_ctx / page_tokens) */
+    const vs_pool* pool;
+    const int32_t* q_start;    /* device [B+1], q_start[0] = 0, non-decreasing */
+    const int32_t* ctx_len;    /* device [B] */
+    const int32_t* tokens;     /* device [M] token ids (the draft tokens of a verify pass) */
+    const int32_t* logit_rows; /* device [M_log], ascending row indices; NULL if M_log = 0 */
+} vs_batch_desc;
+
+typedef struct vs_step_out {
+    float* logits;     /* device [M_log][vocab] fp32, or NULL */
+    int32_t* argmax;   /* device [M]: greedy token of each logit row (lowest index on exact
+                          ties), -1 for rows without logits; may be NULL if M_log = 0 */
+    float* top2_gap;   /* device [M]: top-1 minus top-2 logit (0 on a tie), or NULL */
+    /* Fused greedy acceptance (see verify_accept); all three NULL to skip it. */
+    const int32_t* g0; /* device [B] */
+    int32_t* accept_len; /* device [B] */
+    int32_t* bonus;      /* device [B] */
+} vs_step_out;
+
+/* Workspace bytes decode_step needs for this batch shape and model. */
+vs_status decode_step_workspace_bytes(const vs_batch_desc* desc, const vs_model_desc* dims, size_t* bytes);
+
+/* One forward step of every row of every sequence. The weights are streamed
+ * once for all rows ([Spending the Idle] section 12.2; [KV Cache] section 02):
+ * embedding gather, then per layer RMSNorm, QKV product with rotary q/k and
+ * the K/V write into the pages, paged split-KV attention with an online-softmax
+ * merge ([KV Cache] section 07, Flash-Decoding), output product + residual,
+ * RMSNorm, gate/up product with SwiGLU, down product + residual; final RMSNorm
+ * and LM head on the logit rows, with the per-row argmax and top-2 gap.
+ * block_tables: device [B][max_blocks] int32 page ids. ws: device workspace of
+ * at least decode_step_workspace_bytes. */
+vs_status decode_step(const vs_batch_desc* desc, const int32_t* block_tables, const vs_weights* weights,
+                      const vs_step_out* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Greedy acceptance of a verify pass ([Serving Efficiency] section 31.5;
+ * [Spending the Idle] section 12.4; [KV Cache] section 08). For sequence b
+ * with rows r0 = q_start[b] .. r0+K-1 holding drafts d_1..d_K (the row
+ * tokens), g0[b] the target's greedy token for the first draft's position
+ * (known from the previous pass) and g_j = argmax[r0+j-1] the target's greedy
+ * token after row j-1: accept_len[b] = the largest n with d_j == g_{j-1} for
+ * every j <= n, and bonus[b] = g_n (the target's own token at the first
+ * mismatch, or after the last draft). A plain decode step is the K = 1 case
+ * with d_1 = g0. All arrays are on the device. */
+vs_status verify_accept(int32_t B, const int32_t* q_start, const int32_t* drafts, const int32_t* g0,
+                        const int32_t* argmax, int32_t* accept_len, int32_t* bonus, hipStream_t stream);
+
+/* ------------------------------------------------------------------ instrumentation */
+
+/* Kernel kinds of one step, for timing. */
+#define VS_KERNEL_NONE 0
+#define VS_KERNEL_QKV 1       /* QKV product + rotary + K/V page write */
+#define VS_KERNEL_ATTN 2      /* paged split-KV attention */
+#define VS_KERNEL_MERGE 3     /* split merge */
+#define VS_KERNEL_OPROJ 4     /* output product + residual */
+#define VS_KERNEL_GATEUP 5    /* gate/up product + SwiGLU */
+#define VS_KERNEL_DOWN 6      /* down product + residual */
+#define VS_KERNEL_LMHEAD 7    /* LM head + argmax partials */
+
+/* Measurement aid, not part of the step's function. While armed, every
+ * launch of kernel kind `kind` in decode_step is bracketed by hipEventRecord
+ * of start_events[i] and stop_events[i] on the step's stream, i = 0, 1, ...
+ * up to `capacity` launches (later launches are not timed). The events are
+ * caller-created hipEvent_t handles. kind = VS_KERNEL_NONE disarms.
+ * vs_timed_launches returns how many launches were bracketed since arming.
+ * Process-wide state; not for use while another thread runs decode_step. */
+vs_status vs_time_kernel(int32_t kind, void* const* start_events, void* const* stop_events, int32_t capacity);
+int32_t vs_timed_launches(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VERIFY_STEP_H */

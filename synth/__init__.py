@@ -2,8 +2,8 @@
 
 Only input generation lives here: random weights, KV-cache contents, token ids,
 coin flips and shuffles. Nothing in this package computes any part of the
-decode/verify step. The heavy lifting is ``synth.c`` (SplitMix64 counters and a
-Box-Muller transform, multi-threaded); this module loads it with ctypes and
+decode/verify step. The heavy lifting is ``synth.c`` (SplitMix64 counters and
+Marsaglia's polar method, multi-threaded); this module loads it with ctypes and
 returns NumPy / PyTorch CPU tensors.
 """
 from __future__ import annotations
@@ -28,7 +28,7 @@ def build(force: bool = False) -> str:
     """Compile synth.c into libsynth.so next to it (gcc, OpenMP)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+        subprocess.check_call(["gcc", "-O3", "-fopenmp", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 

@@ -15,9 +15,16 @@
  *                   the golden-ratio increment 0x9E3779B97F4A7C15 and each
  *                   state is passed through the variant-13 finaliser.
  *   uniform(k,i)  = top 53 bits of raw(k, i) scaled to [0, 1).
- *   normal(k,i)   = Box-Muller transform (Box & Muller, 1958) of the pair of
- *                   uniforms (2*floor(i/2), 2*floor(i/2)+1); even i takes the
- *                   cosine branch, odd i the sine branch.
+ *   normal(k,i)   = Marsaglia's polar method (Marsaglia & Bray, "A convenient
+ *                   method for generating normal variables", SIAM Review
+ *                   1964) for the pair p = floor(i/2): attempt a = 0, 1, ...
+ *                   draws u = 2*uniform(k, 256p + 2a) - 1 and
+ *                   v = 2*uniform(k, 256p + 2a + 1) - 1 until
+ *                   0 < s = u^2 + v^2 < 1, then the pair is
+ *                   (u, v) * sqrt(-2 ln(s) / s); even i takes the u branch.
+ *                   (Each attempt fails with probability 1 - pi/4; a pair
+ *                   never needs its 128 reserved attempts in practice, and
+ *                   the last one is taken as is if it ever came to that.)
  *
  * Element i of a tensor is therefore available without generating
  * elements 0..i-1, which lets a checker regenerate any slice of a very large
@@ -27,7 +34,7 @@
  * round-to-nearest-even (fp32 -> fp16 / bf16 conversions written here from
  * the IEEE-754 binary16 and bfloat16 bit layouts).
  *
- * Build: gcc -O2 -fopenmp -shared -fPIC synth.c -o libsynth.so -lm
+ * Build: gcc -O3 -fopenmp -shared -fPIC synth.c -o libsynth.so -lm
  */
 #include <math.h>
 #include <stdint.h>
@@ -119,23 +126,39 @@ static inline void store(void* out, int64_t j, int dtype, double v) {
     else ((uint16_t*)out)[j] = f32_to_bf16_rne(f);
 }
 
+/* Both normal deviates of pair p (polar method, counter-addressed attempts). */
+static inline void normal_pair(uint64_t key, uint64_t p, double* z0, double* z1) {
+    double u = 0.0, v = 0.0, s = 0.0;
+    for (uint64_t a = 0; a < 128; ++a) {
+        u = 2.0 * uniform_at(key, 256 * p + 2 * a) - 1.0;
+        v = 2.0 * uniform_at(key, 256 * p + 2 * a + 1) - 1.0;
+        s = u * u + v * v;
+        if (s > 0.0 && s < 1.0) break;
+    }
+    if (!(s > 0.0 && s < 1.0)) { /* unreachable in practice; keep the output finite */
+        *z0 = 0.0;
+        *z1 = 0.0;
+        return;
+    }
+    const double f = sqrt(-2.0 * log(s) / s);
+    *z0 = u * f;
+    *z1 = v * f;
+}
+
 /* out[j] = round(mean + std * normal(key, start + j)) for j in [0, n). */
 void synth_normal(uint64_t key, uint64_t start, int64_t n, double mean, double std, int dtype, void* out) {
     if (n <= 0) return;
-    const double two_pi = 6.283185307179586476925286766559;
     uint64_t first_pair = start >> 1;
     uint64_t last_pair = (start + (uint64_t)n - 1) >> 1;
     int64_t n_pairs = (int64_t)(last_pair - first_pair + 1);
 #pragma omp parallel for schedule(static)
     for (int64_t pi = 0; pi < n_pairs; ++pi) {
         uint64_t pair = first_pair + (uint64_t)pi;
-        double u1 = 1.0 - uniform_at(key, 2 * pair); /* (0, 1] so the log is finite */
-        double u2 = uniform_at(key, 2 * pair + 1);
-        double r = sqrt(-2.0 * log(u1));
-        double a = two_pi * u2;
+        double z0, z1;
+        normal_pair(key, pair, &z0, &z1);
         uint64_t i0 = 2 * pair;
-        if (i0 >= start) store(out, (int64_t)(i0 - start), dtype, mean + std * (r * cos(a)));
-        if (i0 + 1 < start + (uint64_t)n) store(out, (int64_t)(i0 + 1 - start), dtype, mean + std * (r * sin(a)));
+        if (i0 >= start) store(out, (int64_t)(i0 - start), dtype, mean + std * z0);
+        if (i0 + 1 < start + (uint64_t)n) store(out, (int64_t)(i0 + 1 - start), dtype, mean + std * z1);
     }
 }
 

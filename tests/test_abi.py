@@ -1,0 +1,92 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments before touching the GPU. No compute calls here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import verify_step_amd as vs
+from verify_step_amd import build as vsbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "verify_step.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(vs.LIB_PATH):
+        vsbuild.build()
+    return vs.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["kv_alloc", "kv_free", "kv_share", "kv_append", "decode_step", "verify_accept",
+              "decode_step_workspace_bytes", "kv_pool_create", "vs_last_error"]:
+        assert n in names
+    assert set(names) == set(vs.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_binding_has_the_same_names():
+    for n in vs.EXPORTS:
+        assert callable(getattr(vs, n)), n
+
+
+def _tiny_desc(**kw):
+    d = dict(num_pages=8, page_tokens=16, n_layers=1, n_kv_heads=4, head_dim=64, dtype=vs.VS_F32)
+    d.update(kw)
+    return vs.vs_pool_desc(*d.values())
+
+
+def test_pool_create_rejects_bad_geometry(L):
+    buf = ctypes.create_string_buffer(64)
+    with pytest.raises(vs.VSError) as e:
+        vs.kv_pool_create(_tiny_desc(), ctypes.addressof(buf), 64)
+    assert e.value.status == vs.VS_ERR_INVALID and "smaller" in str(e.value)
+    with pytest.raises(vs.VSError):
+        vs.kv_pool_create(_tiny_desc(num_pages=0), ctypes.addressof(buf), 64)
+    with pytest.raises(vs.VSError):
+        vs.kv_pool_create(_tiny_desc(dtype=7), ctypes.addressof(buf), 64)
+
+
+def test_page_bytes_formula(L):
+    # layers x (K, V) x kv_heads x 16 slots x head_dim x bytes
+    assert vs.kv_page_bytes(_tiny_desc()) == 1 * 2 * 4 * 16 * 64 * 4
+    assert vs.kv_page_bytes(_tiny_desc(n_layers=32, n_kv_heads=32, head_dim=128, dtype=vs.VS_F16)) == 8 * 2 ** 20
+
+
+def test_step_rejects_bad_shapes_before_launching(L):
+    dims = vs.vs_model_desc(256, 4, 4, 64, 1024, 1000, 1, vs.VS_F32, 10000.0, 1e-5)
+    desc = vs.vs_batch_desc(4, 4, 4, 1, 65, 5, None, None, None, None, None)
+    assert vs.decode_step_workspace_bytes(desc, dims) > 0
+    bad = vs.vs_model_desc(256, 4, 4, 96, 1024, 1000, 1, vs.VS_F32, 10000.0, 1e-5)
+    with pytest.raises(vs.VSError) as e:
+        vs.decode_step_workspace_bytes(desc, bad)
+    assert e.value.status == vs.VS_ERR_SHAPE
+    short = vs.vs_batch_desc(4, 4, 4, 1, 100, 5, None, None, None, None, None)  # 5 blocks < 100 positions
+    with pytest.raises(vs.VSError):
+        vs.decode_step_workspace_bytes(short, dims)
+    w = vs.vs_weights(dims, None, None, None, None)
+    out = vs.vs_step_out()
+    with pytest.raises(vs.VSError) as e:
+        vs.decode_step(desc, None, w, out, None, 0, 0)
+    assert e.value.status == vs.VS_ERR_INVALID
+
+
+def test_verify_accept_rejects_null(L):
+    with pytest.raises(vs.VSError):
+        vs.verify_accept(3, None, None, None, None, None, None, 0)
+    vs.verify_accept(0, None, None, None, None, None, None, 0)  # nothing to do

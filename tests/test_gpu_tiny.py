@@ -1,0 +1,155 @@
+"""GPU parity on the tiny 1-layer decoder: the HIP path through the C ABI against the oracle.
+
+The tiny workload: d_model 256, 4 heads x 64, MLP 1024, vocab 1000, one layer;
+weights N(0, 0.02); KV N(0, 1) in 16-token pages drawn at random from a
+64-page pool. Every case prints its name before touching the GPU.
+"""
+import pytest
+import torch
+
+import oracle
+import synth
+from harness import GpuModel, GpuPool, SeqSpec, alloc_rows, make_step, run_step
+from harness.compare import TOL, check_argmax, check_rows
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+SEED_W, SEED_KV, SEED_TOK, SEED_PAGES = 1001, 1002, 1003, 1006
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def run_case(dims, ctxs, rows_per_seq, gains="one", want=None, g0=None, pool_pages=64, contents=None,
+             tokens=None):
+    """Run one step on the GPU and in the oracle; return (gpu results, oracle results, helpers)."""
+    w_cpu = W.make_weights(dims, SEED_W, gains=gains)
+    model = GpuModel(dims, weights_cpu=w_cpu)
+    pool = GpuPool(dims, pool_pages)
+    B = len(ctxs)
+    contents = contents or list(range(B))
+    if tokens is None:
+        tokens = [W.token_ids(SEED_TOK, 100 + b, rows_per_seq[b], dims.vocab) for b in range(B)]
+    want = want or [True] * B
+    rows = alloc_rows(pool, [c + k for c, k in zip(ctxs, rows_per_seq)], shuffle_key=synth.key(SEED_PAGES))
+    seqs_o = []
+    for b in range(B):
+        kv = W.kv_block(dims, SEED_KV, contents[b], 0, ctxs[b])
+        pool.write(rows[b], 0, kv)
+        full = torch.zeros(dims.n_layers, 2, ctxs[b] + rows_per_seq[b], dims.n_kv_heads, dims.head_dim,
+                           dtype=dims.torch_dtype)
+        full[:, :, :ctxs[b]] = kv
+        seqs_o.append(oracle.SeqState(full, ctxs[b], list(tokens[b]), want[b]))
+    sb = make_step(model, pool, [SeqSpec(c, list(t), wl) for c, t, wl in zip(ctxs, tokens, want)], rows, g0=g0)
+    run_step(model, sb)
+    torch.cuda.synchronize()
+    ref = oracle.decode_step(dims, w_cpu, seqs_o)
+    return sb, ref, seqs_o, pool, rows
+
+
+def check_case(dims, sb, ref, seqs_o, pool, rows, ctxs, rows_per_seq):
+    tol = TOL[dims.dtype]
+    M = sum(rows_per_seq)
+    am = sb.argmax[:M].cpu().tolist()
+    gap = sb.gap[:M].cpu()
+    lrows = [r for r in range(M) if ref.logits[r] is not None]
+    gpu_logits = sb.logits[:len(lrows)].cpu() if lrows else []
+    check_rows([gpu_logits[j] for j in range(len(lrows))], [ref.logits[r] for r in lrows], tol, "logits")
+    n_exact = 0
+    for j, r in enumerate(lrows):
+        n_exact += check_argmax(am[r], ref.argmax[r], ref.logits[r], ref.gap[r], f"row {r}")
+        if am[r] == ref.argmax[r]:
+            assert abs(float(gap[r]) - ref.gap[r]) <= tol * max(1.0, float(ref.logits[r].abs().max())), \
+                f"row {r} gap {float(gap[r])} vs {ref.gap[r]}"
+    for r in range(M):
+        if ref.logits[r] is None:
+            assert am[r] == -1
+    # the K/V rows this step wrote, read back through the block tables
+    for b in range(len(ctxs)):
+        got = pool.read(rows[b], ctxs[b], ctxs[b] + rows_per_seq[b]).double()
+        want = seqs_o[b].kv[:, :, ctxs[b]:ctxs[b] + rows_per_seq[b]].double()
+        for l in range(dims.n_layers):
+            for t in range(2):
+                for i in range(rows_per_seq[b]):
+                    check_rows([got[l, t, i]], [want[l, t, i]], tol, f"kv seq {b} layer {l} {'KV'[t]} row {i}")
+        # the cached prefix is untouched
+        assert torch.equal(pool.read(rows[b], 0, ctxs[b]), seqs_o[b].kv[:, :, :ctxs[b]])
+    return n_exact
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_tiny_decode_four_sequences(dtype):
+    """The tiny workload: B=4, contexts 5, 17, 33, 64, one query token each."""
+    _say(f"tiny decode dtype={dtype}")
+    dims = W.TINY.with_dtype(dtype)
+    ctxs, k = [5, 17, 33, 64], [1, 1, 1, 1]
+    sb, ref, so, pool, rows = run_case(dims, ctxs, k)
+    check_case(dims, sb, ref, so, pool, rows, ctxs, k)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_tiny_verify_five_rows_random_gains(dtype):
+    """K=5 causal rows per sequence (a verify pass) with non-unit norm gains, fused acceptance."""
+    _say(f"tiny verify K=5 dtype={dtype}")
+    dims = W.TINY.with_dtype(dtype)
+    ctxs, k = [0, 15, 16, 47], [5, 5, 5, 5]
+    g0 = [7, 8, 9, 10]
+    sb, ref, so, pool, rows = run_case(dims, ctxs, k, gains="random", g0=g0)
+    check_case(dims, sb, ref, so, pool, rows, ctxs, k)
+    acc = sb.accept_len.cpu().tolist()
+    bon = sb.bonus.cpu().tolist()
+    am = sb.argmax.cpu().tolist()
+    toks = sb.tokens.cpu().tolist()
+    for b in range(4):
+        n, bonus = oracle.accept_greedy(toks[5 * b:5 * b + 5], g0[b], am[5 * b:5 * b + 5])
+        assert (acc[b], bon[b]) == (n, bonus)
+
+
+def test_tiny_verify_accepts_oracle_greedy_drafts():
+    """Drafts equal to the oracle's own greedy continuation are accepted in full."""
+    _say("tiny verify with oracle-greedy drafts")
+    dims = W.TINY.with_dtype("f32")
+    ctx = 20
+    # oracle greedy continuation: g0 from a one-row step, then g1..g4 by feeding the greedy tokens
+    w_cpu = W.make_weights(dims, SEED_W)
+    kv = W.kv_block(dims, SEED_KV, 0, 0, ctx)
+    full = torch.zeros(1, 2, ctx + 6, 4, 64, dtype=torch.float32)
+    full[:, :, :ctx] = kv
+    st = oracle.SeqState(full, ctx - 1, [int(W.token_ids(SEED_TOK, 5, 1, 1000)[0])])
+    full[:, :, ctx - 1] = 0  # position ctx-1 is recomputed by the step below
+    g = [oracle.decode_step(dims, w_cpu, [st]).argmax[0]]
+    st.ctx, st.tokens = ctx, [g[0]]
+    for _ in range(4):
+        g.append(oracle.decode_step(dims, w_cpu, [st]).argmax[0])
+        st.ctx += 1
+        st.tokens = [g[-1]]
+    # the GPU sees positions 0..ctx-1 as cached (the oracle's own K/V) and verifies drafts g0..g4
+    model = GpuModel(dims, weights_cpu=w_cpu)
+    pool = GpuPool(dims, 16)
+    rows = alloc_rows(pool, [ctx + 5])
+    pool.write(rows[0], 0, full[:, :, :ctx])
+    sb = make_step(model, pool, [SeqSpec(ctx, g[:5])], rows, g0=[g[0]])
+    run_step(model, sb)
+    torch.cuda.synchronize()
+    assert int(sb.accept_len[0]) == 5
+    assert sb.argmax[:4].cpu().tolist() == g[1:5]
+
+
+def test_tiny_grouped_kv_heads():
+    """4 query heads over 2 KV heads: each KV page block serves two query heads."""
+    _say("tiny GQA 4/2")
+    dims = W.ModelDims("tiny-gqa", 256, 4, 2, 64, 1024, 1000, 1, "f16")
+    ctxs, k = [3, 40], [2, 3]
+    sb, ref, so, pool, rows = run_case(dims, ctxs, k, gains="random")
+    check_case(dims, sb, ref, so, pool, rows, ctxs, k)
+
+
+def test_tiny_rows_without_logits_and_long_context():
+    """A long sequence spanning many splits, one sequence without logits, head_dim 128."""
+    _say("tiny head_dim 128, long context, no-logit sequence")
+    dims = W.ModelDims("tiny-d256-2x128", 256, 2, 2, 128, 512, 1000, 2, "bf16")
+    ctxs, k = [1000, 7, 300], [1, 4, 2]
+    sb, ref, so, pool, rows = run_case(dims, ctxs, k, want=[True, False, True], pool_pages=128)
+    check_case(dims, sb, ref, so, pool, rows, ctxs, k)

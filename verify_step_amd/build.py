@@ -1,0 +1,67 @@
+"""Build the gfx950 shared library libverify_step.so in-tree with hipcc.
+
+    python -m verify_step_amd.build        # or verify_step_amd.build.build()
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libverify_step.so")
+SOURCES = ["step.hip", "pool.cpp"]
+HEADERS = ["common.h", "gemm.h", "attention.h", "misc.h", "error.h"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def command(out: str) -> list[str]:
+    return [
+        hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # keep the compiler from emitting packed fp32 VALU ops
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-result",
+        "-I", os.path.join(ROOT, "include"),
+        *[os.path.join(CSRC, s) for s in SOURCES],
+        "-o", out,
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libverify_step.so (always recompiles)."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # the host pass does not know the packed-fp32 feature and says so; that line is harmless
+    noise = "is not a recognized feature for this target"
+    msgs = [l for l in proc.stdout.splitlines() if noise not in l]
+    if proc.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def sources_newer_than_lib() -> bool:
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    paths = [os.path.join(CSRC, s) for s in SOURCES + HEADERS] + [os.path.join(ROOT, "include", "verify_step.h")]
+    return any(os.path.getmtime(p) > t for p in paths if os.path.exists(p))
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
+    sys.exit(0)

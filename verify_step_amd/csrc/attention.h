@@ -1,0 +1,200 @@
+// Paged split-KV attention for decode and verify rows (gfx950).
+//
+// [KV Cache] section 05: K and V are read through the sequence's block table
+// from pages anywhere in the pool. Section 07, Flash-Decoding: the keys of
+// one (sequence, head) are cut into splits processed in parallel; each split
+// keeps the online-softmax state (running max m, running sum l, rescaled
+// output o) over its keys and stores it, and a merge rescales the splits to a
+// common maximum and divides the summed outputs by the summed sums
+// ([Serving Efficiency] section 31.4, Example 31.2: combine statistics, not
+// normalised tile outputs).
+//
+// One wave64 workgroup per (split, head, sequence). Lane l owns dims
+// [(l%16)*DH/16, +DH/16) of key slot (l/16) within each group of four keys, so
+// one page of 16 keys is four 16-byte loads per lane for K and four for V, and
+// the 16 lanes that share a key finish its dot product with xor shuffles. Every
+// K/V byte is used by exactly one wave, so it goes from HBM straight to
+// registers; the next page is loaded while the current one is reduced.
+// All rows of one sequence (up to RMAX at a time) share each K/V load; row i
+// at position ctx + i keeps keys 0..ctx + i (causal across the rows of a pass).
+// Scores are kept in the log2 domain (q pre-scaled by log2(e)/sqrt(DH)).
+#pragma once
+
+#include "common.h"
+
+namespace vs {
+
+struct AttnArgs {
+    const void* q;  // [M][n_heads*DH] storage type, rotated
+    const void* kv_base;
+    long page_elems, layer_elems;
+    int layer, n_heads, n_kv_heads, page_tokens;
+    const int* block_tables;
+    int max_blocks;
+    int num_pages;  // page ids are clamped into [0, num_pages) before any read
+    int M;          // rows in the step; q_start values are clamped into [0, M]
+    const int* q_start;
+    const int* ctx_len;
+    int n_splits, split_pages;
+    float scale_log2;  // log2(e) / sqrt(DH)
+    float* part;       // [M][n_heads][n_splits][DH + 2]: m (log2 domain), l, o[DH]
+    void* out;         // merge output [M][n_heads*DH] storage type
+};
+
+template <int DT, int DH, int RMAX>
+__global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
+    constexpr int DPL = DH / 16;  // dims per lane
+    const int lane = threadIdx.x;
+    const int g = lane >> 4;   // key slot within a group of four
+    const int c = lane & 15;   // dim chunk
+    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int group = a.n_heads / a.n_kv_heads;
+    const int hk = h / group;
+
+    const int r0 = min(max(a.q_start[b], 0), a.M);
+    const int R = min(max(a.q_start[b + 1] - r0, 0), a.M - r0);
+    const int ctx = max(a.ctx_len[b], 0);
+    const int n_keys = ctx + R;
+    const int T = a.page_tokens;
+    const int n_pages = min((n_keys + T - 1) / T, a.max_blocks);
+    const int p_begin = s * a.split_pages;
+    const int p_end = min(p_begin + a.split_pages, n_pages);
+
+    const int* bt = a.block_tables + (long)b * a.max_blocks;
+    const long kofs = (long)a.layer * a.layer_elems + (long)hk * T * DH + (long)c * DPL;
+    const long vofs = kofs + (long)a.n_kv_heads * T * DH;
+    const int QLD = a.n_heads * DH;
+
+    for (int rg = 0; rg < R; rg += RMAX) {
+        const int nr = min(RMAX, R - rg);
+        float qr[RMAX][DPL];
+        float o[RMAX][DPL];
+        float m[RMAX], l[RMAX];
+#pragma unroll
+        for (int i = 0; i < RMAX; ++i) {
+            m[i] = -INFINITY;
+            l[i] = 0.f;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) o[i][e] = 0.f;
+            if (i < nr) {
+                load_widen<DT, DPL>(reinterpret_cast<const char*>(a.q) +
+                                        ((long)(r0 + rg + i) * QLD + (long)h * DH + c * DPL) * St<DT>::bytes,
+                                    qr[i]);
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) qr[i][e] *= a.scale_log2;
+            } else {
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) qr[i][e] = 0.f;
+            }
+        }
+
+        RawVec<DT, DPL> kf[4], vf[4];  // current page (raw storage words)
+        RawVec<DT, DPL> kn[4], vn[4];  // next page, in flight
+        const char* kvb = reinterpret_cast<const char*>(a.kv_base);
+        if (p_begin < p_end) {
+            const long pb = (long)min(max(bt[p_begin], 0), a.num_pages - 1) * a.page_elems;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                load_raw<DT, DPL>(kn[u], kvb + (pb + kofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
+                load_raw<DT, DPL>(vn[u], kvb + (pb + vofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
+            }
+        }
+        for (int p = p_begin; p < p_end; ++p) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                kf[u] = kn[u];
+                vf[u] = vn[u];
+            }
+            if (p + 1 < p_end) {  // prefetch the next page while this one is reduced
+                const long pb = (long)min(max(bt[p + 1], 0), a.num_pages - 1) * a.page_elems;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    load_raw<DT, DPL>(kn[u], kvb + (pb + kofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
+                    load_raw<DT, DPL>(vn[u], kvb + (pb + vofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < RMAX; ++i) {
+                if (i >= nr) break;
+                const int qpos = ctx + rg + i;
+                float sc[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    float d = 0.f;
+#pragma unroll
+                    for (int e = 0; e < DPL; ++e) d += qr[i][e] * raw_at<DT, DPL>(kf[u], e);
+                    d += shfl_xor(d, 1);
+                    d += shfl_xor(d, 2);
+                    d += shfl_xor(d, 4);
+                    d += shfl_xor(d, 8);
+                    const int kp = p * T + 4 * u + g;
+                    sc[u] = (kp <= qpos) ? d : -INFINITY;
+                }
+                float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+                pm = fmaxf(pm, shfl_xor(pm, 16));
+                pm = fmaxf(pm, shfl_xor(pm, 32));
+                const float mn = fmaxf(m[i], pm);
+                if (mn == -INFINITY) continue;  // no visible key for this row yet
+                const float alpha = exp2f(m[i] - mn);
+                float ps = 0.f;
+                float pu[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    pu[u] = exp2f(sc[u] - mn);
+                    ps += pu[u];
+                }
+                ps += shfl_xor(ps, 16);
+                ps += shfl_xor(ps, 32);
+                l[i] = l[i] * alpha + ps;
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) {
+                    float acc = o[i][e] * alpha;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc += pu[u] * raw_at<DT, DPL>(vf[u], e);
+                    o[i][e] = acc;
+                }
+                m[i] = mn;
+            }
+        }
+        // sum the four key slots' partial outputs and store this split's state
+#pragma unroll
+        for (int i = 0; i < RMAX; ++i) {
+            if (i >= nr) break;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) {
+                o[i][e] += shfl_xor(o[i][e], 16);
+                o[i][e] += shfl_xor(o[i][e], 32);
+            }
+            float* dst = a.part + (((long)(r0 + rg + i) * a.n_heads + h) * a.n_splits + s) * (DH + 2);
+            if (lane == 0) {
+                dst[0] = m[i];
+                dst[1] = l[i];
+            }
+            if (g == 0) {
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) dst[2 + c * DPL + e] = o[i][e];
+            }
+        }
+    }
+}
+
+// One workgroup of DH threads per (row, head): rescale every split's state to
+// the largest running maximum and divide the summed outputs by the summed sums.
+template <int DT, int DH>
+__global__ void __launch_bounds__(DH) attn_merge_kernel(AttnArgs a) {
+    const int row = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    const float* src = a.part + ((long)row * a.n_heads + h) * a.n_splits * (DH + 2);
+    float mx = -INFINITY;
+    for (int s = 0; s < a.n_splits; ++s) mx = fmaxf(mx, src[s * (DH + 2)]);
+    float l = 0.f, o = 0.f;
+    for (int s = 0; s < a.n_splits; ++s) {
+        const float ms = src[s * (DH + 2)];
+        if (ms == -INFINITY) continue;
+        const float w = exp2f(ms - mx);
+        l += w * src[s * (DH + 2) + 1];
+        o += w * src[s * (DH + 2) + 2 + d];
+    }
+    store_round<DT>(a.out, (long)row * a.n_heads * DH + (long)h * DH + d, o / l);
+}
+
+}  // namespace vs

@@ -1,0 +1,360 @@
+// Weight-streaming skinny GEMM for the decode / verify step (gfx950).
+//
+// C[m][n] = sum_k X[m][k] * W[n][k] for the M <= 64 rows of one 64-row group
+// of a step ([KV Cache] section 02: every row passing through a weight matrix
+// shares one read of it; [Spending the Idle] section 12.2: the weights have
+// no idea how many tokens pass through them).
+//
+// Work split. A workgroup owns one tile of 32 output features (two blocks of
+// 16 weight rows, chosen by the epilogue so that values an epilogue combines,
+// such as a rotary pair or a gate/up pair, land in the same lane) and all rows
+// of its row group. Its NW waves split the reduction axis; each wave streams
+// its slice of the two 16-row blocks with 16-byte loads straight into MFMA
+// operand registers (no LDS round trip: every weight byte is used by exactly
+// one wave), multiplies on the matrix cores (16x16x32 fp16/bf16, 16x16x4 fp32
+// with M padded to 16), and the waves' partial tiles are summed in a fixed
+// binary tree through LDS, so results are deterministic.
+//
+// Operand roles: A = weights (MFMA rows = output features), B = activations
+// (MFMA columns = rows of the batch). Lane l supplies weight row (l % 16) and
+// activation row (l % 16), both at reduction offsets (l / 16) * 8 .. +7 of each
+// 32-wide chunk, and receives C[feature (l/16)*4 + r][row l % 16], r = 0..3.
+#pragma once
+
+#include "common.h"
+
+namespace vs {
+
+enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+struct ArgPart {
+    float v1;  // largest value in the tile
+    int i1;    // its index (lowest on exact ties)
+    float v2;  // second-largest value (equal to v1 on a tie)
+    int pad;
+};
+
+struct GemmArgs {
+    const void* w0;
+    const void* w1;
+    const void* w2;
+    int n0, n1, n2;  // rows of each weight segment
+    int K;           // reduction length, a multiple of 32
+    const void* act;  // activations [rows][act_ld] in the storage type
+    int act_ld;
+    int M;  // valid activation rows
+    int n_tiles;
+    // rotary + K/V write (EPI_QKV)
+    void* q_out;  // [M][n_heads*head_dim]
+    void* kv_base;
+    long page_elems;   // elements per page
+    long layer_elems;  // elements per layer inside a page
+    int layer, head_dim, n_heads, n_kv_heads, page_tokens;
+    const int* block_tables;
+    int max_blocks;
+    int num_pages;  // pool size; page ids outside [0, num_pages) are never written
+    const int* row_seq;
+    const int* row_pos;
+    const float* rope_cs;  // [M][head_dim/2][2] (cos, sin)
+    // residual add (EPI_RESID)
+    float* x;
+    int x_ld;
+    // SwiGLU (EPI_SWIGLU)
+    void* h_out;
+    int h_ld;
+    // logits + argmax partials (EPI_LOGITS)
+    float* logits;
+    int vocab;
+    ArgPart* parts;
+};
+
+__device__ __forceinline__ void argpart_combine(float& v1, int& i1, float& v2, float bv1, int bi1, float bv2) {
+    if (bv1 > v1 || (bv1 == v1 && bi1 < i1)) {
+        v2 = fmaxf(bv2, v1);
+        v1 = bv1;
+        i1 = bi1;
+    } else {
+        v2 = fmaxf(v2, bv1);
+    }
+}
+
+// Raw operand fragment of one lane: 8 consecutive storage elements.
+template <int DT> struct Frag;
+template <> struct Frag<F32> {
+    float4_t a, b;
+};
+template <> struct Frag<F16> {
+    uint4 a;
+};
+template <> struct Frag<BF16> {
+    uint4 a;
+};
+
+template <int DT>
+__device__ __forceinline__ void frag_load(Frag<DT>& f, const void* base, long elem, bool valid) {
+    if constexpr (DT == F32) {
+        if (valid) {
+            const float4_t* p = reinterpret_cast<const float4_t*>(reinterpret_cast<const float*>(base) + elem);
+            f.a = p[0];
+            f.b = p[1];
+        } else {
+            f.a = (float4_t){0.f, 0.f, 0.f, 0.f};
+            f.b = f.a;
+        }
+    } else {
+        if (valid) {
+            f.a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+        } else {
+            f.a = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float4_t frag_mma(const Frag<DT>& w, const Frag<DT>& x, float4_t acc) {
+    if constexpr (DT == F16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, w.a), __builtin_bit_cast(half8_t, x.a),
+                                                      acc, 0, 0, 0);
+    } else if constexpr (DT == BF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w.a),
+                                                       __builtin_bit_cast(bf16x8_t, x.a), acc, 0, 0, 0);
+    } else {
+        // eight rank-4 updates; element e of every lane carries reduction offset (l/16)*8 + e
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(w.a[e], x.a[e], acc, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(w.b[e], x.b[e], acc, 0, 0, 0);
+        return acc;
+    }
+}
+
+// Which two 16-row weight blocks a tile covers, and what they mean.
+struct TileMap {
+    const void* w;      // segment base for block A (block B uses wb)
+    const void* wb;
+    int rowA, rowB;     // first weight row of each block inside its segment
+    int nrows;          // rows in the segment (rows >= nrows are padding)
+    int seg;            // EPI_QKV: 0 = q, 1 = k, 2 = v
+    int head, j;        // EPI_QKV: head inside the segment, 16-wide slot of the head's first half
+};
+
+template <int EPI>
+__device__ __forceinline__ TileMap tile_map(const GemmArgs& g, int t) {
+    TileMap m;
+    m.seg = 0;
+    m.head = 0;
+    m.j = 0;
+    if constexpr (EPI == EPI_RESID || EPI == EPI_LOGITS) {
+        m.w = g.w0;
+        m.wb = g.w0;
+        m.rowA = 32 * t;
+        m.rowB = 32 * t + 16;
+        m.nrows = g.n0;
+    } else if constexpr (EPI == EPI_SWIGLU) {
+        m.w = g.w0;  // gate
+        m.wb = g.w1; // up
+        m.rowA = 16 * t;
+        m.rowB = 16 * t;
+        m.nrows = g.n0;
+    } else {
+        const int tph = g.head_dim / 32;  // tiles per head
+        const int qt = g.n_heads * tph, kt = g.n_kv_heads * tph;
+        int tt = t;
+        if (tt < qt) {
+            m.seg = 0;
+            m.w = g.w0;
+            m.nrows = g.n0;
+        } else if (tt < qt + kt) {
+            m.seg = 1;
+            tt -= qt;
+            m.w = g.w1;
+            m.nrows = g.n1;
+        } else {
+            m.seg = 2;
+            tt -= qt + kt;
+            m.w = g.w2;
+            m.nrows = g.n2;
+        }
+        m.wb = m.w;
+        m.head = tt / tph;
+        m.j = tt % tph;
+        m.rowA = m.head * g.head_dim + 16 * m.j;
+        m.rowB = m.rowA + g.head_dim / 2;
+    }
+    return m;
+}
+
+template <int DT, int MT, int NW, int EPI, int U>
+__global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int tile = blockIdx.x;
+    const int mg = blockIdx.y;  // 64-row group
+    const TileMap tm = tile_map<EPI>(g, tile);
+
+    const int KC = g.K / 32;
+    const int kc0 = (wave * KC) / NW;
+    const int kc1 = ((wave + 1) * KC) / NW;
+
+    const int l16 = lane & 15;
+    const int kofs = (lane >> 4) * 8;
+    const int wrowA = tm.rowA + l16, wrowB = tm.rowB + l16;
+    const bool vA = wrowA < tm.nrows, vB = wrowB < tm.nrows;
+    const long baseA = (long)(vA ? wrowA : 0) * g.K + kofs;
+    const long baseB = (long)(vB ? wrowB : 0) * g.K + kofs;
+    long xbase[MT];
+    bool xv[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = mg * 64 + mt * 16 + l16;
+        xv[mt] = m < g.M;
+        xbase[mt] = (long)(xv[mt] ? m : 0) * g.act_ld + kofs;
+    }
+
+    float4_t acc[MT][2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        acc[mt][0] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        acc[mt][1] = acc[mt][0];
+    }
+
+    for (int kc = kc0; kc < kc1; kc += U) {
+        Frag<DT> fa[U], fb[U], fx[U][MT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool in = kc + u < kc1;
+            const long ko = (long)(kc + u) * 32;
+            frag_load<DT>(fa[u], tm.w, baseA + ko, in && vA);
+            frag_load<DT>(fb[u], tm.wb, baseB + ko, in && vB);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) frag_load<DT>(fx[u][mt], g.act, xbase[mt] + ko, in && xv[mt]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                acc[mt][0] = frag_mma<DT>(fa[u], fx[u][mt], acc[mt][0]);
+                acc[mt][1] = frag_mma<DT>(fb[u], fx[u][mt], acc[mt][1]);
+            }
+        }
+    }
+
+    // fixed-order tree reduction of the NW partial tiles into wave 0
+    if constexpr (NW > 1) {
+        __shared__ float red[(NW / 2) * MT * 8 * 64];
+#pragma unroll
+        for (int s = 1; s < NW; s <<= 1) {
+            if ((wave & (2 * s - 1)) == s) {
+                float* dst = red + (wave / (2 * s)) * (MT * 8 * 64);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) dst[((mt * 2 + b) * 4 + r) * 64 + lane] = acc[mt][b][r];
+            }
+            __syncthreads();
+            if ((wave & (2 * s - 1)) == 0) {
+                const float* src = red + (wave / (2 * s)) * (MT * 8 * 64);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[mt][b][r] += src[((mt * 2 + b) * 4 + r) * 64 + lane];
+            }
+            __syncthreads();
+        }
+    }
+    if (wave != 0) return;
+
+    // ---- epilogue on wave 0: lane holds C[feature (lane/16)*4 + r][row lane%16] of each block
+    const int nl0 = (lane >> 4) * 4;
+    if constexpr (EPI == EPI_LOGITS) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = mg * 64 + mt * 16 + l16;
+            float v1 = -INFINITY, v2 = -INFINITY;
+            int i1 = 0x7FFFFFFF;
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int col = (b ? tm.rowB : tm.rowA) + nl0 + r;
+                    const float v = acc[mt][b][r];
+                    if (col < g.vocab) {
+                        if (m < g.M && g.logits) g.logits[(long)m * g.vocab + col] = v;
+                        argpart_combine(v1, i1, v2, v, col, -INFINITY);
+                    }
+                }
+            }
+#pragma unroll
+            for (int mask = 16; mask <= 32; mask <<= 1) {
+                const float o1 = shfl_xor(v1, mask);
+                const int oi = shfl_xor(i1, mask);
+                const float o2 = shfl_xor(v2, mask);
+                argpart_combine(v1, i1, v2, o1, oi, o2);
+            }
+            if (lane < 16 && m < g.M) {
+                ArgPart p;
+                p.v1 = v1;
+                p.i1 = i1;
+                p.v2 = v2;
+                p.pad = 0;
+                g.parts[(long)m * g.n_tiles + tile] = p;
+            }
+        }
+        return;
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = mg * 64 + mt * 16 + l16;
+            if (m >= g.M) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int nl = nl0 + r;
+                const float a = acc[mt][0][r];
+                const float b = acc[mt][1][r];
+                if constexpr (EPI == EPI_RESID) {
+                    float* xr = g.x + (long)m * g.x_ld;
+                    if (tm.rowA + nl < tm.nrows) xr[tm.rowA + nl] += a;
+                    if (tm.rowB + nl < tm.nrows) xr[tm.rowB + nl] += b;
+                } else if constexpr (EPI == EPI_SWIGLU) {
+                    if (tm.rowA + nl < tm.nrows) {
+                        const float s = a / (1.0f + expf(-a));
+                        store_round<DT>(g.h_out, (long)m * g.h_ld + tm.rowA + nl, s * b);
+                    }
+                } else {  // EPI_QKV
+                    const int half = g.head_dim / 2;
+                    const int i = 16 * tm.j + nl;  // rotary pair index inside the head
+                    float ra = a, rb = b;
+                    if (tm.seg < 2) {
+                        const float c = g.rope_cs[((long)m * half + i) * 2 + 0];
+                        const float s = g.rope_cs[((long)m * half + i) * 2 + 1];
+                        ra = a * c - b * s;
+                        rb = b * c + a * s;
+                    }
+                    if (tm.seg == 0) {
+                        const long o = (long)m * (g.n_heads * g.head_dim) + tm.head * g.head_dim + i;
+                        store_round<DT>(g.q_out, o, ra);
+                        store_round<DT>(g.q_out, o + half, rb);
+                    } else {
+                        const int pos = g.row_pos[m];
+                        const int sq = g.row_seq[m];
+                        if (pos < 0 || pos / g.page_tokens >= g.max_blocks) continue;
+                        const int page = g.block_tables[(long)sq * g.max_blocks + pos / g.page_tokens];
+                        if (page < 0 || page >= g.num_pages) continue;
+                        const int slot = pos % g.page_tokens;
+                        const long o = (long)page * g.page_elems + (long)g.layer * g.layer_elems +
+                                       ((long)(tm.seg - 1) * g.n_kv_heads + tm.head) * g.page_tokens * g.head_dim +
+                                       (long)slot * g.head_dim + i;
+                        store_round<DT>(g.kv_base, o, ra);
+                        store_round<DT>(g.kv_base, o + half, rb);
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace vs

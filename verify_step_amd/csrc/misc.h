@@ -1,0 +1,160 @@
+// Small kernels of the step: row bookkeeping + rotary angles, embedding
+// gather, RMSNorm, argmax reduction with fused greedy acceptance.
+#pragma once
+
+#include "common.h"
+#include "gemm.h"
+
+namespace vs {
+
+// Row r -> its sequence and position; rotary (cos, sin) for every pair of
+// every row, from the float64 angle pos * theta^(-2i/head_dim).
+// Grid: one workgroup per row, head_dim/2 threads.
+__global__ void prep_rows_kernel(const int* q_start, const int* ctx_len, int B, int head_dim, double theta,
+                                 int* row_seq, int* row_pos, float* rope_cs) {
+    const int r = blockIdx.x;
+    int lo = 0, hi = B;  // largest b with q_start[b] <= r
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (q_start[mid] <= r) lo = mid;
+        else hi = mid;
+    }
+    const int pos = ctx_len[lo] + (r - q_start[lo]);
+    if (threadIdx.x == 0) {
+        row_seq[r] = lo;
+        row_pos[r] = pos;
+    }
+    const int half = head_dim / 2;
+    for (int i = threadIdx.x; i < half; i += blockDim.x) {
+        const double inv_freq = pow(theta, -2.0 * (double)i / (double)head_dim);
+        const double ang = (double)pos * inv_freq;
+        rope_cs[((long)r * half + i) * 2 + 0] = (float)cos(ang);
+        rope_cs[((long)r * half + i) * 2 + 1] = (float)sin(ang);
+    }
+}
+
+// x[r][:] = embedding row of token r, widened to the fp32 residual stream.
+template <int DT>
+__global__ void embed_kernel(const int* tokens, const void* embed, int vocab, int D, float* x) {
+    const int r = blockIdx.x;
+    int t = tokens[r];
+    t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
+    for (int k = threadIdx.x; k < D; k += blockDim.x) x[(long)r * D + k] = load_one<DT>(embed, (long)t * D + k);
+}
+
+// y[r] = round(x[src] / sqrt(mean(x[src]^2) + eps) * gain), src = map ? map[r] : r
+// (a mapped row is clamped into [0, n_src)). Fixed-order block reduction
+// (deterministic). blockDim = 256.
+template <int DT>
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* x, const int* map, int n_src, const void* gain,
+                                                      int D, float eps, void* y) {
+    const int r = blockIdx.x;
+    const int src = map ? min(max(map[r], 0), n_src - 1) : r;
+    const float* xr = x + (long)src * D;
+    float ss = 0.f;
+    for (int k = threadIdx.x; k < D; k += blockDim.x) ss += xr[k] * xr[k];
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) ss += shfl_xor(ss, mask);
+    __shared__ float wsum[4];
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    const float inv = 1.0f / sqrtf(tot / (float)D + eps);
+    for (int k = threadIdx.x; k < D; k += blockDim.x)
+        store_round<DT>(y, (long)r * D + k, xr[k] * inv * load_one<DT>(gain, k));
+}
+
+// Per sequence: reduce each logit row's tile partials to (argmax, top-2 gap),
+// then optionally run greedy acceptance over the sequence's rows.
+// Grid: B workgroups of 256 threads.
+__global__ void __launch_bounds__(256) argmax_accept_kernel(const ArgPart* parts, int n_tiles, const int* q_start,
+                                                            int M, const int* logit_rows, int M_log,
+                                                            const int* tokens, const int* g0, int* argmax, float* gap,
+                                                            int* accept_len, int* bonus) {
+    const int b = blockIdx.x;
+    const int r0 = min(max(q_start[b], 0), M);
+    const int r1 = min(max(q_start[b + 1], r0), M);
+    __shared__ float sv1[4], sv2[4];
+    __shared__ int si1[4];
+    for (int r = r0; r < r1; ++r) {
+        // logit row index of r: binary search in the ascending logit_rows
+        int j = -1;
+        if (M_log > 0) {
+            int lo = 0, hi = M_log - 1;
+            while (lo <= hi) {
+                const int mid = (lo + hi) >> 1;
+                const int v = logit_rows[mid];
+                if (v == r) {
+                    j = mid;
+                    break;
+                }
+                if (v < r) lo = mid + 1;
+                else hi = mid - 1;
+            }
+        }
+        if (j < 0) {
+            if (threadIdx.x == 0) {
+                if (argmax) argmax[r] = -1;
+                if (gap) gap[r] = NAN;
+            }
+            continue;
+        }
+        float v1 = -INFINITY, v2 = -INFINITY;
+        int i1 = 0x7FFFFFFF;
+        for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) {
+            const ArgPart p = parts[(long)j * n_tiles + t];
+            argpart_combine(v1, i1, v2, p.v1, p.i1, p.v2);
+        }
+#pragma unroll
+        for (int mask = 32; mask >= 1; mask >>= 1) {
+            const float o1 = shfl_xor(v1, mask);
+            const int oi = shfl_xor(i1, mask);
+            const float o2 = shfl_xor(v2, mask);
+            argpart_combine(v1, i1, v2, o1, oi, o2);
+        }
+        if ((threadIdx.x & 63) == 0) {
+            sv1[threadIdx.x >> 6] = v1;
+            si1[threadIdx.x >> 6] = i1;
+            sv2[threadIdx.x >> 6] = v2;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float a1 = sv1[0], a2 = sv2[0];
+            int ai = si1[0];
+            for (int w = 1; w < 4; ++w) argpart_combine(a1, ai, a2, sv1[w], si1[w], sv2[w]);
+            argmax[r] = ai;
+            if (gap) gap[r] = a1 - a2;
+        }
+        __syncthreads();
+    }
+    if (accept_len && threadIdx.x == 0) {
+        // drafts d_1..d_K are the row tokens; g_0 is given, g_j = argmax of row j-1
+        const int K = r1 - r0;
+        int n = 0;
+        int g = g0[b];
+        while (n < K && tokens[r0 + n] == g) {
+            g = argmax[r0 + n];
+            ++n;
+        }
+        accept_len[b] = n;
+        bonus[b] = g;
+    }
+}
+
+// Standalone greedy acceptance: one thread per sequence.
+__global__ void verify_accept_kernel(int B, const int* q_start, const int* drafts, const int* g0, const int* argmax,
+                                     int* accept_len, int* bonus) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const int r0 = q_start[b], K = max(q_start[b + 1] - r0, 0);
+    int n = 0;
+    int g = g0[b];
+    while (n < K && drafts[r0 + n] == g) {
+        g = argmax[r0 + n];
+        ++n;
+    }
+    accept_len[b] = n;
+    bonus[b] = g;
+}
+
+}  // namespace vs

@@ -1,0 +1,415 @@
+// decode_step / verify_accept: host-side validation, workspace plan and the
+// launch sequence of one batched decode / verify step on gfx950.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <string>
+
+#include "../../include/verify_step.h"
+#include "attention.h"
+#include "common.h"
+#include "error.h"
+#include "gemm.h"
+#include "misc.h"
+
+const vs_pool_desc* vs_pool_geometry(const vs_pool* pool);
+
+namespace {
+thread_local std::string g_err;
+}
+
+vs_status vs_fail(vs_status code, const std::string& msg) {
+    g_err = msg;
+    return code;
+}
+vs_status vs_ok() { return VS_OK; }
+
+extern "C" const char* vs_last_error(void) { return g_err.c_str(); }
+
+namespace {
+
+using namespace vs;
+
+constexpr int kPageTokens = 16;
+
+// ---- optional per-kernel event timing (measurement aid) -------------------
+struct KernelTimer {
+    int kind = VS_KERNEL_NONE;
+    void* const* start = nullptr;
+    void* const* stop = nullptr;
+    int capacity = 0;
+    int count = 0;
+} g_timer;
+
+struct TimedScope {
+    hipStream_t s;
+    bool on;
+    int idx;
+    TimedScope(int kind, hipStream_t st) : s(st), on(false), idx(0) {
+        if (g_timer.kind == kind && kind != VS_KERNEL_NONE && g_timer.count < g_timer.capacity) {
+            on = true;
+            idx = g_timer.count++;
+            (void)hipEventRecord(static_cast<hipEvent_t>(g_timer.start[idx]), s);
+        }
+    }
+    ~TimedScope() {
+        if (on) (void)hipEventRecord(static_cast<hipEvent_t>(g_timer.stop[idx]), s);
+    }
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Plan {
+    int B, M, M_log, D, H, Hkv, Dh, F, V, L, dt, esz;
+    int n_splits, split_pages, rmax;
+    int n_tiles_lm;
+    size_t off_row_seq, off_row_pos, off_rope, off_x, off_xn, off_q, off_attn, off_h, off_part, off_xf, off_lmpart;
+    size_t total;
+};
+
+vs_status check_dims(const vs_model_desc* m) {
+    if (m->dtype != VS_F32 && m->dtype != VS_F16 && m->dtype != VS_BF16)
+        return vs_fail(VS_ERR_INVALID, "model dtype must be VS_F32, VS_F16 or VS_BF16");
+    if (m->head_dim != 64 && m->head_dim != 128) return vs_fail(VS_ERR_SHAPE, "head_dim must be 64 or 128");
+    if (m->n_heads <= 0 || m->n_kv_heads <= 0 || m->n_heads % m->n_kv_heads != 0)
+        return vs_fail(VS_ERR_SHAPE, "n_heads must be a positive multiple of n_kv_heads");
+    if (m->d_model != m->n_heads * m->head_dim) return vs_fail(VS_ERR_SHAPE, "d_model must equal n_heads * head_dim");
+    if (m->ffn <= 0 || m->ffn % 32 != 0) return vs_fail(VS_ERR_SHAPE, "ffn must be a positive multiple of 32");
+    if (m->vocab < 2 || m->n_layers <= 0) return vs_fail(VS_ERR_SHAPE, "vocab >= 2 and n_layers >= 1 required");
+    if (!(m->eps > 0.f) || !(m->rope_theta > 0.f)) return vs_fail(VS_ERR_INVALID, "eps and rope_theta must be > 0");
+    return vs_ok();
+}
+
+vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
+    if (!d || !m || !p) return vs_fail(VS_ERR_INVALID, "null argument");
+    vs_status st = check_dims(m);
+    if (st != VS_OK) return st;
+    if (d->B < 1 || d->M < 0 || d->M_log < 0 || d->M_log > d->M || d->max_rows < 1 || d->max_ctx < 1 ||
+        d->max_blocks < 1)
+        return vs_fail(VS_ERR_INVALID, "batch sizes out of range (B >= 1, 0 <= M_log <= M, max_* >= 1)");
+    if ((long)d->max_blocks * kPageTokens < d->max_ctx)
+        return vs_fail(VS_ERR_SHAPE, "max_blocks * 16 must cover max_ctx");
+    p->B = d->B;
+    p->M = d->M;
+    p->M_log = d->M_log;
+    p->D = m->d_model;
+    p->H = m->n_heads;
+    p->Hkv = m->n_kv_heads;
+    p->Dh = m->head_dim;
+    p->F = m->ffn;
+    p->V = m->vocab;
+    p->L = m->n_layers;
+    p->dt = m->dtype;
+    p->esz = m->dtype == VS_F32 ? 4 : 2;
+    // split the keys so that about 4096 single-wave workgroups cover B x heads
+    const int max_pages = (d->max_ctx + kPageTokens - 1) / kPageTokens;
+    const long pairs = (long)d->B * m->n_heads;
+    int ns = (int)std::min<long>(max_pages, std::max<long>(1, (4096 + pairs - 1) / pairs));
+    p->split_pages = (max_pages + ns - 1) / ns;
+    p->n_splits = (max_pages + p->split_pages - 1) / p->split_pages;
+    p->rmax = d->max_rows <= 1 ? 1 : d->max_rows <= 2 ? 2 : d->max_rows <= 4 ? 4 : 8;
+    p->n_tiles_lm = (m->vocab + 31) / 32;
+    const size_t M = (size_t)std::max(d->M, 1), ML = (size_t)std::max(d->M_log, 1);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    p->off_row_seq = take(M * 4);
+    p->off_row_pos = take(M * 4);
+    p->off_rope = take(M * (p->Dh / 2) * 2 * 4);
+    p->off_x = take(M * p->D * 4);
+    p->off_xn = take(M * p->D * p->esz);
+    p->off_q = take(M * p->H * p->Dh * p->esz);
+    p->off_attn = take(M * p->H * p->Dh * p->esz);
+    p->off_h = take(M * p->F * p->esz);
+    p->off_part = take(M * p->H * p->n_splits * (p->Dh + 2) * 4);
+    p->off_xf = take(ML * p->D * p->esz);
+    p->off_lmpart = take(ML * p->n_tiles_lm * sizeof(ArgPart));
+    p->total = o;
+    return vs_ok();
+}
+
+// ---- GEMM dispatch -------------------------------------------------------
+
+template <int DT, int MT, int EPI>
+void launch_gemm_mt(const GemmArgs& g, int NW, int n_mgroups, hipStream_t s) {
+    constexpr int U = (DT == F32 ? 4 : 8) / MT > 0 ? (DT == F32 ? 4 : 8) / MT : 1;
+    dim3 grid(g.n_tiles, n_mgroups);
+    if (NW >= 16) {
+        hipLaunchKernelGGL((gemm_skinny_kernel<DT, MT, 16, EPI, U>), grid, dim3(16 * 64), 0, s, g);
+    } else if (NW >= 8) {
+        hipLaunchKernelGGL((gemm_skinny_kernel<DT, MT, 8, EPI, U>), grid, dim3(8 * 64), 0, s, g);
+    } else {
+        hipLaunchKernelGGL((gemm_skinny_kernel<DT, MT, 4, EPI, U>), grid, dim3(4 * 64), 0, s, g);
+    }
+}
+
+template <int DT, int EPI>
+void launch_gemm(const GemmArgs& g, hipStream_t s) {
+    const int M = g.M;
+    if (M <= 0) return;
+    const int n_mgroups = (M + 63) / 64;
+    const int rows = std::min(M, 64);
+    const int MT = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
+    const long wgs = (long)g.n_tiles * n_mgroups;
+    int NW = wgs < 256 ? 16 : wgs < 512 ? 8 : 4;
+    const int KC = g.K / 32;
+    while (NW > 4 && NW > KC) NW >>= 1;
+    if (MT == 1) launch_gemm_mt<DT, 1, EPI>(g, NW, n_mgroups, s);
+    else if (MT == 2) launch_gemm_mt<DT, 2, EPI>(g, NW, n_mgroups, s);
+    else launch_gemm_mt<DT, 4, EPI>(g, NW, n_mgroups, s);
+}
+
+template <int DT, int DH>
+void launch_attention(const AttnArgs& a, int B, int M, int rmax, hipStream_t s) {
+    dim3 grid(a.n_splits, a.n_heads, B);
+    {
+    TimedScope ts(VS_KERNEL_ATTN, s);
+    switch (rmax) {
+        case 1: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 1>), grid, dim3(64), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 2>), grid, dim3(64), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 4>), grid, dim3(64), 0, s, a); break;
+        default: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 8>), grid, dim3(64), 0, s, a); break;
+    }
+    }
+    TimedScope ts(VS_KERNEL_MERGE, s);
+    hipLaunchKernelGGL((attn_merge_kernel<DT, DH>), dim3(M, a.n_heads), dim3(DH), 0, s, a);
+}
+
+template <int DT>
+vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, const vs_weights* w,
+                   const vs_step_out* out, char* ws, hipStream_t s) {
+    const vs_pool_desc* pg = vs_pool_geometry(d->pool);
+    int* row_seq = reinterpret_cast<int*>(ws + p.off_row_seq);
+    int* row_pos = reinterpret_cast<int*>(ws + p.off_row_pos);
+    float* rope_cs = reinterpret_cast<float*>(ws + p.off_rope);
+    float* x = reinterpret_cast<float*>(ws + p.off_x);
+    void* xn = ws + p.off_xn;
+    void* qb = ws + p.off_q;
+    void* attn = ws + p.off_attn;
+    void* hmid = ws + p.off_h;
+    float* part = reinterpret_cast<float*>(ws + p.off_part);
+    void* xf = ws + p.off_xf;
+    ArgPart* lmpart = reinterpret_cast<ArgPart*>(ws + p.off_lmpart);
+    const float eps = w->dims.eps;
+
+    if (p.M > 0) {
+        hipLaunchKernelGGL(prep_rows_kernel, dim3(p.M), dim3(64), 0, s, d->q_start, d->ctx_len, p.B, p.Dh,
+                           (double)w->dims.rope_theta, row_seq, row_pos, rope_cs);
+        hipLaunchKernelGGL((embed_kernel<DT>), dim3(p.M), dim3(256), 0, s, d->tokens, w->embed, p.V, p.D, x);
+    }
+
+    GemmArgs g = {};
+    g.block_tables = bt;
+    g.max_blocks = d->max_blocks;
+    g.num_pages = pg->num_pages;
+    g.row_seq = row_seq;
+    g.row_pos = row_pos;
+    g.rope_cs = rope_cs;
+    g.kv_base = kv_pool_base(d->pool);
+    g.page_elems = (long)(kv_page_bytes(pg) / p.esz);
+    g.layer_elems = 2L * p.Hkv * kPageTokens * p.Dh;
+    g.head_dim = p.Dh;
+    g.n_heads = p.H;
+    g.n_kv_heads = p.Hkv;
+    g.page_tokens = kPageTokens;
+
+    AttnArgs a = {};
+    a.q = qb;
+    a.kv_base = g.kv_base;
+    a.page_elems = g.page_elems;
+    a.layer_elems = g.layer_elems;
+    a.n_heads = p.H;
+    a.n_kv_heads = p.Hkv;
+    a.page_tokens = kPageTokens;
+    a.block_tables = bt;
+    a.max_blocks = d->max_blocks;
+    a.num_pages = pg->num_pages;
+    a.M = p.M;
+    a.q_start = d->q_start;
+    a.ctx_len = d->ctx_len;
+    a.n_splits = p.n_splits;
+    a.split_pages = p.split_pages;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.Dh));
+    a.part = part;
+    a.out = attn;
+
+    for (int l = 0; l < p.L && p.M > 0; ++l) {
+        const vs_layer_weights& lw = w->layers[l];
+        hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
+                           lw.attn_norm, p.D, eps, xn);
+        GemmArgs q = g;
+        q.w0 = lw.wq;
+        q.w1 = lw.wk;
+        q.w2 = lw.wv;
+        q.n0 = p.H * p.Dh;
+        q.n1 = p.Hkv * p.Dh;
+        q.n2 = p.Hkv * p.Dh;
+        q.K = p.D;
+        q.act = xn;
+        q.act_ld = p.D;
+        q.M = p.M;
+        q.n_tiles = (p.H + 2 * p.Hkv) * p.Dh / 32;
+        q.q_out = qb;
+        q.layer = l;
+        {
+            TimedScope ts(VS_KERNEL_QKV, s);
+            launch_gemm<DT, EPI_QKV>(q, s);
+        }
+
+        a.layer = l;
+        if (p.Dh == 128) launch_attention<DT, 128>(a, p.B, p.M, p.rmax, s);
+        else launch_attention<DT, 64>(a, p.B, p.M, p.rmax, s);
+
+        GemmArgs o = g;
+        o.w0 = lw.wo;
+        o.n0 = p.D;
+        o.K = p.H * p.Dh;
+        o.act = attn;
+        o.act_ld = p.H * p.Dh;
+        o.M = p.M;
+        o.n_tiles = (p.D + 31) / 32;
+        o.x = x;
+        o.x_ld = p.D;
+        {
+            TimedScope ts(VS_KERNEL_OPROJ, s);
+            launch_gemm<DT, EPI_RESID>(o, s);
+        }
+
+        hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
+                           lw.ffn_norm, p.D, eps, xn);
+        GemmArgs gu = g;
+        gu.w0 = lw.wg;
+        gu.w1 = lw.wu;
+        gu.n0 = p.F;
+        gu.n1 = p.F;
+        gu.K = p.D;
+        gu.act = xn;
+        gu.act_ld = p.D;
+        gu.M = p.M;
+        gu.n_tiles = (p.F + 15) / 16;
+        gu.h_out = hmid;
+        gu.h_ld = p.F;
+        {
+            TimedScope ts(VS_KERNEL_GATEUP, s);
+            launch_gemm<DT, EPI_SWIGLU>(gu, s);
+        }
+
+        GemmArgs dn = g;
+        dn.w0 = lw.wd;
+        dn.n0 = p.D;
+        dn.K = p.F;
+        dn.act = hmid;
+        dn.act_ld = p.F;
+        dn.M = p.M;
+        dn.n_tiles = (p.D + 31) / 32;
+        dn.x = x;
+        dn.x_ld = p.D;
+        {
+            TimedScope ts(VS_KERNEL_DOWN, s);
+            launch_gemm<DT, EPI_RESID>(dn, s);
+        }
+    }
+
+    if (p.M_log > 0) {
+        hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M_log), dim3(256), 0, s, x, d->logit_rows, p.M,
+                           w->final_norm, p.D, eps, xf);
+        GemmArgs lm = g;
+        lm.w0 = w->lm_head;
+        lm.n0 = p.V;
+        lm.K = p.D;
+        lm.act = xf;
+        lm.act_ld = p.D;
+        lm.M = p.M_log;
+        lm.n_tiles = p.n_tiles_lm;
+        lm.logits = out->logits;
+        lm.vocab = p.V;
+        lm.parts = lmpart;
+        TimedScope ts(VS_KERNEL_LMHEAD, s);
+        launch_gemm<DT, EPI_LOGITS>(lm, s);
+    }
+    if (p.M > 0 && out->argmax) {
+        hipLaunchKernelGGL(argmax_accept_kernel, dim3(p.B), dim3(256), 0, s, lmpart, p.n_tiles_lm, d->q_start, p.M,
+                           d->logit_rows, p.M_log, d->tokens, out->g0, out->argmax, out->top2_gap, out->accept_len,
+                           out->bonus);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return vs_fail(VS_ERR_HIP, std::string("decode_step launch: ") + hipGetErrorString(e));
+    return vs_ok();
+}
+
+}  // namespace
+
+extern "C" vs_status decode_step_workspace_bytes(const vs_batch_desc* desc, const vs_model_desc* dims, size_t* bytes) {
+    if (!bytes) return vs_fail(VS_ERR_INVALID, "decode_step_workspace_bytes: null output");
+    Plan p;
+    vs_status st = make_plan(desc, dims, &p);
+    if (st != VS_OK) return st;
+    *bytes = p.total;
+    return vs_ok();
+}
+
+extern "C" vs_status decode_step(const vs_batch_desc* desc, const int32_t* block_tables, const vs_weights* weights,
+                                 const vs_step_out* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!desc || !weights || !out) return vs_fail(VS_ERR_INVALID, "decode_step: null argument");
+    Plan p;
+    vs_status st = make_plan(desc, &weights->dims, &p);
+    if (st != VS_OK) return st;
+    if (p.M == 0) return vs_ok();
+    if (!desc->pool || !desc->q_start || !desc->ctx_len || !desc->tokens || !block_tables)
+        return vs_fail(VS_ERR_INVALID, "decode_step: pool, q_start, ctx_len, tokens and block_tables are required");
+    if (p.M_log > 0 && (!desc->logit_rows || !out->argmax))
+        return vs_fail(VS_ERR_INVALID, "decode_step: logit rows need logit_rows and out->argmax");
+    const bool fused = out->accept_len || out->bonus || out->g0;
+    if (fused && !(out->accept_len && out->bonus && out->g0 && out->argmax))
+        return vs_fail(VS_ERR_INVALID, "decode_step: fused acceptance needs g0, accept_len, bonus and argmax");
+    if (!weights->embed || !weights->final_norm || !weights->lm_head || !weights->layers)
+        return vs_fail(VS_ERR_INVALID, "decode_step: missing weight pointer");
+    for (int l = 0; l < p.L; ++l) {
+        const vs_layer_weights& lw = weights->layers[l];
+        if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.wg || !lw.wu || !lw.wd)
+            return vs_fail(VS_ERR_INVALID, "decode_step: missing weight pointer in layer " + std::to_string(l));
+    }
+    const vs_pool_desc* pg = vs_pool_geometry(desc->pool);
+    if (pg->page_tokens != kPageTokens || pg->n_layers != p.L || pg->n_kv_heads != p.Hkv || pg->head_dim != p.Dh ||
+        pg->dtype != p.dt)
+        return vs_fail(VS_ERR_SHAPE, "decode_step: pool geometry does not match the model");
+    if (!ws || ws_bytes < p.total)
+        return vs_fail(VS_ERR_SHAPE, "decode_step: workspace needs " + std::to_string(p.total) + " bytes");
+    char* w = static_cast<char*>(ws);
+    switch (p.dt) {
+        case VS_F32: return run_step<F32>(p, desc, block_tables, weights, out, w, stream);
+        case VS_F16: return run_step<F16>(p, desc, block_tables, weights, out, w, stream);
+        default: return run_step<BF16>(p, desc, block_tables, weights, out, w, stream);
+    }
+}
+
+extern "C" vs_status verify_accept(int32_t B, const int32_t* q_start, const int32_t* drafts, const int32_t* g0,
+                                   const int32_t* argmax, int32_t* accept_len, int32_t* bonus, hipStream_t stream) {
+    if (B < 0) return vs_fail(VS_ERR_INVALID, "verify_accept: B < 0");
+    if (B == 0) return vs_ok();
+    if (!q_start || !drafts || !g0 || !argmax || !accept_len || !bonus)
+        return vs_fail(VS_ERR_INVALID, "verify_accept: null argument");
+    hipLaunchKernelGGL(verify_accept_kernel, dim3((B + 63) / 64), dim3(64), 0, stream, B, q_start, drafts, g0, argmax,
+                       accept_len, bonus);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return vs_fail(VS_ERR_HIP, std::string("verify_accept launch: ") + hipGetErrorString(e));
+    return vs_ok();
+}
+
+extern "C" vs_status vs_time_kernel(int32_t kind, void* const* start_events, void* const* stop_events,
+                                    int32_t capacity) {
+    if (kind < VS_KERNEL_NONE || kind > VS_KERNEL_LMHEAD) return vs_fail(VS_ERR_INVALID, "vs_time_kernel: bad kind");
+    if (kind != VS_KERNEL_NONE && (capacity < 0 || (capacity > 0 && (!start_events || !stop_events))))
+        return vs_fail(VS_ERR_INVALID, "vs_time_kernel: events required");
+    g_timer.kind = kind;
+    g_timer.start = start_events;
+    g_timer.stop = stop_events;
+    g_timer.capacity = kind == VS_KERNEL_NONE ? 0 : capacity;
+    g_timer.count = 0;
+    return vs_ok();
+}
+
+extern "C" int32_t vs_timed_launches(void) { return g_timer.count; }
