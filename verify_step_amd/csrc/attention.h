@@ -4,25 +4,30 @@
 // from pages anywhere in the pool. Section 07, Flash-Decoding: the keys of
 // one (sequence, head) are cut into splits processed in parallel; each split
 // keeps the online-softmax state (running max m, running sum l, rescaled
-// output o) over its keys and stores it, and a merge rescales the splits to a
-// common maximum and divides the summed outputs by the summed sums
-// ([Serving Efficiency] section 31.4, Example 31.2: combine statistics, not
-// normalised tile outputs).
+// output o) over its keys, and the splits are merged by rescaling to a common
+// maximum and dividing the summed outputs by the summed sums ([Serving
+// Efficiency] section 31.4, Example 31.2: combine statistics, not normalised
+// tile outputs).
 //
-// One wave64 workgroup per (split, head, sequence). Lane l owns dims
-// [(l%16)*DH/16, +DH/16) of key slot (l/16) within each group of four keys, so
-// one page of 16 keys is four 16-byte loads per lane for K and four for V, and
-// the 16 lanes that share a key finish its dot product with xor shuffles. Every
-// K/V byte is used by exactly one wave, so it goes from HBM straight to
-// registers; the next page is loaded while the current one is reduced.
-// All rows of one sequence (up to RMAX at a time) share each K/V load; row i
-// at position ctx + i keeps keys 0..ctx + i (causal across the rows of a pass).
-// Scores are kept in the log2 domain (q pre-scaled by log2(e)/sqrt(DH)).
+// One workgroup of four waves per (split, head, sequence). Wave w takes pages
+// w, w+4, ... of the split. Lane l owns dims [(l%16)*DH/16, +DH/16) of key slot
+// (l/16) within each group of four keys, so one page of 16 keys is four loads
+// per lane for K and four for V, and the 16 lanes that share a key finish its
+// dot product with xor shuffles. Every K/V byte is used by exactly one wave, so
+// it goes from HBM straight to registers; the wave's next page is in flight
+// while the current one is reduced. The four waves' states are merged through
+// LDS and the workgroup's state is stored; a merge kernel then combines the
+// splits and writes the attention output in the storage type. All rows of one sequence (up to RMAX
+// at a time) share each K/V load; row i at position ctx + i keeps keys
+// 0..ctx + i (causal across the rows of a pass). Scores are kept in the log2
+// domain (q pre-scaled by log2(e)/sqrt(DH)).
 #pragma once
 
 #include "common.h"
 
 namespace vs {
+
+constexpr int kAttnWaves = 4;
 
 struct AttnArgs {
     const void* q;  // [M][n_heads*DH] storage type, rotated
@@ -38,15 +43,18 @@ struct AttnArgs {
     int n_splits, split_pages;
     float scale_log2;  // log2(e) / sqrt(DH)
     float* part;       // [M][n_heads][n_splits][DH + 2]: m (log2 domain), l, o[DH]
-    void* out;         // merge output [M][n_heads*DH] storage type
+    void* out;         // [M][n_heads*DH] storage type
 };
 
 template <int DT, int DH, int RMAX>
-__global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kAttnWaves * 64) attn_split_kernel(AttnArgs a) {
     constexpr int DPL = DH / 16;  // dims per lane
-    const int lane = threadIdx.x;
-    const int g = lane >> 4;   // key slot within a group of four
-    const int c = lane & 15;   // dim chunk
+    constexpr int NW = kAttnWaves;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+    const int g = lane >> 4;  // key slot within a group of four
+    const int c = lane & 15;  // dim chunk
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int group = a.n_heads / a.n_kv_heads;
     const int hk = h / group;
@@ -64,6 +72,9 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
     const long kofs = (long)a.layer * a.layer_elems + (long)hk * T * DH + (long)c * DPL;
     const long vofs = kofs + (long)a.n_kv_heads * T * DH;
     const int QLD = a.n_heads * DH;
+    const char* kvb = reinterpret_cast<const char*>(a.kv_base);
+
+    __shared__ float wst[NW][RMAX][DH + 2];  // per-wave (m, l, o) of each row
 
     for (int rg = 0; rg < R; rg += RMAX) {
         const int nr = min(RMAX, R - rg);
@@ -90,23 +101,23 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
 
         RawVec<DT, DPL> kf[4], vf[4];  // current page (raw storage words)
         RawVec<DT, DPL> kn[4], vn[4];  // next page, in flight
-        const char* kvb = reinterpret_cast<const char*>(a.kv_base);
-        if (p_begin < p_end) {
-            const long pb = (long)min(max(bt[p_begin], 0), a.num_pages - 1) * a.page_elems;
+        const int pw0 = p_begin + wave;
+        if (pw0 < p_end) {
+            const long pb = (long)min(max(bt[pw0], 0), a.num_pages - 1) * a.page_elems;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 load_raw<DT, DPL>(kn[u], kvb + (pb + kofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
                 load_raw<DT, DPL>(vn[u], kvb + (pb + vofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
             }
         }
-        for (int p = p_begin; p < p_end; ++p) {
+        for (int p = pw0; p < p_end; p += NW) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 kf[u] = kn[u];
                 vf[u] = vn[u];
             }
-            if (p + 1 < p_end) {  // prefetch the next page while this one is reduced
-                const long pb = (long)min(max(bt[p + 1], 0), a.num_pages - 1) * a.page_elems;
+            if (p + NW < p_end) {  // the wave's next page is loaded while this one is reduced
+                const long pb = (long)min(max(bt[p + NW], 0), a.num_pages - 1) * a.page_elems;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     load_raw<DT, DPL>(kn[u], kvb + (pb + kofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
@@ -156,7 +167,7 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
                 m[i] = mn;
             }
         }
-        // sum the four key slots' partial outputs and store this split's state
+        // this wave's state: sum the four key slots' outputs, park it in LDS
 #pragma unroll
         for (int i = 0; i < RMAX; ++i) {
             if (i >= nr) break;
@@ -165,34 +176,77 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
                 o[i][e] += shfl_xor(o[i][e], 16);
                 o[i][e] += shfl_xor(o[i][e], 32);
             }
-            float* dst = a.part + (((long)(r0 + rg + i) * a.n_heads + h) * a.n_splits + s) * (DH + 2);
             if (lane == 0) {
-                dst[0] = m[i];
-                dst[1] = l[i];
+                wst[wave][i][0] = m[i];
+                wst[wave][i][1] = l[i];
             }
             if (g == 0) {
 #pragma unroll
-                for (int e = 0; e < DPL; ++e) dst[2 + c * DPL + e] = o[i][e];
+                for (int e = 0; e < DPL; ++e) wst[wave][i][2 + c * DPL + e] = o[i][e];
             }
         }
+        __syncthreads();
+        // merge the four waves in wave order; thread t takes (row, dim) pairs
+        for (int idx = tid; idx < nr * DH; idx += NW * 64) {
+            const int i = idx / DH, d = idx % DH;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) mx = fmaxf(mx, wst[w][i][0]);
+            float ls = 0.f, os = 0.f;
+            if (mx != -INFINITY) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const float wm = wst[w][i][0];
+                    if (wm == -INFINITY) continue;
+                    const float f = exp2f(wm - mx);
+                    ls += f * wst[w][i][1];
+                    os += f * wst[w][i][2 + d];
+                }
+            }
+            float* dst = a.part + (((long)(r0 + rg + i) * a.n_heads + h) * a.n_splits + s) * (DH + 2);
+            if (d == 0) {
+                dst[0] = mx;
+                dst[1] = ls;
+            }
+            dst[2 + d] = os;
+        }
+        __syncthreads();
     }
+
 }
 
 // One workgroup of DH threads per (row, head): rescale every split's state to
 // the largest running maximum and divide the summed outputs by the summed sums.
+// Split weights are computed once into LDS; thread d then sums dim d over the
+// splits with independent loads.
 template <int DT, int DH>
 __global__ void __launch_bounds__(DH) attn_merge_kernel(AttnArgs a) {
+    constexpr int kMaxSplits = 1024;
+    __shared__ float sm[kMaxSplits], sw[kMaxSplits];
+    __shared__ float s_red[DH / 64];
     const int row = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    const int ns = min(a.n_splits, kMaxSplits);
     const float* src = a.part + ((long)row * a.n_heads + h) * a.n_splits * (DH + 2);
     float mx = -INFINITY;
-    for (int s = 0; s < a.n_splits; ++s) mx = fmaxf(mx, src[s * (DH + 2)]);
+    for (int sp = d; sp < ns; sp += DH) {
+        sm[sp] = src[(long)sp * (DH + 2)];
+        mx = fmaxf(mx, sm[sp]);
+    }
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) mx = fmaxf(mx, shfl_xor(mx, mask));
+    if ((d & 63) == 0) s_red[d >> 6] = mx;
+    __syncthreads();
+    mx = s_red[0];
+#pragma unroll
+    for (int w = 1; w < DH / 64; ++w) mx = fmaxf(mx, s_red[w]);
+    for (int sp = d; sp < ns; sp += DH) sw[sp] = sm[sp] == -INFINITY ? 0.f : exp2f(sm[sp] - mx);
+    __syncthreads();
     float l = 0.f, o = 0.f;
-    for (int s = 0; s < a.n_splits; ++s) {
-        const float ms = src[s * (DH + 2)];
-        if (ms == -INFINITY) continue;
-        const float w = exp2f(ms - mx);
-        l += w * src[s * (DH + 2) + 1];
-        o += w * src[s * (DH + 2) + 2 + d];
+#pragma unroll 4
+    for (int sp = 0; sp < ns; ++sp) {
+        const float w = sw[sp];
+        l += w * src[(long)sp * (DH + 2) + 1];
+        o += w * src[(long)sp * (DH + 2) + 2 + d];
     }
     store_round<DT>(a.out, (long)row * a.n_heads * DH + (long)h * DH + d, o / l);
 }

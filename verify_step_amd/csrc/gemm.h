@@ -5,20 +5,20 @@
 // shares one read of it; [Spending the Idle] section 12.2: the weights have
 // no idea how many tokens pass through them).
 //
-// Work split. A workgroup owns one tile of 32 output features (two blocks of
-// 16 weight rows, chosen by the epilogue so that values an epilogue combines,
+// This is the path for steps of more than a few rows (the row-streaming GEMV
+// covers the rest). A workgroup owns one tile of 32 output features (two
+// blocks of 16 weight rows, chosen by the epilogue so that values it combines,
 // such as a rotary pair or a gate/up pair, land in the same lane) and all rows
-// of its row group. Its NW waves split the reduction axis; each wave streams
+// of one 64-row group. Its NW waves split the reduction axis; each wave loads
 // its slice of the two 16-row blocks with 16-byte loads straight into MFMA
-// operand registers (no LDS round trip: every weight byte is used by exactly
-// one wave), multiplies on the matrix cores (16x16x32 fp16/bf16, 16x16x4 fp32
-// with M padded to 16), and the waves' partial tiles are summed in a fixed
-// binary tree through LDS, so results are deterministic.
+// operand registers and multiplies on the matrix cores (16x16x32 fp16/bf16,
+// 16x16x4 fp32; rows padded to 16). The waves' partial tiles are summed in a
+// fixed binary tree through LDS, so results are deterministic.
 //
 // Operand roles: A = weights (MFMA rows = output features), B = activations
-// (MFMA columns = rows of the batch). Lane l supplies weight row (l % 16) and
-// activation row (l % 16), both at reduction offsets (l / 16) * 8 .. +7 of each
-// 32-wide chunk, and receives C[feature (l/16)*4 + r][row l % 16], r = 0..3.
+// (MFMA columns = batch rows). Lane l supplies weight row (l % 16) and batch
+// row (l % 16), both at reduction offsets (l / 16) * 8 .. +7 of each 32-wide
+// chunk, and receives C[feature (l/16)*4 + r][batch row l % 16], r = 0..3.
 #pragma once
 
 #include "common.h"
@@ -26,6 +26,7 @@
 namespace vs {
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+enum XMode { X_PLAIN = 0, X_NORM = 1 };
 
 struct ArgPart {
     float v1;  // largest value in the tile
@@ -42,7 +43,7 @@ struct GemmArgs {
     int K;           // reduction length, a multiple of 32
     const void* act;  // activations [rows][act_ld] in the storage type
     int act_ld;
-    int M;  // valid activation rows
+    int M;  // rows
     int n_tiles;
     // rotary + K/V write (EPI_QKV)
     void* q_out;  // [M][n_heads*head_dim]
@@ -56,7 +57,7 @@ struct GemmArgs {
     const int* row_seq;
     const int* row_pos;
     const float* rope_cs;  // [M][head_dim/2][2] (cos, sin)
-    // residual add (EPI_RESID)
+    // residual add (EPI_RESID): x += C
     float* x;
     int x_ld;
     // SwiGLU (EPI_SWIGLU)
@@ -91,22 +92,27 @@ template <> struct Frag<BF16> {
 };
 
 template <int DT>
-__device__ __forceinline__ void frag_load(Frag<DT>& f, const void* base, long elem, bool valid) {
+__device__ __forceinline__ void frag_zero(Frag<DT>& f) {
     if constexpr (DT == F32) {
-        if (valid) {
-            const float4_t* p = reinterpret_cast<const float4_t*>(reinterpret_cast<const float*>(base) + elem);
-            f.a = p[0];
-            f.b = p[1];
-        } else {
-            f.a = (float4_t){0.f, 0.f, 0.f, 0.f};
-            f.b = f.a;
-        }
+        f.a = (float4_t){0.f, 0.f, 0.f, 0.f};
+        f.b = f.a;
     } else {
-        if (valid) {
-            f.a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
-        } else {
-            f.a = make_uint4(0u, 0u, 0u, 0u);
-        }
+        f.a = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void frag_load(Frag<DT>& f, const void* base, long elem, bool valid) {
+    if (!valid) {
+        frag_zero<DT>(f);
+        return;
+    }
+    if constexpr (DT == F32) {
+        const float4_t* p = reinterpret_cast<const float4_t*>(reinterpret_cast<const float*>(base) + elem);
+        f.a = p[0];
+        f.b = p[1];
+    } else {
+        f.a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
     }
 }
 
@@ -130,12 +136,12 @@ __device__ __forceinline__ float4_t frag_mma(const Frag<DT>& w, const Frag<DT>& 
 
 // Which two 16-row weight blocks a tile covers, and what they mean.
 struct TileMap {
-    const void* w;      // segment base for block A (block B uses wb)
-    const void* wb;
-    int rowA, rowB;     // first weight row of each block inside its segment
-    int nrows;          // rows in the segment (rows >= nrows are padding)
-    int seg;            // EPI_QKV: 0 = q, 1 = k, 2 = v
-    int head, j;        // EPI_QKV: head inside the segment, 16-wide slot of the head's first half
+    const void* w;   // segment base for block A
+    const void* wb;  // segment base for block B
+    int rowA, rowB;  // first weight row of each block inside its segment
+    int nrows;       // rows in the segment (rows >= nrows are padding)
+    int seg;         // EPI_QKV: 0 = q, 1 = k, 2 = v
+    int head, j;     // EPI_QKV: head inside the segment, 16-wide slot of the head's first half
 };
 
 template <int EPI>
@@ -151,8 +157,8 @@ __device__ __forceinline__ TileMap tile_map(const GemmArgs& g, int t) {
         m.rowB = 32 * t + 16;
         m.nrows = g.n0;
     } else if constexpr (EPI == EPI_SWIGLU) {
-        m.w = g.w0;  // gate
-        m.wb = g.w1; // up
+        m.w = g.w0;   // gate
+        m.wb = g.w1;  // up
         m.rowA = 16 * t;
         m.rowB = 16 * t;
         m.nrows = g.n0;
@@ -184,17 +190,118 @@ __device__ __forceinline__ TileMap tile_map(const GemmArgs& g, int t) {
     return m;
 }
 
+// Epilogue on wave 0, whose lane holds C[feature nl0 + r][row l % 16] of both blocks.
+template <int DT, int MT, int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, const TileMap& tm, int tile, int mg, int lane,
+                                              float4_t (&acc)[MT][2]) {
+    const int l16 = lane & 15;
+    const int nl0 = (lane >> 4) * 4;
+    if constexpr (EPI == EPI_LOGITS) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = mg * 64 + mt * 16 + l16;
+            float v1 = -INFINITY, v2 = -INFINITY;
+            int i1 = 0x7FFFFFFF;
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int col = (b ? tm.rowB : tm.rowA) + nl0 + r;
+                    const float v = acc[mt][b][r];
+                    if (col < g.vocab) {
+                        if (m < g.M && g.logits) g.logits[(long)m * g.vocab + col] = v;
+                        argpart_combine(v1, i1, v2, v, col, -INFINITY);
+                    }
+                }
+            }
+#pragma unroll
+            for (int mask = 16; mask <= 32; mask <<= 1) {
+                const float o1 = shfl_xor(v1, mask);
+                const int oi = shfl_xor(i1, mask);
+                const float o2 = shfl_xor(v2, mask);
+                argpart_combine(v1, i1, v2, o1, oi, o2);
+            }
+            if (lane < 16 && m < g.M) {
+                ArgPart p;
+                p.v1 = v1;
+                p.i1 = i1;
+                p.v2 = v2;
+                p.pad = 0;
+                g.parts[(long)m * g.n_tiles + tile] = p;
+            }
+        }
+    } else if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = mg * 64 + mt * 16 + l16;
+            if (m >= g.M) continue;
+            float* xr = g.x + (long)m * g.x_ld;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int col = (b ? tm.rowB : tm.rowA) + nl0 + r;
+                    if (col < tm.nrows) xr[col] += acc[mt][b][r];
+                }
+        }
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = mg * 64 + mt * 16 + l16;
+            if (m >= g.M) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int nl = nl0 + r;
+                const float a = acc[mt][0][r];
+                const float b = acc[mt][1][r];
+                if constexpr (EPI == EPI_SWIGLU) {
+                    if (tm.rowA + nl < tm.nrows) {
+                        const float s = a / (1.0f + expf(-a));
+                        store_round<DT>(g.h_out, (long)m * g.h_ld + tm.rowA + nl, s * b);
+                    }
+                } else {  // EPI_QKV
+                    const int half = g.head_dim / 2;
+                    const int i = 16 * tm.j + nl;  // rotary pair index inside the head
+                    float ra = a, rb = b;
+                    if (tm.seg < 2) {
+                        const float c = g.rope_cs[((long)m * half + i) * 2 + 0];
+                        const float s = g.rope_cs[((long)m * half + i) * 2 + 1];
+                        ra = a * c - b * s;
+                        rb = b * c + a * s;
+                    }
+                    if (tm.seg == 0) {
+                        const long o = (long)m * (g.n_heads * g.head_dim) + tm.head * g.head_dim + i;
+                        store_round<DT>(g.q_out, o, ra);
+                        store_round<DT>(g.q_out, o + half, rb);
+                    } else {
+                        const int pos = g.row_pos[m];
+                        const int sq = g.row_seq[m];
+                        if (pos < 0 || pos / g.page_tokens >= g.max_blocks) continue;
+                        const int page = g.block_tables[(long)sq * g.max_blocks + pos / g.page_tokens];
+                        if (page < 0 || page >= g.num_pages) continue;
+                        const int slot = pos % g.page_tokens;
+                        const long o = (long)page * g.page_elems + (long)g.layer * g.layer_elems +
+                                       ((long)(tm.seg - 1) * g.n_kv_heads + tm.head) * g.page_tokens * g.head_dim +
+                                       (long)slot * g.head_dim + i;
+                        store_round<DT>(g.kv_base, o, ra);
+                        store_round<DT>(g.kv_base, o + half, rb);
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <int DT, int MT, int NW, int EPI, int U>
 __global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
     const int tile = blockIdx.x;
     const int mg = blockIdx.y;  // 64-row group
     const TileMap tm = tile_map<EPI>(g, tile);
 
     const int KC = g.K / 32;
-    const int kc0 = (wave * KC) / NW;
-    const int kc1 = ((wave + 1) * KC) / NW;
+    const int kc0 = (wave * KC) / NW, kc1 = ((wave + 1) * KC) / NW;
 
     const int l16 = lane & 15;
     const int kofs = (lane >> 4) * 8;
@@ -267,94 +374,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
         }
     }
     if (wave != 0) return;
-
-    // ---- epilogue on wave 0: lane holds C[feature (lane/16)*4 + r][row lane%16] of each block
-    const int nl0 = (lane >> 4) * 4;
-    if constexpr (EPI == EPI_LOGITS) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = mg * 64 + mt * 16 + l16;
-            float v1 = -INFINITY, v2 = -INFINITY;
-            int i1 = 0x7FFFFFFF;
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int col = (b ? tm.rowB : tm.rowA) + nl0 + r;
-                    const float v = acc[mt][b][r];
-                    if (col < g.vocab) {
-                        if (m < g.M && g.logits) g.logits[(long)m * g.vocab + col] = v;
-                        argpart_combine(v1, i1, v2, v, col, -INFINITY);
-                    }
-                }
-            }
-#pragma unroll
-            for (int mask = 16; mask <= 32; mask <<= 1) {
-                const float o1 = shfl_xor(v1, mask);
-                const int oi = shfl_xor(i1, mask);
-                const float o2 = shfl_xor(v2, mask);
-                argpart_combine(v1, i1, v2, o1, oi, o2);
-            }
-            if (lane < 16 && m < g.M) {
-                ArgPart p;
-                p.v1 = v1;
-                p.i1 = i1;
-                p.v2 = v2;
-                p.pad = 0;
-                g.parts[(long)m * g.n_tiles + tile] = p;
-            }
-        }
-        return;
-    } else {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = mg * 64 + mt * 16 + l16;
-            if (m >= g.M) continue;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int nl = nl0 + r;
-                const float a = acc[mt][0][r];
-                const float b = acc[mt][1][r];
-                if constexpr (EPI == EPI_RESID) {
-                    float* xr = g.x + (long)m * g.x_ld;
-                    if (tm.rowA + nl < tm.nrows) xr[tm.rowA + nl] += a;
-                    if (tm.rowB + nl < tm.nrows) xr[tm.rowB + nl] += b;
-                } else if constexpr (EPI == EPI_SWIGLU) {
-                    if (tm.rowA + nl < tm.nrows) {
-                        const float s = a / (1.0f + expf(-a));
-                        store_round<DT>(g.h_out, (long)m * g.h_ld + tm.rowA + nl, s * b);
-                    }
-                } else {  // EPI_QKV
-                    const int half = g.head_dim / 2;
-                    const int i = 16 * tm.j + nl;  // rotary pair index inside the head
-                    float ra = a, rb = b;
-                    if (tm.seg < 2) {
-                        const float c = g.rope_cs[((long)m * half + i) * 2 + 0];
-                        const float s = g.rope_cs[((long)m * half + i) * 2 + 1];
-                        ra = a * c - b * s;
-                        rb = b * c + a * s;
-                    }
-                    if (tm.seg == 0) {
-                        const long o = (long)m * (g.n_heads * g.head_dim) + tm.head * g.head_dim + i;
-                        store_round<DT>(g.q_out, o, ra);
-                        store_round<DT>(g.q_out, o + half, rb);
-                    } else {
-                        const int pos = g.row_pos[m];
-                        const int sq = g.row_seq[m];
-                        if (pos < 0 || pos / g.page_tokens >= g.max_blocks) continue;
-                        const int page = g.block_tables[(long)sq * g.max_blocks + pos / g.page_tokens];
-                        if (page < 0 || page >= g.num_pages) continue;
-                        const int slot = pos % g.page_tokens;
-                        const long o = (long)page * g.page_elems + (long)g.layer * g.layer_elems +
-                                       ((long)(tm.seg - 1) * g.n_kv_heads + tm.head) * g.page_tokens * g.head_dim +
-                                       (long)slot * g.head_dim + i;
-                        store_round<DT>(g.kv_base, o, ra);
-                        store_round<DT>(g.kv_base, o + half, rb);
-                    }
-                }
-            }
-        }
-    }
+    gemm_epilogue<DT, MT, EPI>(g, tm, tile, mg, lane, acc);
 }
 
 }  // namespace vs

@@ -1,5 +1,5 @@
-// Small kernels of the step: row bookkeeping + rotary angles, embedding
-// gather, RMSNorm, argmax reduction with fused greedy acceptance.
+// Small kernels of the step: row bookkeeping + rotary angles + embedding
+// gather, argmax reduction with fused greedy acceptance.
 #pragma once
 
 #include "common.h"
@@ -7,61 +7,90 @@
 
 namespace vs {
 
-// Row r -> its sequence and position; rotary (cos, sin) for every pair of
-// every row, from the float64 angle pos * theta^(-2i/head_dim).
-// Grid: one workgroup per row, head_dim/2 threads.
-__global__ void prep_rows_kernel(const int* q_start, const int* ctx_len, int B, int head_dim, double theta,
-                                 int* row_seq, int* row_pos, float* rope_cs) {
-    const int r = blockIdx.x;
-    int lo = 0, hi = B;  // largest b with q_start[b] <= r
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (q_start[mid] <= r) lo = mid;
-        else hi = mid;
-    }
-    const int pos = ctx_len[lo] + (r - q_start[lo]);
-    if (threadIdx.x == 0) {
-        row_seq[r] = lo;
-        row_pos[r] = pos;
-    }
-    const int half = head_dim / 2;
-    for (int i = threadIdx.x; i < half; i += blockDim.x) {
-        const double inv_freq = pow(theta, -2.0 * (double)i / (double)head_dim);
-        const double ang = (double)pos * inv_freq;
-        rope_cs[((long)r * half + i) * 2 + 0] = (float)cos(ang);
-        rope_cs[((long)r * half + i) * 2 + 1] = (float)sin(ang);
-    }
-}
+struct PrepArgs {
+    const int* q_start;
+    const int* ctx_len;
+    int B, M, head_dim;
+    double theta;
+    const int* tokens;
+    const void* embed;
+    int vocab, D;
+    int* row_seq;
+    int* row_pos;
+    float* rope_cs;  // [M][head_dim/2][2]
+    float* x;        // [M][D] fp32 residual stream
+};
 
-// x[r][:] = embedding row of token r, widened to the fp32 residual stream.
+// One workgroup (256 threads) per row r: its sequence and position, the rotary
+// (cos, sin) of every pair from the float64 angle pos * theta^(-2i/head_dim),
+// and the embedding row widened into the fp32 residual stream.
 template <int DT>
-__global__ void embed_kernel(const int* tokens, const void* embed, int vocab, int D, float* x) {
+__global__ void __launch_bounds__(256) prep_embed_kernel(PrepArgs p) {
     const int r = blockIdx.x;
-    int t = tokens[r];
-    t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
-    for (int k = threadIdx.x; k < D; k += blockDim.x) x[(long)r * D + k] = load_one<DT>(embed, (long)t * D + k);
+    const int tid = threadIdx.x;
+    __shared__ int s_pos;
+    if (tid == 0) {
+        int lo = 0, hi = p.B;  // largest b with q_start[b] <= r
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (p.q_start[mid] <= r) lo = mid;
+            else hi = mid;
+        }
+        const int pos = p.ctx_len[lo] + (r - p.q_start[lo]);
+        p.row_seq[r] = lo;
+        p.row_pos[r] = pos;
+        s_pos = pos;
+    }
+    __syncthreads();
+    const int pos = s_pos;
+    const int half = p.head_dim / 2;
+    for (int i = tid; i < half; i += blockDim.x) {
+        const double inv_freq = pow(p.theta, -2.0 * (double)i / (double)p.head_dim);
+        const double ang = (double)pos * inv_freq;
+        p.rope_cs[((long)r * half + i) * 2 + 0] = (float)cos(ang);
+        p.rope_cs[((long)r * half + i) * 2 + 1] = (float)sin(ang);
+    }
+    int t = p.tokens[r];
+    t = t < 0 ? 0 : (t >= p.vocab ? p.vocab - 1 : t);
+    const long base = (long)t * p.D;
+    for (int k0 = tid * 8; k0 < p.D; k0 += blockDim.x * 8) {
+        float v[8];
+        load_widen<DT, 8>(reinterpret_cast<const char*>(p.embed) + (base + k0) * St<DT>::bytes, v);
+        float* xr = p.x + (long)r * p.D + k0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xr[e] = v[e];
+    }
 }
 
 // y[r] = round(x[src] / sqrt(mean(x[src]^2) + eps) * gain), src = map ? map[r] : r
-// (a mapped row is clamped into [0, n_src)). Fixed-order block reduction
-// (deterministic). blockDim = 256.
+// (a mapped row is clamped into [0, n_src)); one 256-thread workgroup per row,
+// fixed-order reduction. Used ahead of the MFMA path; the GEMV path normalises
+// inside its own prologue.
 template <int DT>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* x, const int* map, int n_src, const void* gain,
                                                       int D, float eps, void* y) {
     const int r = blockIdx.x;
+    const int tid = threadIdx.x;
     const int src = map ? min(max(map[r], 0), n_src - 1) : r;
     const float* xr = x + (long)src * D;
     float ss = 0.f;
-    for (int k = threadIdx.x; k < D; k += blockDim.x) ss += xr[k] * xr[k];
+    for (int k = tid * 4; k < D; k += 256 * 4) {
+        const float4_t v = *reinterpret_cast<const float4_t*>(xr + k);
+        ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    }
 #pragma unroll
     for (int mask = 32; mask >= 1; mask >>= 1) ss += shfl_xor(ss, mask);
     __shared__ float wsum[4];
-    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+    if ((tid & 63) == 0) wsum[tid >> 6] = ss;
     __syncthreads();
-    const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-    const float inv = 1.0f / sqrtf(tot / (float)D + eps);
-    for (int k = threadIdx.x; k < D; k += blockDim.x)
-        store_round<DT>(y, (long)r * D + k, xr[k] * inv * load_one<DT>(gain, k));
+    const float inv = 1.0f / sqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)D + eps);
+    for (int k = tid * 4; k < D; k += 256 * 4) {
+        const float4_t v = *reinterpret_cast<const float4_t*>(xr + k);
+        float gv[4];
+        load_widen<DT, 4>(reinterpret_cast<const char*>(gain) + (long)k * St<DT>::bytes, gv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_round<DT>(y, (long)r * D + k + e, v[e] * inv * gv[e]);
+    }
 }
 
 // Per sequence: reduce each logit row's tile partials to (argmax, top-2 gap),

@@ -10,6 +10,7 @@
 #include "common.h"
 #include "error.h"
 #include "gemm.h"
+#include "gemv.h"
 #include "misc.h"
 
 const vs_pool_desc* vs_pool_geometry(const vs_pool* pool);
@@ -59,10 +60,16 @@ struct TimedScope {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Rows of a step at which the row-streaming GEMV gives way to the MFMA tiles,
+// and the LDS the GEMV may use for its batch rows.
+constexpr int kGemvMaxRows = 8;
+constexpr size_t kGemvMaxLds = 96 * 1024;
+
 struct Plan {
     int B, M, M_log, D, H, Hkv, Dh, F, V, L, dt, esz;
     int n_splits, split_pages, rmax;
-    int n_tiles_lm;
+    bool gemv;      // the row-streaming path serves every product of the step
+    int n_lm_parts; // argmax partials per logit row
     size_t off_row_seq, off_row_pos, off_rope, off_x, off_xn, off_q, off_attn, off_h, off_part, off_xf, off_lmpart;
     size_t total;
 };
@@ -78,6 +85,14 @@ vs_status check_dims(const vs_model_desc* m) {
     if (m->vocab < 2 || m->n_layers <= 0) return vs_fail(VS_ERR_SHAPE, "vocab >= 2 and n_layers >= 1 required");
     if (!(m->eps > 0.f) || !(m->rope_theta > 0.f)) return vs_fail(VS_ERR_INVALID, "eps and rope_theta must be > 0");
     return vs_ok();
+}
+
+// Units per GEMV workgroup: about 512 workgroups (two per CU), a multiple of the 4 waves,
+// at most kGemvMaxUnits.
+int gemv_units_per_wg(int n_units) {
+    int u = (n_units + 511) / 512;
+    u = (u + kGemvWaves - 1) / kGemvWaves * kGemvWaves;
+    return std::min(std::max(u, kGemvWaves), kGemvMaxUnits);
 }
 
 vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
@@ -101,19 +116,21 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->L = m->n_layers;
     p->dt = m->dtype;
     p->esz = m->dtype == VS_F32 ? 4 : 2;
-    // split the keys so that about 4096 single-wave workgroups cover B x heads
+    // key splits: about 512 four-wave workgroups over B x heads, at least 4 pages a split
     const int max_pages = (d->max_ctx + kPageTokens - 1) / kPageTokens;
     const long pairs = (long)d->B * m->n_heads;
-    int ns = (int)std::min<long>(max_pages, std::max<long>(1, (4096 + pairs - 1) / pairs));
+    const int ns = (int)std::min<long>(std::max(1, max_pages / 4), std::max<long>(1, (512 + pairs - 1) / pairs));
     p->split_pages = (max_pages + ns - 1) / ns;
     p->n_splits = (max_pages + p->split_pages - 1) / p->split_pages;
     p->rmax = d->max_rows <= 1 ? 1 : d->max_rows <= 2 ? 2 : d->max_rows <= 4 ? 4 : 8;
-    p->n_tiles_lm = (m->vocab + 31) / 32;
+    const size_t kmax = (size_t)std::max(p->D, p->F);
+    p->gemv = d->M <= kGemvMaxRows && (size_t)std::max(d->M, 1) * kmax * p->esz <= kGemvMaxLds;
+    p->n_lm_parts = p->gemv ? (p->V + gemv_units_per_wg(p->V) - 1) / gemv_units_per_wg(p->V) : (p->V + 31) / 32;
     const size_t M = (size_t)std::max(d->M, 1), ML = (size_t)std::max(d->M_log, 1);
     size_t o = 0;
     auto take = [&](size_t bytes) {
         size_t at = o;
-        o = align256(o + bytes);
+        o = align256(o + std::max<size_t>(bytes, 4));
         return at;
     };
     p->off_row_seq = take(M * 4);
@@ -126,24 +143,20 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->off_h = take(M * p->F * p->esz);
     p->off_part = take(M * p->H * p->n_splits * (p->Dh + 2) * 4);
     p->off_xf = take(ML * p->D * p->esz);
-    p->off_lmpart = take(ML * p->n_tiles_lm * sizeof(ArgPart));
+    p->off_lmpart = take(ML * p->n_lm_parts * sizeof(ArgPart));
     p->total = o;
     return vs_ok();
 }
 
-// ---- GEMM dispatch -------------------------------------------------------
+// ---- launches ------------------------------------------------------------
 
 template <int DT, int MT, int EPI>
 void launch_gemm_mt(const GemmArgs& g, int NW, int n_mgroups, hipStream_t s) {
     constexpr int U = (DT == F32 ? 4 : 8) / MT > 0 ? (DT == F32 ? 4 : 8) / MT : 1;
     dim3 grid(g.n_tiles, n_mgroups);
-    if (NW >= 16) {
-        hipLaunchKernelGGL((gemm_skinny_kernel<DT, MT, 16, EPI, U>), grid, dim3(16 * 64), 0, s, g);
-    } else if (NW >= 8) {
-        hipLaunchKernelGGL((gemm_skinny_kernel<DT, MT, 8, EPI, U>), grid, dim3(8 * 64), 0, s, g);
-    } else {
-        hipLaunchKernelGGL((gemm_skinny_kernel<DT, MT, 4, EPI, U>), grid, dim3(4 * 64), 0, s, g);
-    }
+    if (NW >= 16) hipLaunchKernelGGL((gemm_skinny_kernel<DT, MT, 16, EPI, U>), grid, dim3(16 * 64), 0, s, g);
+    else if (NW >= 8) hipLaunchKernelGGL((gemm_skinny_kernel<DT, MT, 8, EPI, U>), grid, dim3(8 * 64), 0, s, g);
+    else hipLaunchKernelGGL((gemm_skinny_kernel<DT, MT, 4, EPI, U>), grid, dim3(4 * 64), 0, s, g);
 }
 
 template <int DT, int EPI>
@@ -162,20 +175,63 @@ void launch_gemm(const GemmArgs& g, hipStream_t s) {
     else launch_gemm_mt<DT, 4, EPI>(g, NW, n_mgroups, s);
 }
 
+template <int DT, int MR, int XM, int EPI>
+void launch_gemv_mr(const GemvArgs& g, hipStream_t s) {
+    const size_t lds = (size_t)g.M * g.K * St<DT>::bytes;
+    static bool attr_set = false;  // per instantiation: allow more than 64 KB of dynamic LDS
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<DT, MR, XM, EPI>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemvMaxLds);
+        attr_set = true;
+    }
+    const int n_wg = (g.n_units + g.units_per_wg - 1) / g.units_per_wg;
+    hipLaunchKernelGGL((gemv_kernel<DT, MR, XM, EPI>), dim3(n_wg), dim3(kGemvWaves * 64), lds, s, g);
+}
+
+template <int DT, int XM, int EPI>
+void launch_gemv(GemvArgs g, hipStream_t s) {
+    if (g.M <= 0) return;
+    g.units_per_wg = gemv_units_per_wg(g.n_units);
+    if (g.M <= 1) launch_gemv_mr<DT, 1, XM, EPI>(g, s);
+    else if (g.M <= 2) launch_gemv_mr<DT, 2, XM, EPI>(g, s);
+    else if (g.M <= 4) launch_gemv_mr<DT, 4, XM, EPI>(g, s);
+    else launch_gemv_mr<DT, 8, XM, EPI>(g, s);
+}
+
 template <int DT, int DH>
 void launch_attention(const AttnArgs& a, int B, int M, int rmax, hipStream_t s) {
     dim3 grid(a.n_splits, a.n_heads, B);
+    dim3 block(kAttnWaves * 64);
     {
-    TimedScope ts(VS_KERNEL_ATTN, s);
-    switch (rmax) {
-        case 1: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 1>), grid, dim3(64), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 2>), grid, dim3(64), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 4>), grid, dim3(64), 0, s, a); break;
-        default: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 8>), grid, dim3(64), 0, s, a); break;
-    }
+        TimedScope ts(VS_KERNEL_ATTN, s);
+        switch (rmax) {
+            case 1: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 1>), grid, block, 0, s, a); break;
+            case 2: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 2>), grid, block, 0, s, a); break;
+            case 4: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 4>), grid, block, 0, s, a); break;
+            default: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 8>), grid, block, 0, s, a); break;
+        }
     }
     TimedScope ts(VS_KERNEL_MERGE, s);
     hipLaunchKernelGGL((attn_merge_kernel<DT, DH>), dim3(M, a.n_heads), dim3(DH), 0, s, a);
+}
+
+// Common epilogue fields of both product paths.
+template <typename A>
+void fill_epilogue(A& g, const Plan& p, const vs_batch_desc* d, const int32_t* bt, const vs_pool_desc* pg,
+                   const int* row_seq, const int* row_pos, const float* rope_cs) {
+    g.block_tables = bt;
+    g.max_blocks = d->max_blocks;
+    g.num_pages = pg->num_pages;
+    g.row_seq = row_seq;
+    g.row_pos = row_pos;
+    g.rope_cs = rope_cs;
+    g.kv_base = kv_pool_base(d->pool);
+    g.page_elems = (long)(kv_page_bytes(pg) / p.esz);
+    g.layer_elems = 2L * p.Hkv * kPageTokens * p.Dh;
+    g.head_dim = p.Dh;
+    g.n_heads = p.H;
+    g.n_kv_heads = p.Hkv;
+    g.page_tokens = kPageTokens;
 }
 
 template <int DT>
@@ -195,32 +251,38 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     ArgPart* lmpart = reinterpret_cast<ArgPart*>(ws + p.off_lmpart);
     const float eps = w->dims.eps;
 
-    if (p.M > 0) {
-        hipLaunchKernelGGL(prep_rows_kernel, dim3(p.M), dim3(64), 0, s, d->q_start, d->ctx_len, p.B, p.Dh,
-                           (double)w->dims.rope_theta, row_seq, row_pos, rope_cs);
-        hipLaunchKernelGGL((embed_kernel<DT>), dim3(p.M), dim3(256), 0, s, d->tokens, w->embed, p.V, p.D, x);
-    }
+    PrepArgs pa;
+    pa.q_start = d->q_start;
+    pa.ctx_len = d->ctx_len;
+    pa.B = p.B;
+    pa.M = p.M;
+    pa.head_dim = p.Dh;
+    pa.theta = (double)w->dims.rope_theta;
+    pa.tokens = d->tokens;
+    pa.embed = w->embed;
+    pa.vocab = p.V;
+    pa.D = p.D;
+    pa.row_seq = row_seq;
+    pa.row_pos = row_pos;
+    pa.rope_cs = rope_cs;
+    pa.x = x;
+    hipLaunchKernelGGL((prep_embed_kernel<DT>), dim3(p.M), dim3(256), 0, s, pa);
 
-    GemmArgs g = {};
-    g.block_tables = bt;
-    g.max_blocks = d->max_blocks;
-    g.num_pages = pg->num_pages;
-    g.row_seq = row_seq;
-    g.row_pos = row_pos;
-    g.rope_cs = rope_cs;
-    g.kv_base = kv_pool_base(d->pool);
-    g.page_elems = (long)(kv_page_bytes(pg) / p.esz);
-    g.layer_elems = 2L * p.Hkv * kPageTokens * p.Dh;
-    g.head_dim = p.Dh;
-    g.n_heads = p.H;
-    g.n_kv_heads = p.Hkv;
-    g.page_tokens = kPageTokens;
+    GemvArgs gv = {};
+    fill_epilogue(gv, p, d, bt, pg, row_seq, row_pos, rope_cs);
+    gv.M = p.M;
+    gv.xin = x;
+    gv.xin_ld = p.D;
+    gv.eps = eps;
+    GemmArgs gm = {};
+    fill_epilogue(gm, p, d, bt, pg, row_seq, row_pos, rope_cs);
+    gm.M = p.M;
 
     AttnArgs a = {};
     a.q = qb;
-    a.kv_base = g.kv_base;
-    a.page_elems = g.page_elems;
-    a.layer_elems = g.layer_elems;
+    a.kv_base = kv_pool_base(d->pool);
+    a.page_elems = (long)(kv_page_bytes(pg) / p.esz);
+    a.layer_elems = 2L * p.Hkv * kPageTokens * p.Dh;
     a.n_heads = p.H;
     a.n_kv_heads = p.Hkv;
     a.page_tokens = kPageTokens;
@@ -236,25 +298,37 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     a.part = part;
     a.out = attn;
 
-    for (int l = 0; l < p.L && p.M > 0; ++l) {
+    for (int l = 0; l < p.L; ++l) {
         const vs_layer_weights& lw = w->layers[l];
-        hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
-                           lw.attn_norm, p.D, eps, xn);
-        GemmArgs q = g;
-        q.w0 = lw.wq;
-        q.w1 = lw.wk;
-        q.w2 = lw.wv;
-        q.n0 = p.H * p.Dh;
-        q.n1 = p.Hkv * p.Dh;
-        q.n2 = p.Hkv * p.Dh;
-        q.K = p.D;
-        q.act = xn;
-        q.act_ld = p.D;
-        q.M = p.M;
-        q.n_tiles = (p.H + 2 * p.Hkv) * p.Dh / 32;
-        q.q_out = qb;
-        q.layer = l;
-        {
+        // RMSNorm(x) -> q, k, v; rotary; K/V into the pages
+        if (p.gemv) {
+            GemvArgs q = gv;
+            q.w0 = lw.wq;
+            q.w1 = lw.wk;
+            q.w2 = lw.wv;
+            q.K = p.D;
+            q.gain = lw.attn_norm;
+            q.q_out = qb;
+            q.layer = l;
+            q.n_units = (p.H + 2 * p.Hkv) * p.Dh / 2;
+            TimedScope ts(VS_KERNEL_QKV, s);
+            launch_gemv<DT, X_NORM, EPI_QKV>(q, s);
+        } else {
+            hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
+                               lw.attn_norm, p.D, eps, xn);
+            GemmArgs q = gm;
+            q.w0 = lw.wq;
+            q.w1 = lw.wk;
+            q.w2 = lw.wv;
+            q.n0 = p.H * p.Dh;
+            q.n1 = p.Hkv * p.Dh;
+            q.n2 = p.Hkv * p.Dh;
+            q.K = p.D;
+            q.act = xn;
+            q.act_ld = p.D;
+            q.n_tiles = (p.H + 2 * p.Hkv) * p.Dh / 32;
+            q.q_out = qb;
+            q.layer = l;
             TimedScope ts(VS_KERNEL_QKV, s);
             launch_gemm<DT, EPI_QKV>(q, s);
         }
@@ -263,75 +337,124 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
         if (p.Dh == 128) launch_attention<DT, 128>(a, p.B, p.M, p.rmax, s);
         else launch_attention<DT, 64>(a, p.B, p.M, p.rmax, s);
 
-        GemmArgs o = g;
-        o.w0 = lw.wo;
-        o.n0 = p.D;
-        o.K = p.H * p.Dh;
-        o.act = attn;
-        o.act_ld = p.H * p.Dh;
-        o.M = p.M;
-        o.n_tiles = (p.D + 31) / 32;
-        o.x = x;
-        o.x_ld = p.D;
-        {
+        // x += W_o attn
+        if (p.gemv) {
+            GemvArgs o = gv;
+            o.w0 = lw.wo;
+            o.K = p.H * p.Dh;
+            o.act = attn;
+            o.act_ld = p.H * p.Dh;
+            o.x = x;
+            o.x_ld = p.D;
+            o.n_units = p.D;
+            TimedScope ts(VS_KERNEL_OPROJ, s);
+            launch_gemv<DT, X_PLAIN, EPI_RESID>(o, s);
+        } else {
+            GemmArgs o = gm;
+            o.w0 = lw.wo;
+            o.n0 = p.D;
+            o.K = p.H * p.Dh;
+            o.act = attn;
+            o.act_ld = p.H * p.Dh;
+            o.n_tiles = (p.D + 31) / 32;
+            o.x = x;
+            o.x_ld = p.D;
             TimedScope ts(VS_KERNEL_OPROJ, s);
             launch_gemm<DT, EPI_RESID>(o, s);
         }
 
-        hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
-                           lw.ffn_norm, p.D, eps, xn);
-        GemmArgs gu = g;
-        gu.w0 = lw.wg;
-        gu.w1 = lw.wu;
-        gu.n0 = p.F;
-        gu.n1 = p.F;
-        gu.K = p.D;
-        gu.act = xn;
-        gu.act_ld = p.D;
-        gu.M = p.M;
-        gu.n_tiles = (p.F + 15) / 16;
-        gu.h_out = hmid;
-        gu.h_ld = p.F;
-        {
+        // RMSNorm(x) -> silu(gate) * up
+        if (p.gemv) {
+            GemvArgs gu = gv;
+            gu.w0 = lw.wg;
+            gu.w1 = lw.wu;
+            gu.K = p.D;
+            gu.gain = lw.ffn_norm;
+            gu.h_out = hmid;
+            gu.h_ld = p.F;
+            gu.n_units = p.F;
+            TimedScope ts(VS_KERNEL_GATEUP, s);
+            launch_gemv<DT, X_NORM, EPI_SWIGLU>(gu, s);
+        } else {
+            hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
+                               lw.ffn_norm, p.D, eps, xn);
+            GemmArgs gu = gm;
+            gu.w0 = lw.wg;
+            gu.w1 = lw.wu;
+            gu.n0 = p.F;
+            gu.n1 = p.F;
+            gu.K = p.D;
+            gu.act = xn;
+            gu.act_ld = p.D;
+            gu.n_tiles = (p.F + 15) / 16;
+            gu.h_out = hmid;
+            gu.h_ld = p.F;
             TimedScope ts(VS_KERNEL_GATEUP, s);
             launch_gemm<DT, EPI_SWIGLU>(gu, s);
         }
 
-        GemmArgs dn = g;
-        dn.w0 = lw.wd;
-        dn.n0 = p.D;
-        dn.K = p.F;
-        dn.act = hmid;
-        dn.act_ld = p.F;
-        dn.M = p.M;
-        dn.n_tiles = (p.D + 31) / 32;
-        dn.x = x;
-        dn.x_ld = p.D;
-        {
+        // x += W_d h
+        if (p.gemv) {
+            GemvArgs dn = gv;
+            dn.w0 = lw.wd;
+            dn.K = p.F;
+            dn.act = hmid;
+            dn.act_ld = p.F;
+            dn.x = x;
+            dn.x_ld = p.D;
+            dn.n_units = p.D;
+            TimedScope ts(VS_KERNEL_DOWN, s);
+            launch_gemv<DT, X_PLAIN, EPI_RESID>(dn, s);
+        } else {
+            GemmArgs dn = gm;
+            dn.w0 = lw.wd;
+            dn.n0 = p.D;
+            dn.K = p.F;
+            dn.act = hmid;
+            dn.act_ld = p.F;
+            dn.n_tiles = (p.D + 31) / 32;
+            dn.x = x;
+            dn.x_ld = p.D;
             TimedScope ts(VS_KERNEL_DOWN, s);
             launch_gemm<DT, EPI_RESID>(dn, s);
         }
     }
 
-    if (p.M_log > 0) {
-        hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M_log), dim3(256), 0, s, x, d->logit_rows, p.M,
-                           w->final_norm, p.D, eps, xf);
-        GemmArgs lm = g;
-        lm.w0 = w->lm_head;
-        lm.n0 = p.V;
-        lm.K = p.D;
-        lm.act = xf;
-        lm.act_ld = p.D;
-        lm.M = p.M_log;
-        lm.n_tiles = p.n_tiles_lm;
-        lm.logits = out->logits;
-        lm.vocab = p.V;
-        lm.parts = lmpart;
-        TimedScope ts(VS_KERNEL_LMHEAD, s);
-        launch_gemm<DT, EPI_LOGITS>(lm, s);
+    if (p.M_log > 0) {  // final RMSNorm of the logit rows -> LM head, argmax partials
+        if (p.gemv) {
+            GemvArgs lm = gv;
+            lm.w0 = w->lm_head;
+            lm.K = p.D;
+            lm.gain = w->final_norm;
+            lm.act_rows = d->logit_rows;
+            lm.M = p.M_log;
+            lm.logits = out->logits;
+            lm.vocab = p.V;
+            lm.parts = lmpart;
+            lm.n_parts = p.n_lm_parts;
+            lm.n_units = p.V;
+            TimedScope ts(VS_KERNEL_LMHEAD, s);
+            launch_gemv<DT, X_NORM, EPI_LOGITS>(lm, s);
+        } else {
+            hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M_log), dim3(256), 0, s, x, d->logit_rows, p.M,
+                               w->final_norm, p.D, eps, xf);
+            GemmArgs lm = gm;
+            lm.w0 = w->lm_head;
+            lm.n0 = p.V;
+            lm.K = p.D;
+            lm.act = xf;
+            lm.act_ld = p.D;
+            lm.M = p.M_log;
+            lm.n_tiles = p.n_lm_parts;
+            lm.logits = out->logits;
+            lm.vocab = p.V;
+            lm.parts = lmpart;
+            TimedScope ts(VS_KERNEL_LMHEAD, s);
+            launch_gemm<DT, EPI_LOGITS>(lm, s);
+        }
     }
-    if (p.M > 0 && out->argmax) {
-        hipLaunchKernelGGL(argmax_accept_kernel, dim3(p.B), dim3(256), 0, s, lmpart, p.n_tiles_lm, d->q_start, p.M,
+    if (out->argmax) {
+        hipLaunchKernelGGL(argmax_accept_kernel, dim3(p.B), dim3(256), 0, s, lmpart, p.n_lm_parts, d->q_start, p.M,
                            d->logit_rows, p.M_log, d->tokens, out->g0, out->argmax, out->top2_gap, out->accept_len,
                            out->bonus);
     }
