@@ -13,9 +13,9 @@
 // w, w+4, ... of the split. Lane l owns dims [(l%16)*DH/16, +DH/16) of key slot
 // (l/16) within each group of four keys, so one page of 16 keys is four loads
 // per lane for K and four for V, and the 16 lanes that share a key finish its
-// dot product with xor shuffles. Every K/V byte is used by exactly one wave, so
-// it goes from HBM straight to registers; the wave's next page is in flight
-// while the current one is reduced. The four waves' states are merged through
+// dot product with DPP row sums. Every K/V byte is used by exactly one wave, so
+// it goes from HBM straight to registers; each wave keeps a ring of three
+// pages, two in flight while one is reduced. The four waves' states are merged through
 // LDS and the workgroup's state is stored; a merge kernel then combines the
 // splits and writes the attention output in the storage type. All rows of one sequence (up to RMAX
 // at a time) share each K/V load; row i at position ctx + i keeps keys
@@ -99,31 +99,17 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attn_split_kernel(AttnArgs a)
             }
         }
 
-        RawVec<DT, DPL> kf[4], vf[4];  // current page (raw storage words)
-        RawVec<DT, DPL> kn[4], vn[4];  // next page, in flight
-        const int pw0 = p_begin + wave;
-        if (pw0 < p_end) {
-            const long pb = (long)min(max(bt[pw0], 0), a.num_pages - 1) * a.page_elems;
+        // a ring of three pages per wave: two are in flight while one is reduced
+        RawVec<DT, DPL> ka[4], va[4], kb[4], vb[4], kc[4], vc[4];
+        auto load_page = [&](RawVec<DT, DPL>(&kk)[4], RawVec<DT, DPL>(&vv)[4], int p) {
+            const long pb = (long)min(max(bt[p], 0), a.num_pages - 1) * a.page_elems;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                load_raw<DT, DPL>(kn[u], kvb + (pb + kofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
-                load_raw<DT, DPL>(vn[u], kvb + (pb + vofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
+                load_raw<DT, DPL>(kk[u], kvb + (pb + kofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
+                load_raw<DT, DPL>(vv[u], kvb + (pb + vofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
             }
-        }
-        for (int p = pw0; p < p_end; p += NW) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                kf[u] = kn[u];
-                vf[u] = vn[u];
-            }
-            if (p + NW < p_end) {  // the wave's next page is loaded while this one is reduced
-                const long pb = (long)min(max(bt[p + NW], 0), a.num_pages - 1) * a.page_elems;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    load_raw<DT, DPL>(kn[u], kvb + (pb + kofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
-                    load_raw<DT, DPL>(vn[u], kvb + (pb + vofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
-                }
-            }
+        };
+        auto reduce_page = [&](const RawVec<DT, DPL>(&kk)[4], const RawVec<DT, DPL>(&vv)[4], int p) {
 #pragma unroll
             for (int i = 0; i < RMAX; ++i) {
                 if (i >= nr) break;
@@ -133,11 +119,8 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attn_split_kernel(AttnArgs a)
                 for (int u = 0; u < 4; ++u) {
                     float d = 0.f;
 #pragma unroll
-                    for (int e = 0; e < DPL; ++e) d += qr[i][e] * raw_at<DT, DPL>(kf[u], e);
-                    d += shfl_xor(d, 1);
-                    d += shfl_xor(d, 2);
-                    d += shfl_xor(d, 4);
-                    d += shfl_xor(d, 8);
+                    for (int e = 0; e < DPL; ++e) d += qr[i][e] * raw_at<DT, DPL>(kk[u], e);
+                    d = row16_sum(d);  // the 16 lanes of a key slot hold its 16 dim chunks
                     const int kp = p * T + 4 * u + g;
                     sc[u] = (kp <= qpos) ? d : -INFINITY;
                 }
@@ -161,11 +144,24 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attn_split_kernel(AttnArgs a)
                 for (int e = 0; e < DPL; ++e) {
                     float acc = o[i][e] * alpha;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) acc += pu[u] * raw_at<DT, DPL>(vf[u], e);
+                    for (int u = 0; u < 4; ++u) acc += pu[u] * raw_at<DT, DPL>(vv[u], e);
                     o[i][e] = acc;
                 }
                 m[i] = mn;
             }
+        };
+        const int p0 = p_begin + wave;
+        if (p0 < p_end) load_page(ka, va, p0);
+        if (p0 + NW < p_end) load_page(kb, vb, p0 + NW);
+        for (int p = p0; p < p_end; p += 3 * NW) {
+            if (p + 2 * NW < p_end) load_page(kc, vc, p + 2 * NW);
+            reduce_page(ka, va, p);
+            if (p + NW >= p_end) break;
+            if (p + 3 * NW < p_end) load_page(ka, va, p + 3 * NW);
+            reduce_page(kb, vb, p + NW);
+            if (p + 2 * NW >= p_end) break;
+            if (p + 4 * NW < p_end) load_page(kb, vb, p + 4 * NW);
+            reduce_page(kc, vc, p + 2 * NW);
         }
         // this wave's state: sum the four key slots' outputs, park it in LDS
 #pragma unroll

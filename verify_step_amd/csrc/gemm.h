@@ -101,7 +101,7 @@ __device__ __forceinline__ void frag_zero(Frag<DT>& f) {
     }
 }
 
-template <int DT>
+template <int DT, bool STREAM = false>
 __device__ __forceinline__ void frag_load(Frag<DT>& f, const void* base, long elem, bool valid) {
     if (!valid) {
         frag_zero<DT>(f);
@@ -109,10 +109,16 @@ __device__ __forceinline__ void frag_load(Frag<DT>& f, const void* base, long el
     }
     if constexpr (DT == F32) {
         const float4_t* p = reinterpret_cast<const float4_t*>(reinterpret_cast<const float*>(base) + elem);
-        f.a = p[0];
-        f.b = p[1];
+        if constexpr (STREAM) {
+            f.a = __builtin_bit_cast(float4_t, load_stream16(p));
+            f.b = __builtin_bit_cast(float4_t, load_stream16(p + 1));
+        } else {
+            f.a = p[0];
+            f.b = p[1];
+        }
     } else {
-        f.a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + elem;
+        f.a = STREAM ? load_stream16(p) : *reinterpret_cast<const uint4*>(p);
     }
 }
 
@@ -331,8 +337,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
         for (int u = 0; u < U; ++u) {
             const bool in = kc + u < kc1;
             const long ko = (long)(kc + u) * 32;
-            frag_load<DT>(fa[u], tm.w, baseA + ko, in && vA);
-            frag_load<DT>(fb[u], tm.wb, baseB + ko, in && vB);
+            frag_load<DT, true>(fa[u], tm.w, baseA + ko, in && vA);
+            frag_load<DT, true>(fb[u], tm.wb, baseB + ko, in && vB);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) frag_load<DT>(fx[u][mt], g.act, xbase[mt] + ko, in && xv[mt]);
         }

@@ -184,12 +184,11 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& g, int u, int m, f
 
 constexpr int kGemvMaxUnits = 128;  // units per workgroup (results parked in LDS)
 
-template <int DT, int MR, int XM, int EPI>
-__global__ void __launch_bounds__(kGemvWaves * 64) gemv_kernel(GemvArgs g) {
+template <int DT, int MR, int XM, int EPI, int NW = kGemvWaves, int CG = kGemvChunks>
+__global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs g) {
     constexpr int RU = (EPI == EPI_RESID || EPI == EPI_LOGITS) ? 1 : 2;  // rows per unit
     constexpr int EPL = 16 / St<DT>::bytes;                              // elements per lane-load
     constexpr int CE = EPL * 64;                                         // elements per 1 KB chunk
-    constexpr int CG = kGemvChunks;  // chunks per row in one group of loads
     extern __shared__ __align__(16) unsigned char smem[];  // X: [M][K] in the storage type
     __shared__ float res[kGemvMaxUnits][RU][MR];           // per-unit dot products, epilogue input
 
@@ -201,7 +200,7 @@ __global__ void __launch_bounds__(kGemvWaves * 64) gemv_kernel(GemvArgs g) {
     const int K = g.K;
     const int NC = (K + CE - 1) / CE;      // 1 KB chunks per row
     const int NG = (NC + CG - 1) / CG;     // bursts per unit
-    const int my_units = n_local > wave ? (n_local - wave + kGemvWaves - 1) / kGemvWaves : 0;
+    const int my_units = n_local > wave ? (n_local - wave + NW - 1) / NW : 0;
     const long lane_byte = (long)lane * 16;
     const long row_bytes = (long)K * St<DT>::bytes;
 
@@ -215,7 +214,7 @@ __global__ void __launch_bounds__(kGemvWaves * 64) gemv_kernel(GemvArgs g) {
 #pragma unroll
             for (int c = 0; c < CG; ++c) {
                 const long off = (long)(gi * CG + c) * 1024 + lane_byte;
-                buf[r][c] = *reinterpret_cast<const uint4*>(rowp + (off < row_bytes ? off : 0));
+                buf[r][c] = load_stream16(rowp + (off < row_bytes ? off : 0));
             }
         }
     };
@@ -226,7 +225,7 @@ __global__ void __launch_bounds__(kGemvWaves * 64) gemv_kernel(GemvArgs g) {
 
     // ---- prologue: the batch rows into LDS ----
     if constexpr (XM == X_NORM) {
-        __shared__ float red[kGemvWaves][MR];
+        __shared__ float red[NW][MR];
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             if (m >= g.M) break;
@@ -234,7 +233,7 @@ __global__ void __launch_bounds__(kGemvWaves * 64) gemv_kernel(GemvArgs g) {
             const float* xr = g.xin + (long)src * g.xin_ld;
             float ss = 0.f;
 #pragma unroll 4
-            for (int k = tid * 4; k < K; k += kGemvWaves * 64 * 4) {
+            for (int k = tid * 4; k < K; k += NW * 64 * 4) {
                 const float4_t v = *reinterpret_cast<const float4_t*>(xr + k);
                 ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
             }
@@ -246,20 +245,20 @@ __global__ void __launch_bounds__(kGemvWaves * 64) gemv_kernel(GemvArgs g) {
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             if (m >= g.M) break;
-            float part[kGemvWaves];
+            float part[NW];
 #pragma unroll
-            for (int w = 0; w < kGemvWaves; ++w) part[w] = red[w][m];
+            for (int w = 0; w < NW; ++w) part[w] = red[w][m];
 #pragma unroll
-            for (int span = 1; span < kGemvWaves; span <<= 1)  // fixed pairwise tree
+            for (int span = 1; span < NW; span <<= 1)  // fixed pairwise tree
 #pragma unroll
-                for (int w = 0; w + span < kGemvWaves; w += 2 * span) part[w] += part[w + span];
+                for (int w = 0; w + span < NW; w += 2 * span) part[w] += part[w + span];
             const float tot = part[0];
             const float rinv = 1.0f / sqrtf(tot / (float)K + g.eps);
             const int src = g.act_rows ? g.act_rows[m] : m;
             const float* xr = g.xin + (long)src * g.xin_ld;
             typename St<DT>::raw* xs = reinterpret_cast<typename St<DT>::raw*>(smem) + (long)m * K;
 #pragma unroll 4
-            for (int k = tid * 4; k < K; k += kGemvWaves * 64 * 4) {
+            for (int k = tid * 4; k < K; k += NW * 64 * 4) {
                 const float4_t v = *reinterpret_cast<const float4_t*>(xr + k);
                 float gv[4];
                 load_widen<DT, 4>(reinterpret_cast<const char*>(g.gain) + (long)k * St<DT>::bytes, gv);
@@ -275,14 +274,14 @@ __global__ void __launch_bounds__(kGemvWaves * 64) gemv_kernel(GemvArgs g) {
             const char* ar = reinterpret_cast<const char*>(g.act) + (long)src * g.act_ld * St<DT>::bytes;
             char* xs = reinterpret_cast<char*>(smem) + (long)m * K * St<DT>::bytes;
 #pragma unroll 4
-            for (long off = tid * 16; off < (long)K * St<DT>::bytes; off += kGemvWaves * 64 * 16)
+            for (long off = tid * 16; off < (long)K * St<DT>::bytes; off += NW * 64 * 16)
                 *reinterpret_cast<uint4*>(xs + off) = *reinterpret_cast<const uint4*>(ar + off);
         }
     }
     __syncthreads();
 
     for (int uj = 0; uj < my_units; ++uj) {
-        const int ul = wave + kGemvWaves * uj;
+        const int ul = wave + NW * uj;
         const UnitMap um = unit_map<EPI>(g, u_begin + ul);
         float acc[RU][MR];
 #pragma unroll
@@ -327,13 +326,13 @@ __global__ void __launch_bounds__(kGemvWaves * 64) gemv_kernel(GemvArgs g) {
     __syncthreads();
 
     // ---- epilogues of the workgroup's units, all threads ----
-    for (int idx = tid; idx < n_local * g.M; idx += kGemvWaves * 64) {
+    for (int idx = tid; idx < n_local * g.M; idx += NW * 64) {
         const int ul = idx / g.M, m = idx % g.M;
         gemv_epilogue<DT, EPI>(g, u_begin + ul, m, res[ul][0][m], res[ul][RU - 1][m]);
     }
     if constexpr (EPI == EPI_LOGITS) {
         // argmax partial of this workgroup's vocabulary range, per batch row (wave w takes rows w, w+4)
-        for (int m = wave; m < g.M; m += kGemvWaves) {
+        for (int m = wave; m < g.M; m += NW) {
             float v1 = -INFINITY, v2 = -INFINITY;
             int i1 = 0x7FFFFFFF;
             for (int ul = lane; ul < n_local; ul += 64) argpart_combine(v1, i1, v2, res[ul][0][m], u_begin + ul, -INFINITY);

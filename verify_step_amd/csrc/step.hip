@@ -87,12 +87,11 @@ vs_status check_dims(const vs_model_desc* m) {
     return vs_ok();
 }
 
-// Units per GEMV workgroup: about 512 workgroups (two per CU), a multiple of the 4 waves,
-// at most kGemvMaxUnits.
+// Units per GEMV workgroup: the units spread evenly over about 512 workgroups (two per
+// CU, so every CU streams the same number of bytes), at most kGemvMaxUnits.
 int gemv_units_per_wg(int n_units) {
-    int u = (n_units + 511) / 512;
-    u = (u + kGemvWaves - 1) / kGemvWaves * kGemvWaves;
-    return std::min(std::max(u, kGemvWaves), kGemvMaxUnits);
+    const int u = (n_units + 511) / 512;
+    return std::min(std::max(u, 1), kGemvMaxUnits);
 }
 
 vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
