@@ -10,8 +10,10 @@ bookkeeping (kv_append) and the on-device token / length update.
 
 Prints one JSON line. `value` is decode tokens/s over the timed steps;
 `roofline` reports the gate/up product (the kernel that streams the most
-weight bytes) against the 8 TB/s HBM peak; `cpu_baseline` times the CPU
-oracle on one step of the same workload.
+weight bytes) against the 8 TB/s HBM peak, with its HBM traffic per launch
+from the committed counter summary under profiles/ while that summary's
+kernel-source digest matches; `cpu_baseline` times the CPU oracle on one
+step of the same workload.
 """
 from __future__ import annotations
 
@@ -28,6 +30,9 @@ sys.path.insert(0, ROOT)
 METRIC = "decode tokens/s + achieved HBM TB/s vs peak, 7B-shaped, B=1..64, K=1/5"
 HBM_PEAK_GBPS = 8000.0
 CTX0 = 2048
+ROOFLINE_STEPS = 8
+GATEUP_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gateup_gemv_7b_decode_b1_hbm_traffic.md")
+CSRC = os.path.join(ROOT, "verify_step_amd", "csrc")
 SEED_W, SEED_KV, SEED_TOK, SEED_PAGES = 2001, 2002, 2003, 2006
 
 
@@ -71,6 +76,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly instead of replaying a graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with plain device copies of known size (reference dispatches for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -92,7 +99,7 @@ def main():
     dev = torch.device("cuda:0")
     dims = W.LLAMA7B  # fp16
     K, Wm = args.steps, args.warmup
-    total_len = CTX0 + Wm + K + 1
+    total_len = CTX0 + Wm + K + min(K, ROOFLINE_STEPS) + 1  # every position a step of this run writes
 
     # ---- weights (generated on the host, one tensor at a time) ----
     t0 = time.time()
@@ -186,11 +193,13 @@ def main():
     ms_step = ms_total / K
     log(f"timed {K} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / K:.3f} ms/step)")
 
-    # ---- dominant kernel: gate/up product, timed launch by launch with HIP events ----
-    n_tk = 2 * dims.n_layers
+    # ---- dominant kernel: gate/up GEMV, each launch timed by its own dispatch events ----
+    # (a graph hides its nodes from events, so this window runs the same step eagerly)
+    n_rf = min(K, ROOFLINE_STEPS)
+    n_tk = dims.n_layers * n_rf
     ev = HipEvents(n_tk)
     vs.vs_time_kernel(vs.VS_KERNEL["gateup"], ev.start, ev.stop, n_tk)
-    for _ in range(2):
+    for _ in range(n_rf):
         device_step()
         host_bookkeeping()
     torch.cuda.synchronize()
@@ -201,12 +210,11 @@ def main():
     gu_ms = sum(durs) / len(durs)
     gu_bytes = 2 * dims.ffn * dims.d_model * dims.elem_bytes  # W_gate + W_up, read once per launch
     gu_gbps = gu_bytes / (gu_ms * 1e-3) / 1e9
+    traffic = measured_traffic(GATEUP_TRAFFIC_PROFILE)
 
     # ---- byte accounting for the whole step ----
-    import oracle  # byte counts only (the step is not run here)
-
-    wbytes = oracle.streamed_weight_bytes(dims)
-    kvpt = oracle.kv_bytes_per_token(dims.n_layers, dims.n_kv_heads, dims.head_dim, dims.elem_bytes)
+    wbytes = streamed_weight_bytes(dims)
+    kvpt = 2 * dims.n_layers * dims.n_kv_heads * dims.head_dim * dims.elem_bytes  # K and V of one token
     first = CTX0 + Wm + 1  # keys read by the first timed step
     avg_keys = first + (K - 1) / 2.0
     step_bytes = wbytes + avg_keys * kvpt + kvpt
@@ -240,22 +248,80 @@ def main():
             "wall_ms_per_step": round(wall * 1e3 / K, 4),
         },
         "roofline": {
-            "kernel": "gate/up product + SwiGLU (gemm_skinny_kernel, EPI_SWIGLU)",
+            "kernel": "gate/up GEMV + SwiGLU (gemv_kernel, EPI_SWIGLU)",
             "bound": "hbm",
             "achieved": round(gu_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "bytes_per_launch": gu_bytes,
             "avg_launch_us": round(gu_ms * 1e3, 3),
             "launches_timed": n_done,
+            "timing": f"dispatch events of every gate/up launch in {n_rf} eager steps after the timed window",
         },
     }
 
+    if args.copy_calibration:
+        copy_calibration()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(dims, w_cpu, kv0, tok0)
     print(json.dumps(result), flush=True)
+
+
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration():
+    """Three elementwise copies (negation) of 256 MiB of fp32 each: every dispatch reads and writes exactly
+    COPY_BYTES, the yardstick for scaling HBM byte counters."""
+    import torch
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 x {COPY_BYTES} B read + written")
+
+
+def streamed_weight_bytes(dims):
+    """Bytes of weights one step streams: every per-layer tensor, the final norm and the LM head (the
+    embedding is gathered row by row, not streamed)."""
+    D, F, V = dims.d_model, dims.ffn, dims.vocab
+    q, kv = dims.n_heads * dims.head_dim, dims.n_kv_heads * dims.head_dim
+    per_layer = D + q * D + 2 * kv * D + D * q + D + 3 * F * D
+    return (dims.n_layers * per_layer + D + V * D) * dims.elem_bytes
+
+
+def csrc_digest():
+    """sha256 over the kernel sources, so a counter summary can tell whether it still describes them."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(path):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None when there is none or its
+    kernel sources differ from the ones built here (the counters would describe other code)."""
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("csrc_sha256") != csrc_digest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def _load_model(model, dims, items, dev):

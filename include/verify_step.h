@@ -234,10 +234,11 @@ vs_status verify_accept(int32_t B, const int32_t* q_start, const int32_t* drafts
 #define VS_KERNEL_LMHEAD 7    /* LM head + argmax partials */
 
 /* Measurement aid, not part of the step's function. While armed, every
- * launch of kernel kind `kind` in decode_step is bracketed by hipEventRecord
- * of start_events[i] and stop_events[i] on the step's stream, i = 0, 1, ...
- * up to `capacity` launches (later launches are not timed). The events are
- * caller-created hipEvent_t handles. kind = VS_KERNEL_NONE disarms.
+ * launch of kernel kind `kind` in decode_step is dispatched with
+ * hipExtLaunchKernel so that start_events[i] and stop_events[i] take the
+ * dispatch's own start and end times, i = 0, 1, ... up to `capacity` launches
+ * (later launches are not timed). The events are caller-created hipEvent_t
+ * handles. kind = VS_KERNEL_NONE disarms.
  * vs_timed_launches returns how many launches were bracketed since arming.
  * Process-wide state; not for use while another thread runs decode_step. */
 vs_status vs_time_kernel(int32_t kind, void* const* start_events, void* const* stop_events, int32_t capacity);

@@ -1,5 +1,6 @@
 // decode_step / verify_accept: host-side validation, workspace plan and the
 // launch sequence of one batched decode / verify step on gfx950.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -42,21 +43,21 @@ struct KernelTimer {
     int count = 0;
 } g_timer;
 
-struct TimedScope {
-    hipStream_t s;
-    bool on;
-    int idx;
-    TimedScope(int kind, hipStream_t st) : s(st), on(false), idx(0) {
-        if (g_timer.kind == kind && kind != VS_KERNEL_NONE && g_timer.count < g_timer.capacity) {
-            on = true;
-            idx = g_timer.count++;
-            (void)hipEventRecord(static_cast<hipEvent_t>(g_timer.start[idx]), s);
-        }
+// Launch of a kernel that takes one argument struct. When the timer is armed for
+// `kind`, the start / stop events come from the dispatch itself (hipExtLaunchKernel),
+// so they bracket the kernel's execution and nothing queued around it.
+template <typename T>
+void launch1(int kind, void (*kern)(T), dim3 grid, dim3 block, size_t lds, hipStream_t s, T arg) {
+    void* argv[] = {&arg};
+    if (kind != VS_KERNEL_NONE && g_timer.kind == kind && g_timer.count < g_timer.capacity) {
+        const int i = g_timer.count++;
+        (void)hipExtLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, lds, s,
+                                 static_cast<hipEvent_t>(g_timer.start[i]), static_cast<hipEvent_t>(g_timer.stop[i]),
+                                 0);
+    } else {
+        (void)hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, lds, s);
     }
-    ~TimedScope() {
-        if (on) (void)hipEventRecord(static_cast<hipEvent_t>(g_timer.stop[idx]), s);
-    }
-};
+}
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -150,16 +151,16 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
 // ---- launches ------------------------------------------------------------
 
 template <int DT, int MT, int EPI>
-void launch_gemm_mt(const GemmArgs& g, int NW, int n_mgroups, hipStream_t s) {
+void launch_gemm_mt(int kind, const GemmArgs& g, int NW, int n_mgroups, hipStream_t s) {
     constexpr int U = (DT == F32 ? 4 : 8) / MT > 0 ? (DT == F32 ? 4 : 8) / MT : 1;
     dim3 grid(g.n_tiles, n_mgroups);
-    if (NW >= 16) hipLaunchKernelGGL((gemm_skinny_kernel<DT, MT, 16, EPI, U>), grid, dim3(16 * 64), 0, s, g);
-    else if (NW >= 8) hipLaunchKernelGGL((gemm_skinny_kernel<DT, MT, 8, EPI, U>), grid, dim3(8 * 64), 0, s, g);
-    else hipLaunchKernelGGL((gemm_skinny_kernel<DT, MT, 4, EPI, U>), grid, dim3(4 * 64), 0, s, g);
+    if (NW >= 16) launch1(kind, gemm_skinny_kernel<DT, MT, 16, EPI, U>, grid, dim3(16 * 64), 0, s, g);
+    else if (NW >= 8) launch1(kind, gemm_skinny_kernel<DT, MT, 8, EPI, U>, grid, dim3(8 * 64), 0, s, g);
+    else launch1(kind, gemm_skinny_kernel<DT, MT, 4, EPI, U>, grid, dim3(4 * 64), 0, s, g);
 }
 
 template <int DT, int EPI>
-void launch_gemm(const GemmArgs& g, hipStream_t s) {
+void launch_gemm(int kind, const GemmArgs& g, hipStream_t s) {
     const int M = g.M;
     if (M <= 0) return;
     const int n_mgroups = (M + 63) / 64;
@@ -169,13 +170,13 @@ void launch_gemm(const GemmArgs& g, hipStream_t s) {
     int NW = wgs < 256 ? 16 : wgs < 512 ? 8 : 4;
     const int KC = g.K / 32;
     while (NW > 4 && NW > KC) NW >>= 1;
-    if (MT == 1) launch_gemm_mt<DT, 1, EPI>(g, NW, n_mgroups, s);
-    else if (MT == 2) launch_gemm_mt<DT, 2, EPI>(g, NW, n_mgroups, s);
-    else launch_gemm_mt<DT, 4, EPI>(g, NW, n_mgroups, s);
+    if (MT == 1) launch_gemm_mt<DT, 1, EPI>(kind, g, NW, n_mgroups, s);
+    else if (MT == 2) launch_gemm_mt<DT, 2, EPI>(kind, g, NW, n_mgroups, s);
+    else launch_gemm_mt<DT, 4, EPI>(kind, g, NW, n_mgroups, s);
 }
 
 template <int DT, int MR, int XM, int EPI>
-void launch_gemv_mr(const GemvArgs& g, hipStream_t s) {
+void launch_gemv_mr(int kind, const GemvArgs& g, hipStream_t s) {
     const size_t lds = (size_t)g.M * g.K * St<DT>::bytes;
     static bool attr_set = false;  // per instantiation: allow more than 64 KB of dynamic LDS
     if (!attr_set) {
@@ -184,34 +185,30 @@ void launch_gemv_mr(const GemvArgs& g, hipStream_t s) {
         attr_set = true;
     }
     const int n_wg = (g.n_units + g.units_per_wg - 1) / g.units_per_wg;
-    hipLaunchKernelGGL((gemv_kernel<DT, MR, XM, EPI>), dim3(n_wg), dim3(kGemvWaves * 64), lds, s, g);
+    launch1(kind, gemv_kernel<DT, MR, XM, EPI>, dim3(n_wg), dim3(kGemvWaves * 64), lds, s, g);
 }
 
 template <int DT, int XM, int EPI>
-void launch_gemv(GemvArgs g, hipStream_t s) {
+void launch_gemv(int kind, GemvArgs g, hipStream_t s) {
     if (g.M <= 0) return;
     g.units_per_wg = gemv_units_per_wg(g.n_units);
-    if (g.M <= 1) launch_gemv_mr<DT, 1, XM, EPI>(g, s);
-    else if (g.M <= 2) launch_gemv_mr<DT, 2, XM, EPI>(g, s);
-    else if (g.M <= 4) launch_gemv_mr<DT, 4, XM, EPI>(g, s);
-    else launch_gemv_mr<DT, 8, XM, EPI>(g, s);
+    if (g.M <= 1) launch_gemv_mr<DT, 1, XM, EPI>(kind, g, s);
+    else if (g.M <= 2) launch_gemv_mr<DT, 2, XM, EPI>(kind, g, s);
+    else if (g.M <= 4) launch_gemv_mr<DT, 4, XM, EPI>(kind, g, s);
+    else launch_gemv_mr<DT, 8, XM, EPI>(kind, g, s);
 }
 
 template <int DT, int DH>
 void launch_attention(const AttnArgs& a, int B, int M, int rmax, hipStream_t s) {
     dim3 grid(a.n_splits, a.n_heads, B);
     dim3 block(kAttnWaves * 64);
-    {
-        TimedScope ts(VS_KERNEL_ATTN, s);
-        switch (rmax) {
-            case 1: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 1>), grid, block, 0, s, a); break;
-            case 2: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 2>), grid, block, 0, s, a); break;
-            case 4: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 4>), grid, block, 0, s, a); break;
-            default: hipLaunchKernelGGL((attn_split_kernel<DT, DH, 8>), grid, block, 0, s, a); break;
-        }
+    switch (rmax) {
+        case 1: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 1>, grid, block, 0, s, a); break;
+        case 2: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 2>, grid, block, 0, s, a); break;
+        case 4: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 4>, grid, block, 0, s, a); break;
+        default: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 8>, grid, block, 0, s, a); break;
     }
-    TimedScope ts(VS_KERNEL_MERGE, s);
-    hipLaunchKernelGGL((attn_merge_kernel<DT, DH>), dim3(M, a.n_heads), dim3(DH), 0, s, a);
+    launch1(VS_KERNEL_MERGE, attn_merge_kernel<DT, DH>, dim3(M, a.n_heads), dim3(DH), 0, s, a);
 }
 
 // Common epilogue fields of both product paths.
@@ -310,8 +307,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             q.q_out = qb;
             q.layer = l;
             q.n_units = (p.H + 2 * p.Hkv) * p.Dh / 2;
-            TimedScope ts(VS_KERNEL_QKV, s);
-            launch_gemv<DT, X_NORM, EPI_QKV>(q, s);
+            launch_gemv<DT, X_NORM, EPI_QKV>(VS_KERNEL_QKV, q, s);
         } else {
             hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
                                lw.attn_norm, p.D, eps, xn);
@@ -328,8 +324,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             q.n_tiles = (p.H + 2 * p.Hkv) * p.Dh / 32;
             q.q_out = qb;
             q.layer = l;
-            TimedScope ts(VS_KERNEL_QKV, s);
-            launch_gemm<DT, EPI_QKV>(q, s);
+            launch_gemm<DT, EPI_QKV>(VS_KERNEL_QKV, q, s);
         }
 
         a.layer = l;
@@ -346,8 +341,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             o.x = x;
             o.x_ld = p.D;
             o.n_units = p.D;
-            TimedScope ts(VS_KERNEL_OPROJ, s);
-            launch_gemv<DT, X_PLAIN, EPI_RESID>(o, s);
+            launch_gemv<DT, X_PLAIN, EPI_RESID>(VS_KERNEL_OPROJ, o, s);
         } else {
             GemmArgs o = gm;
             o.w0 = lw.wo;
@@ -358,8 +352,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             o.n_tiles = (p.D + 31) / 32;
             o.x = x;
             o.x_ld = p.D;
-            TimedScope ts(VS_KERNEL_OPROJ, s);
-            launch_gemm<DT, EPI_RESID>(o, s);
+            launch_gemm<DT, EPI_RESID>(VS_KERNEL_OPROJ, o, s);
         }
 
         // RMSNorm(x) -> silu(gate) * up
@@ -372,8 +365,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             gu.h_out = hmid;
             gu.h_ld = p.F;
             gu.n_units = p.F;
-            TimedScope ts(VS_KERNEL_GATEUP, s);
-            launch_gemv<DT, X_NORM, EPI_SWIGLU>(gu, s);
+            launch_gemv<DT, X_NORM, EPI_SWIGLU>(VS_KERNEL_GATEUP, gu, s);
         } else {
             hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
                                lw.ffn_norm, p.D, eps, xn);
@@ -388,8 +380,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             gu.n_tiles = (p.F + 15) / 16;
             gu.h_out = hmid;
             gu.h_ld = p.F;
-            TimedScope ts(VS_KERNEL_GATEUP, s);
-            launch_gemm<DT, EPI_SWIGLU>(gu, s);
+            launch_gemm<DT, EPI_SWIGLU>(VS_KERNEL_GATEUP, gu, s);
         }
 
         // x += W_d h
@@ -402,8 +393,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             dn.x = x;
             dn.x_ld = p.D;
             dn.n_units = p.D;
-            TimedScope ts(VS_KERNEL_DOWN, s);
-            launch_gemv<DT, X_PLAIN, EPI_RESID>(dn, s);
+            launch_gemv<DT, X_PLAIN, EPI_RESID>(VS_KERNEL_DOWN, dn, s);
         } else {
             GemmArgs dn = gm;
             dn.w0 = lw.wd;
@@ -414,8 +404,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             dn.n_tiles = (p.D + 31) / 32;
             dn.x = x;
             dn.x_ld = p.D;
-            TimedScope ts(VS_KERNEL_DOWN, s);
-            launch_gemm<DT, EPI_RESID>(dn, s);
+            launch_gemm<DT, EPI_RESID>(VS_KERNEL_DOWN, dn, s);
         }
     }
 
@@ -432,8 +421,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             lm.parts = lmpart;
             lm.n_parts = p.n_lm_parts;
             lm.n_units = p.V;
-            TimedScope ts(VS_KERNEL_LMHEAD, s);
-            launch_gemv<DT, X_NORM, EPI_LOGITS>(lm, s);
+            launch_gemv<DT, X_NORM, EPI_LOGITS>(VS_KERNEL_LMHEAD, lm, s);
         } else {
             hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M_log), dim3(256), 0, s, x, d->logit_rows, p.M,
                                w->final_norm, p.D, eps, xf);
@@ -448,8 +436,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             lm.logits = out->logits;
             lm.vocab = p.V;
             lm.parts = lmpart;
-            TimedScope ts(VS_KERNEL_LMHEAD, s);
-            launch_gemm<DT, EPI_LOGITS>(lm, s);
+            launch_gemm<DT, EPI_LOGITS>(VS_KERNEL_LMHEAD, lm, s);
         }
     }
     if (out->argmax) {
