@@ -41,26 +41,27 @@ def round_to(x: torch.Tensor, dt: str) -> torch.Tensor:
     return x.to(_STORAGE[dt]).to(F64)
 
 
-def linear(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
-    """y = x W^T for a weight stored row-major as [out][in] (float64 product).
+def linear(x: torch.Tensor, w: torch.Tensor, cdt: torch.dtype = F64) -> torch.Tensor:
+    """y = x W^T for a weight stored row-major as [out][in] (a float64 product by default).
 
     [KV Cache] section 02 ("Counting FLOPs and counting bytes"): every matrix
     multiply reads the full weight once and uses it for every row passing
-    through; the rows share the read. The product itself is the library matmul.
+    through; the rows share the read. The product itself is the library matmul,
+    in the compute type cdt; the result is returned as float64.
     """
-    return x.to(F64) @ w.to(F64).T
+    return (x.to(cdt) @ w.to(cdt).T).to(F64)
 
 
-def rmsnorm(x: torch.Tensor, gain: torch.Tensor, eps: float) -> torch.Tensor:
+def rmsnorm(x: torch.Tensor, gain: torch.Tensor, eps: float, cdt: torch.dtype = F64) -> torch.Tensor:
     """Root-mean-square normalisation of the last axis, times a per-feature gain.
 
     The pages name RMSNorm as a fused step of the decode path without
     writing it out; this is the textbook definition
-    y_i = x_i / sqrt(mean_j(x_j^2) + eps) * g_i.
+    y_i = x_i / sqrt(mean_j(x_j^2) + eps) * g_i, computed in cdt.
     """
-    x = x.to(F64)
+    x = x.to(cdt)
     ms = (x * x).mean(dim=-1, keepdim=True)
-    return x / torch.sqrt(ms + eps) * gain.to(F64)
+    return (x / torch.sqrt(ms + eps) * gain.to(cdt)).to(F64)
 
 
 def rope_angles(positions: torch.Tensor, head_dim: int, theta: float) -> torch.Tensor:
@@ -76,21 +77,22 @@ def rope_angles(positions: torch.Tensor, head_dim: int, theta: float) -> torch.T
     return positions.to(F64).unsqueeze(-1) * inv_freq
 
 
-def rope(x: torch.Tensor, positions: torch.Tensor, theta: float) -> torch.Tensor:
+def rope(x: torch.Tensor, positions: torch.Tensor, theta: float, cdt: torch.dtype = F64) -> torch.Tensor:
     """Rotate pairs (x_i, x_{i+d/2}) of each head vector by the angle of its position.
 
     x: [..., n_heads, head_dim] with the leading axes matching `positions`
     (one position per row). Pairing is "rotate half": feature i is paired with
-    feature i + head_dim/2.
+    feature i + head_dim/2. The angle is float64; cos, sin and the rotation are
+    taken in cdt.
     """
-    x = x.to(F64)
+    x = x.to(cdt)
     d = x.shape[-1]
     half = d // 2
     ang = rope_angles(positions, d, theta)  # [..., half]
-    cos = torch.cos(ang).unsqueeze(-2)  # broadcast over heads
-    sin = torch.sin(ang).unsqueeze(-2)
+    cos = torch.cos(ang).to(cdt).unsqueeze(-2)  # broadcast over heads
+    sin = torch.sin(ang).to(cdt).unsqueeze(-2)
     a, b = x[..., :half], x[..., half:]
-    return torch.cat([a * cos - b * sin, b * cos + a * sin], dim=-1)
+    return torch.cat([a * cos - b * sin, b * cos + a * sin], dim=-1).to(F64)
 
 
 def attention_standard(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: torch.Tensor | None = None,
@@ -174,15 +176,15 @@ def combine_partials(nums: torch.Tensor, dens: torch.Tensor, maxes: torch.Tensor
     return nums.sum(dim=0) / dens.sum(dim=0)
 
 
-def silu(x: torch.Tensor) -> torch.Tensor:
-    """x * sigmoid(x) = x / (1 + exp(-x)), float64."""
-    x = x.to(F64)
+def silu(x: torch.Tensor, cdt: torch.dtype = F64) -> torch.Tensor:
+    """x * sigmoid(x) = x / (1 + exp(-x)), in cdt (float64 by default)."""
+    x = x.to(cdt)
     return x / (1.0 + torch.exp(-x))
 
 
-def swiglu(gate: torch.Tensor, up: torch.Tensor) -> torch.Tensor:
+def swiglu(gate: torch.Tensor, up: torch.Tensor, cdt: torch.dtype = F64) -> torch.Tensor:
     """Gated feed-forward activation silu(gate) * up (the SwiGLU MLP of a 7B Llama-style model)."""
-    return silu(gate) * up.to(F64)
+    return (silu(gate, cdt) * up.to(cdt)).to(F64)
 
 
 def argmax_lowest(logits: torch.Tensor) -> tuple[int, float]:

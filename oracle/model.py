@@ -32,6 +32,13 @@ Storage points (the only places values are rounded):
     after rotation;
   * logits are fp32 and the argmax is taken on the fp32 values.
 Everything between two storage points is float64.
+
+decode_step(..., compute="f32") carries those in-between values in fp32
+instead (torch's fp32 CPU kernels: other rounding, other summation order).
+It is a second correct realisation of the same storage points, used only to
+measure how far two correct implementations drift apart through the layers,
+the way [KV Cache] section 07 runs one attention in fp32 and in fp64 and
+reads the difference as the size of rounding.
 """
 from __future__ import annotations
 
@@ -69,8 +76,9 @@ def _w(t: torch.Tensor) -> torch.Tensor:
     return t.to(F64)
 
 
-def decode_step(dims, weights: dict, seqs: list[SeqState], layer_hook=None) -> StepResult:
+def decode_step(dims, weights: dict, seqs: list[SeqState], layer_hook=None, compute: str = "f64") -> StepResult:
     """Run one step for all rows of all sequences; updates each seq.kv in place."""
+    cdt = {"f64": F64, "f32": torch.float32}[compute]
     dt = dims.dtype
     H, Hkv, Dh = dims.n_heads, dims.n_kv_heads, dims.head_dim
     group = H // Hkv  # query heads per KV head (1 for MHA)
@@ -90,12 +98,12 @@ def decode_step(dims, weights: dict, seqs: list[SeqState], layer_hook=None) -> S
     for l in range(dims.n_layers):
         lw = weights["layers"][l]
         # --- attention block ---
-        xn = round_to(rmsnorm(x, lw["attn_norm"], dims.eps), dt)
-        q = linear(xn, lw["wq"]).reshape(M, H, Dh)
-        k = linear(xn, lw["wk"]).reshape(M, Hkv, Dh)
-        v = linear(xn, lw["wv"]).reshape(M, Hkv, Dh)
-        q = round_to(rope(q, pos, dims.rope_theta), dt)
-        k = round_to(rope(k, pos, dims.rope_theta), dt)
+        xn = round_to(rmsnorm(x, lw["attn_norm"], dims.eps, cdt), dt)
+        q = linear(xn, lw["wq"], cdt).reshape(M, H, Dh)
+        k = linear(xn, lw["wk"], cdt).reshape(M, Hkv, Dh)
+        v = linear(xn, lw["wv"], cdt).reshape(M, Hkv, Dh)
+        q = round_to(rope(q, pos, dims.rope_theta, cdt), dt)
+        k = round_to(rope(k, pos, dims.rope_theta, cdt), dt)
         v = round_to(v, dt)
         for r, (b, i) in enumerate(rows):  # append this step's K/V rows to each cache
             p = int(pos[r])
@@ -108,22 +116,22 @@ def decode_step(dims, weights: dict, seqs: list[SeqState], layer_hook=None) -> S
             if n_rows == 0:
                 continue
             n_keys = s.ctx + n_rows
-            K = s.kv[l, 0, :n_keys].to(F64)  # [n_keys][Hkv][Dh]
-            V = s.kv[l, 1, :n_keys].to(F64)
+            K = s.kv[l, 0, :n_keys].to(cdt)  # [n_keys][Hkv][Dh]
+            V = s.kv[l, 1, :n_keys].to(cdt)
             # row i (position ctx + i) keeps keys 0..ctx + i
             keep = torch.arange(n_keys).unsqueeze(0) <= (s.ctx + torch.arange(n_rows)).unsqueeze(1)
             for h in range(H):
                 kh = K[:, h // group, :]
                 vh = V[:, h // group, :]
-                o[r0:r0 + n_rows, h, :] = attention_standard(q[r0:r0 + n_rows, h, :], kh, vh, keep,
+                o[r0:r0 + n_rows, h, :] = attention_standard(q[r0:r0 + n_rows, h, :].to(cdt), kh, vh, keep,
                                                              1.0 / math.sqrt(Dh))
             r0 += n_rows
         o = round_to(o.reshape(M, H * Dh), dt)
-        x = round_to(x + linear(o, lw["wo"]), "f32")
+        x = round_to(x + linear(o, lw["wo"], cdt), "f32")
         # --- MLP block ---
-        xn2 = round_to(rmsnorm(x, lw["ffn_norm"], dims.eps), dt)
-        hmid = round_to(swiglu(linear(xn2, lw["wg"]), linear(xn2, lw["wu"])), dt)
-        x = round_to(x + linear(hmid, lw["wd"]), "f32")
+        xn2 = round_to(rmsnorm(x, lw["ffn_norm"], dims.eps, cdt), dt)
+        hmid = round_to(swiglu(linear(xn2, lw["wg"], cdt), linear(xn2, lw["wu"], cdt), cdt), dt)
+        x = round_to(x + linear(hmid, lw["wd"], cdt), "f32")
         if layer_hook is not None:
             layer_hook(l, x)
 
@@ -132,8 +140,8 @@ def decode_step(dims, weights: dict, seqs: list[SeqState], layer_hook=None) -> S
     res.argmax = [-1] * M
     res.gap = [float("nan")] * M
     if want:
-        xf = round_to(rmsnorm(x[want], weights["final_norm"], dims.eps), dt)
-        logits = round_to(linear(xf, weights["lm_head"]), "f32")
+        xf = round_to(rmsnorm(x[want], weights["final_norm"], dims.eps, cdt), dt)
+        logits = round_to(linear(xf, weights["lm_head"], cdt), "f32")
         for j, r in enumerate(want):
             res.logits[r] = logits[j]
             res.argmax[r], res.gap[r] = argmax_lowest(logits[j])

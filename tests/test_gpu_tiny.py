@@ -9,6 +9,7 @@ import torch
 
 import oracle
 import synth
+import verify_step_amd as vs
 from harness import GpuModel, GpuPool, SeqSpec, alloc_rows, make_step, run_step
 from harness.compare import TOL, check_argmax, check_rows
 from synth import workloads as W
@@ -59,7 +60,7 @@ def check_case(dims, sb, ref, seqs_o, pool, rows, ctxs, rows_per_seq):
     check_rows([gpu_logits[j] for j in range(len(lrows))], [ref.logits[r] for r in lrows], tol, "logits")
     n_exact = 0
     for j, r in enumerate(lrows):
-        n_exact += check_argmax(am[r], ref.argmax[r], ref.logits[r], ref.gap[r], f"row {r}")
+        n_exact += check_argmax(am[r], ref.argmax[r], ref.logits[r], ref.gap[r], f"row {r}", gpu_logits[j])
         if am[r] == ref.argmax[r]:
             assert abs(float(gap[r]) - ref.gap[r]) <= tol * max(1.0, float(ref.logits[r].abs().max())), \
                 f"row {r} gap {float(gap[r])} vs {ref.gap[r]}"
@@ -153,3 +154,112 @@ def test_tiny_rows_without_logits_and_long_context():
     ctxs, k = [1000, 7, 300], [1, 4, 2]
     sb, ref, so, pool, rows = run_case(dims, ctxs, k, want=[True, False, True], pool_pages=128)
     check_case(dims, sb, ref, so, pool, rows, ctxs, k)
+
+
+@pytest.mark.parametrize("want_any", [True, False])
+def test_tiny_edge_cases(want_any):
+    """First token of a sequence (no cache), a sequence with no rows this step, a row on the last slot of a
+    page, nine rows in one sequence (more than one row group of the attention kernel), and a step without
+    any logit row."""
+    _say(f"tiny edge cases, logits={want_any}")
+    dims = W.TINY.with_dtype("f16")
+    ctxs, k = [0, 16, 15, 30, 3], [1, 0, 1, 9, 2]
+    want = [want_any, want_any, want_any, want_any, False]
+    sb, ref, so, pool, rows = run_case(dims, ctxs, k, gains="random", want=want)
+    check_case(dims, sb, ref, so, pool, rows, ctxs, k)
+
+
+def test_tiny_paged_equals_contiguous_bitwise():
+    """The same logical K/V behind two different block tables (ascending pages, shuffled pages) gives
+    bit-identical outputs: the page indirection changes addresses only."""
+    _say("tiny paged == contiguous")
+    dims = W.TINY.with_dtype("f16")
+    w_cpu = W.make_weights(dims, SEED_W, gains="random")
+    model = GpuModel(dims, weights_cpu=w_cpu)
+    ctxs, k = [40, 100, 7], [1, 3, 2]
+    outs = []
+    for shuffle in (None, synth.key(SEED_PAGES, 9)):
+        pool = GpuPool(dims, 64)
+        rows = alloc_rows(pool, [c + n for c, n in zip(ctxs, k)], shuffle_key=shuffle)
+        if shuffle is None:
+            flat = [p for r in rows for p in r]
+            assert flat == sorted(flat)
+        for b in range(3):
+            pool.write(rows[b], 0, W.kv_block(dims, SEED_KV, b, 0, ctxs[b]))
+        toks = [W.token_ids(SEED_TOK, 300 + b, k[b], dims.vocab) for b in range(3)]
+        sb = make_step(model, pool, [SeqSpec(c, t) for c, t in zip(ctxs, toks)], rows)
+        run_step(model, sb)
+        torch.cuda.synchronize()
+        kv_new = [pool.read(rows[b], ctxs[b], ctxs[b] + k[b]) for b in range(3)]
+        outs.append((sb.logits.cpu(), sb.argmax.cpu(), sb.gap.cpu(), kv_new))
+        pool.close()
+    a, b = outs
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    assert all(torch.equal(x, y) for x, y in zip(a[3], b[3]))
+
+
+def test_tiny_copy_on_append_of_a_shared_partial_page():
+    """Two sequences share a 1000-token prefix (62.5 pages). The first to append gets a private copy of the
+    half-filled last page (one page copy enqueued by kv_append); the second then owns the original alone
+    and appends in place. Both steps match the oracle run on contiguous caches."""
+    _say("tiny copy-on-append")
+    dims = W.TINY.with_dtype("f16")
+    w_cpu = W.make_weights(dims, SEED_W)
+    model = GpuModel(dims, weights_cpu=w_cpu)
+    pool = GpuPool(dims, 160)
+    ctx = 1000
+    pre = vs.kv_alloc(pool.handle, -(-ctx // 16))
+    kv = W.kv_block(dims, SEED_KV, 0, 0, ctx)
+    pool.write(pre, 0, kv)
+    vs.kv_share(pool.handle, pre)
+    last = pre[-1]
+    assert vs.kv_refcount(pool.handle, last) == 2
+    max_blocks = -(-(ctx + 1) // 16)
+    free0 = vs.kv_num_free(pool.handle)
+    r0 = vs.kv_append(pool.handle, pre, max_blocks, ctx, 1, torch.cuda.current_stream().cuda_stream)
+    assert r0[:-1] == pre[:-1] and r0[-1] != last
+    assert vs.kv_refcount(pool.handle, last) == 1 and vs.kv_refcount(pool.handle, r0[-1]) == 1
+    assert vs.kv_num_free(pool.handle) == free0 - 1
+    r1 = vs.kv_append(pool.handle, pre, max_blocks, ctx, 1, torch.cuda.current_stream().cuda_stream)
+    assert r1 == pre, "the last holder of a page writes into it without a copy"
+    assert vs.kv_num_free(pool.handle) == free0 - 1
+    torch.cuda.synchronize()
+    # the copy holds the filled slots of the shared page
+    assert torch.equal(pool.view()[r0[-1], :, :, :, :ctx % 16], pool.view()[last, :, :, :, :ctx % 16])
+    toks = [W.token_ids(SEED_TOK, 400 + b, 1, dims.vocab) for b in range(2)]
+    sb = make_step(model, pool, [SeqSpec(ctx, toks[0]), SeqSpec(ctx, toks[1])], [r0, r1])
+    run_step(model, sb)
+    torch.cuda.synchronize()
+    seqs_o = []
+    for b in range(2):
+        full = torch.zeros(dims.n_layers, 2, ctx + 1, dims.n_kv_heads, dims.head_dim, dtype=dims.torch_dtype)
+        full[:, :, :ctx] = kv
+        seqs_o.append(oracle.SeqState(full, ctx, list(toks[b])))
+    ref = oracle.decode_step(dims, w_cpu, seqs_o)
+    check_case(dims, sb, ref, seqs_o, pool, [r0, r1], [ctx, ctx], [1, 1])
+    pool.close()
+
+
+def test_verify_accept_entry_point_against_the_rule():
+    """verify_accept on device arrays, every sequence length 0..5 and tokens from {0, 1, 2} so that matches
+    are frequent; compared with the acceptance rule of the oracle, exactly."""
+    _say("verify_accept entry point")
+    gen = torch.Generator().manual_seed(1007)
+    B = 257
+    K = torch.randint(0, 6, (B,), generator=gen)
+    q_start = torch.zeros(B + 1, dtype=torch.int32)
+    q_start[1:] = torch.cumsum(K, 0)
+    M = int(q_start[-1])
+    drafts = torch.randint(0, 3, (M,), generator=gen, dtype=torch.int32)
+    argmax = torch.randint(0, 3, (M,), generator=gen, dtype=torch.int32)
+    g0 = torch.randint(0, 3, (B,), generator=gen, dtype=torch.int32)
+    dev = [t.cuda() for t in (q_start, drafts, g0, argmax)]
+    acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    bon = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    vs.verify_accept(B, *dev, acc, bon, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    acc, bon = acc.cpu().tolist(), bon.cpu().tolist()
+    for b in range(B):
+        s, e = int(q_start[b]), int(q_start[b + 1])
+        want = oracle.accept_greedy(drafts[s:e].tolist(), int(g0[b]), argmax[s:e].tolist())
+        assert (acc[b], bon[b]) == want, (b, drafts[s:e].tolist(), int(g0[b]), argmax[s:e].tolist())

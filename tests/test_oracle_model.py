@@ -236,3 +236,26 @@ def test_grouped_kv_heads_equal_duplicated_full_heads():
     rm = decode_step(m, wm, [sm])
     for i in range(3):
         assert rel(rg.logits[i], rm.logits[i]) < 1e-12
+
+
+def test_fp32_realisation_agrees_to_rounding(model):
+    """compute="f32" keeps the storage points and changes only the arithmetic between them: on the
+    all-fp32 tiny model the two realisations agree to fp32 rounding, and with fp16 / bf16 storage they
+    agree within the storage type's tolerance through one layer; the cache rows they write differ only
+    by a rounding step of the storage type."""
+    dims, w = model
+    a = [seq(dims, b, c, W.token_ids(1003, 40 + b, 2, dims.vocab)) for b, c in enumerate([5, 40])]
+    b32 = [clone(s) for s in a]
+    r64 = decode_step(dims, w, a)
+    r32 = decode_step(dims, w, b32, compute="f32")
+    bound = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2}[dims.dtype]
+    for x, y in zip(r64.logits, r32.logits):
+        assert rel(y, x) < bound
+        assert rel(y, x) > 0 or dims.dtype != "f32"  # a different summation really happened
+    # per cached row (layer, K|V, position): fp32 storage differs by accumulation rounding only; fp16 /
+    # bf16 storage by at most one rounding step of the row's largest element
+    step = {"f32": 2.0 ** -16, "f16": 2.0 ** -10, "bf16": 2.0 ** -7}[dims.dtype]
+    for s64, s32 in zip(a, b32):
+        x, y = s64.kv.double(), s32.kv.double()
+        d = (x - y).abs().amax(dim=(3, 4))
+        assert bool((d <= step * x.abs().amax(dim=(3, 4))).all())
