@@ -5,8 +5,9 @@ vocab 32000, RMSNorm + RoPE, fp16 random-init weights N(0, 0.02) (13.2 GB
 streamed per step), one sequence whose 2048-token synthetic context sits in
 16-token pages scattered through the pool, K = 1, each step's input token is
 the previous step's argmax. One "step" is one decode_step over the whole
-path (embedding, 32 layers, LM head, argmax) plus the host's per-step page
-bookkeeping (kv_append) and the on-device token / length update.
+path (embedding, 32 layers, LM head, argmax, which also feeds the next
+step's token and advances the context length on the device) plus the host's
+per-step page bookkeeping (kv_append).
 
 Prints one JSON line. `value` is decode tokens/s over the timed steps;
 `roofline` reports the gate/up product (the kernel that streams the most
@@ -133,6 +134,11 @@ def main():
     sb.desc.max_ctx = total_len
     sb.ws_bytes = vs.decode_step_workspace_bytes(sb.desc, __import__("harness").model_desc(dims))
     sb.ws = torch.empty(sb.ws_bytes, dtype=torch.uint8, device=dev)
+    # a device-side greedy loop: each step reads its input token from the argmax array the previous
+    # step wrote, and advances the context length itself
+    sb.argmax[:1].copy_(sb.tokens[:1])
+    sb.desc.tokens = sb.argmax.data_ptr()
+    sb.desc.ctx_advance = sb.ctx_len.data_ptr()
     bt_host = torch.zeros(max_blocks, dtype=torch.int32).pin_memory()
     bt_host[:len(row)] = torch.tensor(row, dtype=torch.int32)
     sb.block_tables[0].copy_(bt_host)
@@ -144,8 +150,6 @@ def main():
     def device_step():
         vs.decode_step(sb.desc, sb.block_tables, model.w, sb.out, sb.ws, sb.ws_bytes,
                        torch.cuda.current_stream().cuda_stream)
-        sb.tokens.copy_(sb.argmax[:1])
-        sb.ctx_len.add_(1)
 
     def host_bookkeeping():
         # the step about to run writes position len + 1's K/V next time; make room for it

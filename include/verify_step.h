@@ -179,8 +179,15 @@ typedef struct vs_batch_desc {
     const vs_pool* pool;
     const int32_t* q_start;    /* device [B+1], q_start[0] = 0, non-decreasing */
     const int32_t* ctx_len;    /* device [B] */
-    const int32_t* tokens;     /* device [M] token ids (the draft tokens of a verify pass) */
+    const int32_t* tokens;     /* device [M] token ids (the draft tokens of a verify pass). May be the
+                                  same array as out->argmax when acceptance is not fused: every
+                                  token is read before any argmax is written, so a replayed
+                                  greedy loop feeds each step's tokens to the next. */
     const int32_t* logit_rows; /* device [M_log], ascending row indices; NULL if M_log = 0 */
+    int32_t* ctx_advance;      /* device [B] or NULL. If set, the step's last kernel adds each
+                                  sequence's row count to ctx_advance[b] after every other use of
+                                  ctx_len; it may be ctx_len itself (a replayed decode loop then
+                                  needs no host update of the context lengths). */
 } vs_batch_desc;
 
 typedef struct vs_step_out {

@@ -75,11 +75,14 @@ def test_7b_decode_b1_graph_replays_match_oracle():
     st = oracle.SeqState(full, CTX0, list(tok0))
     st32 = oracle.SeqState(full.clone(), CTX0, list(tok0))  # the oracle's fp32 realisation, its own cache
 
+    # the benchmark's device-side loop: tokens are read from the argmax array, ctx_len advances in the step
+    sb.argmax[:1].copy_(sb.tokens[:1])
+    sb.desc.tokens = sb.argmax.data_ptr()
+    sb.desc.ctx_advance = sb.ctx_len.data_ptr()
+
     def device_step():
         vs.decode_step(sb.desc, sb.block_tables, model.w, sb.out, sb.ws, sb.ws_bytes,
                        torch.cuda.current_stream().cuda_stream)
-        sb.tokens.copy_(sb.argmax[:1])
-        sb.ctx_len.add_(1)
 
     state = {"row": row, "len": CTX0}
 
@@ -117,7 +120,7 @@ def test_7b_decode_b1_graph_replays_match_oracle():
         for l in range(dims.n_layers):
             check_rows([got[l, 0, 0], got[l, 1, 0]], [want[l, 0, 0], want[l, 1, 0]], TOL[dims.dtype],
                        f"step {step} layer {l} K/V", [want32[l, 0, 0], want32[l, 1, 0]])
-        assert int(sb.tokens[0]) == am and int(sb.ctx_len[0]) == pos + 1
+        assert int(sb.ctx_len[0]) == pos + 1, "the step advances the context length"
         for o in (st, st32):
             o.ctx += 1
             o.tokens = [am]

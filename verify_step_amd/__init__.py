@@ -58,7 +58,7 @@ class vs_pool_desc(Structure):
 class vs_batch_desc(Structure):
     _fields_ = [("B", c_int32), ("M", c_int32), ("M_log", c_int32), ("max_rows", c_int32), ("max_ctx", c_int32),
                 ("max_blocks", c_int32), ("pool", c_void_p), ("q_start", c_void_p), ("ctx_len", c_void_p),
-                ("tokens", c_void_p), ("logit_rows", c_void_p)]
+                ("tokens", c_void_p), ("logit_rows", c_void_p), ("ctx_advance", c_void_p)]
 
 
 class vs_step_out(Structure):

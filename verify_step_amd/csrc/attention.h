@@ -9,8 +9,10 @@
 // Efficiency] section 31.4, Example 31.2: combine statistics, not normalised
 // tile outputs).
 //
-// One workgroup of four waves per (split, head, sequence). Wave w takes pages
-// w, w+4, ... of the split. Lane l owns dims [(l%16)*DH/16, +DH/16) of key slot
+// With a single split the workgroup's state is final: it writes the attention
+// output itself (o / l in the storage type) and no merge is needed.
+// One workgroup of NW waves per (split, head, sequence). Wave w takes pages
+// w, w+NW, ... of the split. Lane l owns dims [(l%16)*DH/16, +DH/16) of key slot
 // (l/16) within each group of four keys, so one page of 16 keys is four loads
 // per lane for K and four for V, and the 16 lanes that share a key finish its
 // dot product with DPP row sums. Every K/V byte is used by exactly one wave, so
@@ -27,8 +29,6 @@
 
 namespace vs {
 
-constexpr int kAttnWaves = 4;
-
 struct AttnArgs {
     const void* q;  // [M][n_heads*DH] storage type, rotated
     const void* kv_base;
@@ -42,14 +42,20 @@ struct AttnArgs {
     const int* ctx_len;
     int n_splits, split_pages;
     float scale_log2;  // log2(e) / sqrt(DH)
-    float* part;       // [M][n_heads][n_splits][DH + 2]: m (log2 domain), l, o[DH]
+    float* part;       // [M][n_heads][n_splits][part_stride(DH)]: m (log2 domain), l, -, -, o[DH]
     void* out;         // [M][n_heads*DH] storage type
 };
 
-template <int DT, int DH, int RMAX>
-__global__ void __launch_bounds__(kAttnWaves * 64) attn_split_kernel(AttnArgs a) {
+// One split's statistics: m, l, two unused floats (so o starts 16-byte aligned), o[dh].
+__host__ __device__ constexpr int part_stride(int dh) { return dh + 4; }
+constexpr int kPartO = 4;  // offset of o in a split's statistics
+
+// o / l; a row with no visible key (l = 0, only if the block table is cut short) gives 0
+__device__ __forceinline__ float safe_div(float o, float l) { return l > 0.f ? o / l : 0.f; }
+
+template <int DT, int DH, int RMAX, int NW>
+__global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
     constexpr int DPL = DH / 16;  // dims per lane
-    constexpr int NW = kAttnWaves;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -182,7 +188,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attn_split_kernel(AttnArgs a)
             }
         }
         __syncthreads();
-        // merge the four waves in wave order; thread t takes (row, dim) pairs
+        // merge the waves in wave order; thread t takes (row, dim) pairs
         for (int idx = tid; idx < nr * DH; idx += NW * 64) {
             const int i = idx / DH, d = idx % DH;
             float mx = -INFINITY;
@@ -199,12 +205,16 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attn_split_kernel(AttnArgs a)
                     os += f * wst[w][i][2 + d];
                 }
             }
-            float* dst = a.part + (((long)(r0 + rg + i) * a.n_heads + h) * a.n_splits + s) * (DH + 2);
-            if (d == 0) {
-                dst[0] = mx;
-                dst[1] = ls;
+            if (a.n_splits == 1) {  // the only split: the state is final
+                store_round<DT>(a.out, (long)(r0 + rg + i) * a.n_heads * DH + (long)h * DH + d, safe_div(os, ls));
+            } else {
+                float* dst = a.part + (((long)(r0 + rg + i) * a.n_heads + h) * a.n_splits + s) * part_stride(DH);
+                if (d == 0) {
+                    dst[0] = mx;
+                    dst[1] = ls;
+                }
+                dst[kPartO + d] = os;
             }
-            dst[2 + d] = os;
         }
         __syncthreads();
     }
@@ -222,10 +232,11 @@ __global__ void __launch_bounds__(DH) attn_merge_kernel(AttnArgs a) {
     __shared__ float s_red[DH / 64];
     const int row = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
     const int ns = min(a.n_splits, kMaxSplits);
-    const float* src = a.part + ((long)row * a.n_heads + h) * a.n_splits * (DH + 2);
+    constexpr int SD = part_stride(DH);
+    const float* src = a.part + ((long)row * a.n_heads + h) * a.n_splits * SD;
     float mx = -INFINITY;
     for (int sp = d; sp < ns; sp += DH) {
-        sm[sp] = src[(long)sp * (DH + 2)];
+        sm[sp] = src[(long)sp * SD];
         mx = fmaxf(mx, sm[sp]);
     }
 #pragma unroll
@@ -241,10 +252,10 @@ __global__ void __launch_bounds__(DH) attn_merge_kernel(AttnArgs a) {
 #pragma unroll 4
     for (int sp = 0; sp < ns; ++sp) {
         const float w = sw[sp];
-        l += w * src[(long)sp * (DH + 2) + 1];
-        o += w * src[(long)sp * (DH + 2) + 2 + d];
+        l += w * src[(long)sp * SD + 1];
+        o += w * src[(long)sp * SD + kPartO + d];
     }
-    store_round<DT>(a.out, (long)row * a.n_heads * DH + (long)h * DH + d, o / l);
+    store_round<DT>(a.out, (long)row * a.n_heads * DH + (long)h * DH + d, safe_div(o, l));
 }
 
 }  // namespace vs

@@ -26,7 +26,7 @@
 namespace vs {
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
-enum XMode { X_PLAIN = 0, X_NORM = 1 };
+enum XMode { X_PLAIN = 0, X_NORM = 1, X_MERGE = 2 };
 
 struct ArgPart {
     float v1;  // largest value in the tile

@@ -22,12 +22,18 @@
 //
 // The workgroup's batch rows X live in LDS in the storage type, loaded once in
 // a prologue that runs while the first weight batch is already in flight:
-// either copied (X_PLAIN) or built from the fp32 residual stream as RMSNorm
+// either copied (X_PLAIN), or built from the fp32 residual stream as RMSNorm
 // output, round(x * rsqrt(mean(x^2) + eps) * gain) (X_NORM), with the sum of
-// squares reduced in a fixed order so every workgroup computes the same scale.
+// squares reduced in a fixed order so every workgroup computes the same scale,
+// or merged from the attention kernel's per-split statistics (X_MERGE, the
+// output product's input): every split is rescaled to the largest running
+// maximum and the summed outputs are divided by the summed sums ([Serving
+// Efficiency] section 31.4; [KV Cache] section 07, Flash-Decoding), in the same
+// order as the standalone merge kernel, so both give the same bits.
 #pragma once
 
 #include "common.h"
+#include "attention.h"
 #include "gemm.h"
 
 namespace vs {
@@ -48,6 +54,9 @@ struct GemvArgs {
     const void* gain;  // X_NORM: gain [K]
     float eps;
     const int* act_rows;  // optional GEMV row -> activation row map
+    // X_MERGE: attention split statistics [rows][n_heads][n_splits][part_stride(head_dim)]
+    const float* part;
+    int n_splits;
     int M;                // batch rows (<= MR)
     int n_units, units_per_wg;
     // rotary + K/V write (EPI_QKV)
@@ -183,6 +192,7 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& g, int u, int m, f
 }
 
 constexpr int kGemvMaxUnits = 128;  // units per workgroup (results parked in LDS)
+constexpr int kMergeMaxSplits = 8;  // X_MERGE: most key splits the prologue merges
 
 template <int DT, int MR, int XM, int EPI, int NW = kGemvWaves, int CG = kGemvChunks>
 __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs g) {
@@ -265,6 +275,49 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs g) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) xs[k + e] = St<DT>::from_f(v[e] * rinv * gv[e]);
             }
+        }
+    } else if constexpr (XM == X_MERGE) {
+        // Thread t builds 8 consecutive elements of one head: it loads that head's (m, l) of every
+        // split and its 8 output values of every split in one batch (a single L2 round trip), then
+        // rescales to the largest maximum and divides the summed outputs by the summed sums, in
+        // split order, as the standalone merge kernel does.
+        constexpr int NS = kMergeMaxSplits;
+        const int H = g.n_heads, ns = g.n_splits, Dh = g.head_dim, SD = part_stride(g.head_dim);
+        const int MK = g.M * K;
+        typename St<DT>::raw* xs = reinterpret_cast<typename St<DT>::raw*>(smem);
+        for (int e0 = tid * 8; e0 < MK; e0 += NW * 64 * 8) {
+            const int m = e0 / K, k = e0 - m * K, h = k / Dh, d0 = k - h * Dh;
+            const float* src = g.part + ((long)m * H + h) * ns * SD;
+            float2 ml[NS];
+            float4_t oa[NS], ob[NS];
+#pragma unroll
+            for (int sp = 0; sp < NS; ++sp) {
+                const float* ss = src + (long)(sp < ns ? sp : ns - 1) * SD;
+                ml[sp] = *reinterpret_cast<const float2*>(ss);
+                oa[sp] = *reinterpret_cast<const float4_t*>(ss + kPartO + d0);
+                ob[sp] = *reinterpret_cast<const float4_t*>(ss + kPartO + d0 + 4);
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int sp = 0; sp < NS; ++sp)
+                if (sp < ns) mx = fmaxf(mx, ml[sp].x);
+            float l = 0.f, o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll
+            for (int sp = 0; sp < NS; ++sp) {
+                if (sp < ns) {
+                    const float w = ml[sp].x == -INFINITY ? 0.f : exp2f(ml[sp].x - mx);
+                    l += w * ml[sp].y;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        o[e] += w * oa[sp][e];
+                        o[4 + e] += w * ob[sp][e];
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xs[e0 + e] = St<DT>::from_f(l > 0.f ? o[e] / l : 0.f);
         }
     } else {
 #pragma unroll

@@ -94,18 +94,19 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* x, const int*
 }
 
 // Per sequence: reduce each logit row's tile partials to (argmax, top-2 gap),
-// then optionally run greedy acceptance over the sequence's rows.
+// then optionally run greedy acceptance over the sequence's rows and advance
+// the sequence's context length by its row count.
 // Grid: B workgroups of 256 threads.
 __global__ void __launch_bounds__(256) argmax_accept_kernel(const ArgPart* parts, int n_tiles, const int* q_start,
                                                             int M, const int* logit_rows, int M_log,
                                                             const int* tokens, const int* g0, int* argmax, float* gap,
-                                                            int* accept_len, int* bonus) {
+                                                            int* accept_len, int* bonus, int* ctx_advance) {
     const int b = blockIdx.x;
     const int r0 = min(max(q_start[b], 0), M);
     const int r1 = min(max(q_start[b + 1], r0), M);
     __shared__ float sv1[4], sv2[4];
     __shared__ int si1[4];
-    for (int r = r0; r < r1; ++r) {
+    for (int r = r0; r < r1 && argmax; ++r) {
         // logit row index of r: binary search in the ascending logit_rows
         int j = -1;
         if (M_log > 0) {
@@ -168,6 +169,7 @@ __global__ void __launch_bounds__(256) argmax_accept_kernel(const ArgPart* parts
         accept_len[b] = n;
         bonus[b] = g;
     }
+    if (ctx_advance && threadIdx.x == 0) ctx_advance[b] += r1 - r0;
 }
 
 // Standalone greedy acceptance: one thread per sequence.

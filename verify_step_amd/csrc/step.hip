@@ -65,11 +65,18 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // and the LDS the GEMV may use for its batch rows.
 constexpr int kGemvMaxRows = 8;
 constexpr size_t kGemvMaxLds = 96 * 1024;
+// Waves per attention workgroup (fewer where more rows per sequence need more registers),
+// and the workgroups the key splits aim for (one per CU).
+int attn_waves(int rmax, int dt) { return rmax == 1 || (rmax == 2 && dt != VS_F32) ? 8 : 4; }
+constexpr long kAttnTargetWgs = 256;
+// Output units per workgroup of the output GEMV when it merges the key splits itself.
+constexpr int kGemvMergeUnits = 16;
 
 struct Plan {
     int B, M, M_log, D, H, Hkv, Dh, F, V, L, dt, esz;
-    int n_splits, split_pages, rmax;
+    int n_splits, split_pages, rmax, attn_waves;
     bool gemv;      // the row-streaming path serves every product of the step
+    bool merge_in_o; // the output product's prologue merges the key splits (no merge kernel)
     int n_lm_parts; // argmax partials per logit row
     size_t off_row_seq, off_row_pos, off_rope, off_x, off_xn, off_q, off_attn, off_h, off_part, off_xf, off_lmpart;
     size_t total;
@@ -116,15 +123,18 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->L = m->n_layers;
     p->dt = m->dtype;
     p->esz = m->dtype == VS_F32 ? 4 : 2;
-    // key splits: about 512 four-wave workgroups over B x heads, at least 4 pages a split
+    // key splits: about one workgroup per CU over B x heads, at least two pages per wave of a split
+    p->rmax = d->max_rows <= 1 ? 1 : d->max_rows <= 2 ? 2 : d->max_rows <= 4 ? 4 : 8;
+    p->attn_waves = attn_waves(p->rmax, m->dtype);
     const int max_pages = (d->max_ctx + kPageTokens - 1) / kPageTokens;
     const long pairs = (long)d->B * m->n_heads;
-    const int ns = (int)std::min<long>(std::max(1, max_pages / 4), std::max<long>(1, (512 + pairs - 1) / pairs));
+    const int ns = (int)std::min<long>(std::max(1, max_pages / (2 * p->attn_waves)),
+                                       std::max<long>(1, (kAttnTargetWgs + pairs - 1) / pairs));
     p->split_pages = (max_pages + ns - 1) / ns;
     p->n_splits = (max_pages + p->split_pages - 1) / p->split_pages;
-    p->rmax = d->max_rows <= 1 ? 1 : d->max_rows <= 2 ? 2 : d->max_rows <= 4 ? 4 : 8;
     const size_t kmax = (size_t)std::max(p->D, p->F);
     p->gemv = d->M <= kGemvMaxRows && (size_t)std::max(d->M, 1) * kmax * p->esz <= kGemvMaxLds;
+    p->merge_in_o = p->gemv && p->n_splits > 1 && p->n_splits <= kMergeMaxSplits;
     p->n_lm_parts = p->gemv ? (p->V + gemv_units_per_wg(p->V) - 1) / gemv_units_per_wg(p->V) : (p->V + 31) / 32;
     const size_t M = (size_t)std::max(d->M, 1), ML = (size_t)std::max(d->M_log, 1);
     size_t o = 0;
@@ -141,7 +151,7 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->off_q = take(M * p->H * p->Dh * p->esz);
     p->off_attn = take(M * p->H * p->Dh * p->esz);
     p->off_h = take(M * p->F * p->esz);
-    p->off_part = take(M * p->H * p->n_splits * (p->Dh + 2) * 4);
+    p->off_part = take(M * p->H * p->n_splits * part_stride(p->Dh) * 4);
     p->off_xf = take(ML * p->D * p->esz);
     p->off_lmpart = take(ML * p->n_lm_parts * sizeof(ArgPart));
     p->total = o;
@@ -189,26 +199,38 @@ void launch_gemv_mr(int kind, const GemvArgs& g, hipStream_t s) {
 }
 
 template <int DT, int XM, int EPI>
-void launch_gemv(int kind, GemvArgs g, hipStream_t s) {
+void launch_gemv(int kind, GemvArgs g, hipStream_t s, int units_per_wg = 0) {
     if (g.M <= 0) return;
-    g.units_per_wg = gemv_units_per_wg(g.n_units);
+    g.units_per_wg = units_per_wg > 0 ? units_per_wg : gemv_units_per_wg(g.n_units);
     if (g.M <= 1) launch_gemv_mr<DT, 1, XM, EPI>(kind, g, s);
     else if (g.M <= 2) launch_gemv_mr<DT, 2, XM, EPI>(kind, g, s);
     else if (g.M <= 4) launch_gemv_mr<DT, 4, XM, EPI>(kind, g, s);
     else launch_gemv_mr<DT, 8, XM, EPI>(kind, g, s);
 }
 
+// The split pass, then the merge kernel unless the splits are merged elsewhere (one split
+// needs none; the output GEMV can merge them in its prologue).
 template <int DT, int DH>
-void launch_attention(const AttnArgs& a, int B, int M, int rmax, hipStream_t s) {
+void launch_attention(const AttnArgs& a, int B, int M, int rmax, bool merge_kernel, hipStream_t s) {
     dim3 grid(a.n_splits, a.n_heads, B);
-    dim3 block(kAttnWaves * 64);
+    const int nw = attn_waves(rmax, DT);
+    dim3 block(nw * 64);
     switch (rmax) {
-        case 1: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 1>, grid, block, 0, s, a); break;
-        case 2: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 2>, grid, block, 0, s, a); break;
-        case 4: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 4>, grid, block, 0, s, a); break;
-        default: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 8>, grid, block, 0, s, a); break;
+        case 1: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 1, 8>, grid, block, 0, s, a); break;
+        case 2:
+            if constexpr (DT != F32) {
+                if (nw == 8) {
+                    launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 2, 8>, grid, block, 0, s, a);
+                    break;
+                }
+            }
+            launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 2, 4>, grid, block, 0, s, a);
+            break;
+        case 4: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 4, 4>, grid, block, 0, s, a); break;
+        default: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 8, 4>, grid, block, 0, s, a); break;
     }
-    launch1(VS_KERNEL_MERGE, attn_merge_kernel<DT, DH>, dim3(M, a.n_heads), dim3(DH), 0, s, a);
+    if (merge_kernel && a.n_splits > 1)
+        launch1(VS_KERNEL_MERGE, attn_merge_kernel<DT, DH>, dim3(M, a.n_heads), dim3(DH), 0, s, a);
 }
 
 // Common epilogue fields of both product paths.
@@ -328,8 +350,8 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
         }
 
         a.layer = l;
-        if (p.Dh == 128) launch_attention<DT, 128>(a, p.B, p.M, p.rmax, s);
-        else launch_attention<DT, 64>(a, p.B, p.M, p.rmax, s);
+        if (p.Dh == 128) launch_attention<DT, 128>(a, p.B, p.M, p.rmax, !p.merge_in_o, s);
+        else launch_attention<DT, 64>(a, p.B, p.M, p.rmax, !p.merge_in_o, s);
 
         // x += W_o attn
         if (p.gemv) {
@@ -341,7 +363,14 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             o.x = x;
             o.x_ld = p.D;
             o.n_units = p.D;
-            launch_gemv<DT, X_PLAIN, EPI_RESID>(VS_KERNEL_OPROJ, o, s);
+            if (p.merge_in_o) {
+                o.part = part;
+                o.n_splits = p.n_splits;
+                // fewer, wider workgroups: each one reads every split's statistics from L2
+                launch_gemv<DT, X_MERGE, EPI_RESID>(VS_KERNEL_OPROJ, o, s, kGemvMergeUnits);
+            } else {
+                launch_gemv<DT, X_PLAIN, EPI_RESID>(VS_KERNEL_OPROJ, o, s);
+            }
         } else {
             GemmArgs o = gm;
             o.w0 = lw.wo;
@@ -439,10 +468,10 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             launch_gemm<DT, EPI_LOGITS>(VS_KERNEL_LMHEAD, lm, s);
         }
     }
-    if (out->argmax) {
+    if (out->argmax || d->ctx_advance) {
         hipLaunchKernelGGL(argmax_accept_kernel, dim3(p.B), dim3(256), 0, s, lmpart, p.n_lm_parts, d->q_start, p.M,
                            d->logit_rows, p.M_log, d->tokens, out->g0, out->argmax, out->top2_gap, out->accept_len,
-                           out->bonus);
+                           out->bonus, d->ctx_advance);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return vs_fail(VS_ERR_HIP, std::string("decode_step launch: ") + hipGetErrorString(e));
