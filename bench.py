@@ -79,6 +79,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly instead of replaying a graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with plain device copies of known size (reference dispatches for HBM byte counters)")
+    ap.add_argument("--workload", default="decode-b1", choices=["decode-b1"] + sorted(OTHER_WORKLOADS),
+                    help="decode-b1 is the headline line; the others measure the remaining step shapes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -97,6 +99,8 @@ def main():
         vsbuild.build()
     vs.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload != "decode-b1":
+        return other_workload(args)
     dev = torch.device("cuda:0")
     dims = W.LLAMA7B  # fp16
     K, Wm = args.steps, args.warmup
@@ -288,6 +292,97 @@ def copy_calibration():
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     log(f"copy calibration: 3 x {COPY_BYTES} B read + written")
+
+
+# ---------------------------------------------------------------- the other step shapes
+
+OTHER_WORKLOADS = {
+    # name: (dtype, batch, rows per sequence, context rule, prompt-chunk rows)
+    "batch-bf16-b8": ("bf16", 8, 1, "uniform", 0),
+    "batch-bf16-b32": ("bf16", 32, 1, "uniform", 0),
+    "batch-bf16-b64": ("bf16", 64, 1, "uniform", 0),
+    "verify-f16-b8k5": ("f16", 8, 5, "1024", 0),
+    "mixed-f16-64+512": ("f16", 64, 1, "prefix", 512),
+}
+
+
+def other_workload(args):
+    """One step of another shape, repeated: continuous batching of B sequences with contexts uniform in
+    128..4096 (bf16), an 8 x 5 verify pass at context 1024, or 64 decode rows on shared 1024-token
+    prefixes plus a 512-row prompt chunk. Every repetition rewrites the same K/V rows, so the work per
+    step is fixed. K/V contents are arbitrary normals (timing does not depend on them)."""
+    import torch
+
+    import synth
+    import verify_step_amd as vs
+    from harness import GpuModel, GpuPool, SeqSpec, make_step
+    from synth import workloads as W
+
+    dt, B, K, ctx_rule, chunk = OTHER_WORKLOADS[args.workload]
+    dims = W.LLAMA7B.with_dtype(dt)
+    wl = 3 if args.workload.startswith("batch") else 4 if args.workload.startswith("verify") else 5
+    t0 = time.time()
+    model = GpuModel(dims, seed=1000 * wl + 1)
+    log(f"weights ready in {time.time() - t0:.1f}s")
+    if ctx_rule == "uniform":
+        ctxs = [int(c) for c in synth.uniform_int(synth.key(1000 * wl + 4, B), 0, B, 128, 4097)]
+    elif ctx_rule == "1024":
+        ctxs = [1024] * B
+    else:
+        ctxs = [1024 + int(s) for s in synth.uniform_int(synth.key(1000 * wl + 4, 1), 0, B, 16, 513)]
+    max_blocks = -(-(max(ctxs + [chunk]) + K) // 16)
+    n_pages = sum(-(-(c + K) // 16) for c in ctxs) + -(-chunk // 16) + 16
+    pool = GpuPool(dims, n_pages)
+    pool.view().normal_()
+    ids = vs.kv_alloc(pool.handle, n_pages)
+    perm = synth.permutation(synth.key(1000 * wl + 6), n_pages)
+    vs.kv_free(pool.handle, [ids[int(i)] for i in perm])
+    rows, specs = [], []
+    prefix_rows = {}
+    for b in range(B):
+        if ctx_rule == "prefix":  # 4 prefixes of 1024 tokens, each shared by 16 sequences
+            p = b // 16
+            if p not in prefix_rows:
+                prefix_rows[p] = vs.kv_alloc(pool.handle, 64)
+            vs.kv_share(pool.handle, prefix_rows[p])
+            r = vs.kv_append(pool.handle, list(prefix_rows[p]), max_blocks, 1024, ctxs[b] - 1024 + K)
+        else:
+            r = vs.kv_alloc(pool.handle, -(-ctxs[b] // 16))
+            r = vs.kv_append(pool.handle, r, max_blocks, ctxs[b], K)
+        rows.append(r)
+        specs.append(SeqSpec(ctxs[b], W.token_ids(1000 * wl + 3, b, K, dims.vocab)))
+    if chunk:
+        rows.append(vs.kv_append(pool.handle, [], max_blocks, 0, chunk))
+        specs.append(SeqSpec(0, W.token_ids(1000 * wl + 3, 999, chunk, dims.vocab), want_logits=False))
+    g0 = [0] * len(specs) if K > 1 else None
+    sb = make_step(model, pool, specs, rows, max_blocks=max_blocks, want_logits_tensor=False, g0=g0)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        vs.decode_step(sb.desc, sb.block_tables, model.w, sb.out, sb.ws, sb.ws_bytes, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    M = sum(len(s.tokens) for s in specs)
+    kvpt = 2 * dims.n_layers * dims.n_kv_heads * dims.head_dim * dims.elem_bytes
+    kv_read = sum(s.ctx + len(s.tokens) for s in specs) * kvpt  # logical K/V bytes the attention reads
+    step_bytes = streamed_weight_bytes(dims) + kv_read + M * kvpt
+    result = {
+        "workload": args.workload, "dtype": dt, "batch": B, "rows": M, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "rows_per_s": round(M * 1000.0 / ms, 1),
+        "step_bytes": step_bytes, "step_TBps": round(step_bytes / (ms * 1e-3) / 1e12, 4),
+        "step_frac_of_hbm_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "contexts": [min(ctxs), max(ctxs)], "prompt_chunk_rows": chunk,
+    }
+    print(json.dumps(result), flush=True)
 
 
 def streamed_weight_bytes(dims):

@@ -211,20 +211,21 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs g) {
     const int NC = (K + CE - 1) / CE;      // 1 KB chunks per row
     const int NG = (NC + CG - 1) / CG;     // bursts per unit
     const int my_units = n_local > wave ? (n_local - wave + NW - 1) / NW : 0;
-    const long lane_byte = (long)lane * 16;
-    const long row_bytes = (long)K * St<DT>::bytes;
+    const uint32_t lane_byte = (uint32_t)lane * 16;
+    const uint32_t row_bytes = (uint32_t)K * St<DT>::bytes;
 
     // One burst: chunks [CG * gi, +CG) of each of the unit's RU rows, all loads unconditional
     // (past a row's end a lane re-reads the row's first 16 bytes; the value is masked out).
     auto issue = [&](uint4(&buf)[RU][CG], const UnitMap& um, int gi) {
 #pragma unroll
         for (int r = 0; r < RU; ++r) {
+            // wave-uniform row address + a 32-bit per-lane offset (scalar-base addressing)
             const char* rowp = reinterpret_cast<const char*>(r == 0 ? um.w[0] : um.w[1]) +
                                (long)(r == 0 ? um.row[0] : um.row[1]) * row_bytes;
 #pragma unroll
             for (int c = 0; c < CG; ++c) {
-                const long off = (long)(gi * CG + c) * 1024 + lane_byte;
-                buf[r][c] = load_stream16(rowp + (off < row_bytes ? off : 0));
+                const uint32_t off = (uint32_t)(gi * CG + c) * 1024u + lane_byte;
+                buf[r][c] = load_stream16(rowp + (off < row_bytes ? off : 0u));
             }
         }
     };
@@ -333,48 +334,70 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs g) {
     }
     __syncthreads();
 
-    for (int uj = 0; uj < my_units; ++uj) {
-        const int ul = wave + NW * uj;
-        const UnitMap um = unit_map<EPI>(g, u_begin + ul);
-        float acc[RU][MR];
+    // The wave's work is a sequence of bursts t = 0 .. my_units * NG - 1 (unit t / NG, burst t % NG).
+    // Single-row units keep the next burst in flight while the current one is consumed (two
+    // buffers); two-row units, whose buffers are twice as large, load one burst at a time.
+    const int total = my_units * NG;
+    float acc[RU][MR];
 #pragma unroll
-        for (int r = 0; r < RU; ++r)
+    for (int r = 0; r < RU; ++r)
 #pragma unroll
-            for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
-        for (int gi = 0; gi < NG; ++gi) {
-            if (uj > 0 || gi > 0) issue(buf, um, gi);
+        for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
+    auto consume = [&](const uint4(&cur)[RU][CG], int t) {
+        const int uj = t / NG, gi = t - uj * NG;
 #pragma unroll
-            for (int c = 0; c < CG; ++c) {
-                const long k = (long)(gi * CG + c) * CE + lane * EPL;
-                const uint32_t keep = k < K ? 0xFFFFFFFFu : 0u;
-                uint4 xf[MR];
+        for (int c = 0; c < CG; ++c) {
+            const long k = (long)(gi * CG + c) * CE + lane * EPL;
+            const uint32_t keep = k < K ? 0xFFFFFFFFu : 0u;
+            uint4 xf[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                if (m < g.M) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(smem + ((long)m * K + (keep ? k : 0)) * St<DT>::bytes);
+                    xf[m] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < RU; ++r) {
+                const uint4 w = make_uint4(cur[r][c].x & keep, cur[r][c].y & keep, cur[r][c].z & keep,
+                                           cur[r][c].w & keep);
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+                    if (m < g.M) acc[r][m] = dot16<DT>(w, xf[m], acc[r][m]);
+            }
+        }
+        if (gi == NG - 1) {  // unit complete: reduce over the wave, park in LDS
+            const int ul = wave + NW * uj;
+#pragma unroll
+            for (int r = 0; r < RU; ++r)
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
                     if (m < g.M) {
-                        const uint4 v =
-                            *reinterpret_cast<const uint4*>(smem + ((long)m * K + (keep ? k : 0)) * St<DT>::bytes);
-                        xf[m] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+                        const float s2 = wave_sum(acc[r][m]);
+                        if (lane == 0) res[ul][r][m] = s2;
                     }
+                    acc[r][m] = 0.f;
                 }
-#pragma unroll
-                for (int r = 0; r < RU; ++r) {
-                    const uint4 w = make_uint4(buf[r][c].x & keep, buf[r][c].y & keep, buf[r][c].z & keep,
-                                               buf[r][c].w & keep);
-#pragma unroll
-                    for (int m = 0; m < MR; ++m)
-                        if (m < g.M) acc[r][m] = dot16<DT>(w, xf[m], acc[r][m]);
-                }
-            }
         }
-        // unit complete: reduce over the wave, park in LDS
-#pragma unroll
-        for (int r = 0; r < RU; ++r)
-#pragma unroll
-            for (int m = 0; m < MR; ++m)
-                if (m < g.M) {
-                    const float s2 = wave_sum(acc[r][m]);
-                    if (lane == 0) res[ul][r][m] = s2;
-                }
+    };
+    auto issue_t = [&](uint4(&dst)[RU][CG], int t) {
+        const int uj = t / NG;
+        issue(dst, unit_map<EPI>(g, u_begin + wave + NW * uj), t - uj * NG);
+    };
+    if constexpr (RU == 1) {
+        uint4 buf2[RU][CG];
+        for (int t = 0; t < total; t += 2) {
+            if (t + 1 < total) issue_t(buf2, t + 1);
+            consume(buf, t);
+            if (t + 1 >= total) break;
+            if (t + 2 < total) issue_t(buf, t + 2);
+            consume(buf2, t + 1);
+        }
+    } else {
+        for (int t = 0; t < total; ++t) {
+            if (t > 0) issue_t(buf, t);
+            consume(buf, t);
+        }
     }
     __syncthreads();
 
