@@ -11,8 +11,9 @@
 //
 // With a single split the workgroup's state is final: it writes the attention
 // output itself (o / l in the storage type) and no merge is needed.
-// One workgroup of NW waves per (split, head, sequence). Wave w takes pages
-// w, w+NW, ... of the split. Lane l owns dims [(l%16)*DH/16, +DH/16) of key slot
+// One workgroup of NW waves per (split, head, sequence, row-group block). Wave w takes pages
+// w, w+NW, ... of the split. A prompt chunk's rows are spread over row-group blocks, so its
+// row groups run in parallel. Lane l owns dims [(l%16)*DH/16, +DH/16) of key slot
 // (l/16) within each group of four keys, so one page of 16 keys is four loads
 // per lane for K and four for V, and the 16 lanes that share a key finish its
 // dot product with DPP row sums. Every K/V byte is used by exactly one wave, so
@@ -41,6 +42,8 @@ struct AttnArgs {
     const int* q_start;
     const int* ctx_len;
     int n_splits, split_pages;
+    int B;             // sequences; grid z = B x row-group blocks
+    int rg_blocks;     // workgroups over one sequence's row groups (each takes every rg_blocks-th group)
     float scale_log2;  // log2(e) / sqrt(DH)
     float* part;       // [M][n_heads][n_splits][part_stride(DH)]: m (log2 domain), l, -, -, o[DH]
     void* out;         // [M][n_heads*DH] storage type
@@ -61,18 +64,16 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int g = lane >> 4;  // key slot within a group of four
     const int c = lane & 15;  // dim chunk
-    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int s = blockIdx.x, h = blockIdx.y;
+    const int b = blockIdx.z % a.B, rgb = blockIdx.z / a.B;
     const int group = a.n_heads / a.n_kv_heads;
     const int hk = h / group;
 
     const int r0 = min(max(a.q_start[b], 0), a.M);
     const int R = min(max(a.q_start[b + 1] - r0, 0), a.M - r0);
     const int ctx = max(a.ctx_len[b], 0);
-    const int n_keys = ctx + R;
     const int T = a.page_tokens;
-    const int n_pages = min((n_keys + T - 1) / T, a.max_blocks);
     const int p_begin = s * a.split_pages;
-    const int p_end = min(p_begin + a.split_pages, n_pages);
 
     const int* bt = a.block_tables + (long)b * a.max_blocks;
     const long kofs = (long)a.layer * a.layer_elems + (long)hk * T * DH + (long)c * DPL;
@@ -82,8 +83,12 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
 
     __shared__ float wst[NW][RMAX][DH + 2];  // per-wave (m, l, o) of each row
 
-    for (int rg = 0; rg < R; rg += RMAX) {
+    // row groups of RMAX rows: this workgroup takes groups rgb, rgb + rg_blocks, ...; a group's last
+    // row sits at position ctx + rg + nr - 1, so the group reads only the pages up to there
+    for (int rg = rgb * RMAX; rg < R; rg += a.rg_blocks * RMAX) {
         const int nr = min(RMAX, R - rg);
+        const int n_pages = min((ctx + rg + nr + T - 1) / T, a.max_blocks);
+        const int p_end = min(p_begin + a.split_pages, n_pages);
         float qr[RMAX][DPL];
         float o[RMAX][DPL];
         float m[RMAX], l[RMAX];

@@ -26,6 +26,10 @@
 namespace vs {
 
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+// A tile workgroup multiplies one group of MT x 16 batch rows (MT <= 4); larger steps run several
+// row groups per tile, launched next to each other so that they share the tile's weight reads in the
+// caches (their weight loads then keep the normal cache policy instead of streaming).
 enum XMode { X_PLAIN = 0, X_NORM = 1, X_MERGE = 2 };
 
 struct ArgPart {
@@ -156,11 +160,11 @@ __device__ __forceinline__ TileMap tile_map(const GemmArgs& g, int t) {
     m.seg = 0;
     m.head = 0;
     m.j = 0;
-    if constexpr (EPI == EPI_RESID || EPI == EPI_LOGITS) {
+    if constexpr (EPI == EPI_RESID || EPI == EPI_LOGITS) {  // one block of 16 rows per tile
         m.w = g.w0;
         m.wb = g.w0;
-        m.rowA = 32 * t;
-        m.rowB = 32 * t + 16;
+        m.rowA = 16 * t;
+        m.rowB = 16 * t;
         m.nrows = g.n0;
     } else if constexpr (EPI == EPI_SWIGLU) {
         m.w = g.w0;   // gate
@@ -205,14 +209,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, const TileMap& 
     if constexpr (EPI == EPI_LOGITS) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int m = mg * 64 + mt * 16 + l16;
+            const int m = mg * (16 * MT) + mt * 16 + l16;
             float v1 = -INFINITY, v2 = -INFINITY;
             int i1 = 0x7FFFFFFF;
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            {
+                constexpr int b = 0;  // one 16-row block per tile
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int col = (b ? tm.rowB : tm.rowA) + nl0 + r;
+                    const int col = tm.rowA + nl0 + r;
                     const float v = acc[mt][b][r];
                     if (col < g.vocab) {
                         if (m < g.M && g.logits) g.logits[(long)m * g.vocab + col] = v;
@@ -239,21 +243,19 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, const TileMap& 
     } else if constexpr (EPI == EPI_RESID) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int m = mg * 64 + mt * 16 + l16;
+            const int m = mg * (16 * MT) + mt * 16 + l16;
             if (m >= g.M) continue;
             float* xr = g.x + (long)m * g.x_ld;
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int col = (b ? tm.rowB : tm.rowA) + nl0 + r;
-                    if (col < tm.nrows) xr[col] += acc[mt][b][r];
-                }
+            for (int r = 0; r < 4; ++r) {  // one 16-row block per tile
+                const int col = tm.rowA + nl0 + r;
+                if (col < tm.nrows) xr[col] += acc[mt][0][r];
+            }
         }
     } else {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int m = mg * 64 + mt * 16 + l16;
+            const int m = mg * (16 * MT) + mt * 16 + l16;
             if (m >= g.M) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -300,10 +302,17 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, const TileMap& 
 
 template <int DT, int MT, int NW, int EPI, int U>
 __global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
+    constexpr bool SB = EPI == EPI_RESID || EPI == EPI_LOGITS;  // tiles of one 16-row block
+    constexpr int NB = SB ? 1 : 2;
+    constexpr int ROWB = 256 + 16;  // LDS slab row stride in bytes (padding spreads the banks)
+    constexpr int SLAB = NB * 16 * ROWB;
+    constexpr int RED = (NW / 2) * MT * 8 * 64 * 4;
+    // per-wave weight slabs during the main loop, the partial-tile tree afterwards
+    __shared__ __align__(16) unsigned char lds[(NW * SLAB > RED ? NW * SLAB : RED)];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (scalar)
-    const int tile = blockIdx.x;
-    const int mg = blockIdx.y;  // 64-row group
+    const int mg = blockIdx.x;    // 64-row group (fastest: a tile's row groups run together and share its weights)
+    const int tile = blockIdx.y;
     const TileMap tm = tile_map<EPI>(g, tile);
 
     const int KC = g.K / 32;
@@ -319,7 +328,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
     bool xv[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int m = mg * 64 + mt * 16 + l16;
+        const int m = mg * (16 * MT) + mt * 16 + l16;
         xv[mt] = m < g.M;
         xbase[mt] = (long)(xv[mt] ? m : 0) * g.act_ld + kofs;
     }
@@ -331,30 +340,128 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
         acc[mt][1] = acc[mt][0];
     }
 
-    for (int kc = kc0; kc < kc1; kc += U) {
-        Frag<DT> fa[U], fb[U], fx[U][MT];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const bool in = kc + u < kc1;
-            const long ko = (long)(kc + u) * 32;
-            frag_load<DT, true>(fa[u], tm.w, baseA + ko, in && vA);
-            frag_load<DT, true>(fb[u], tm.wb, baseB + ko, in && vB);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) frag_load<DT>(fx[u][mt], g.act, xbase[mt] + ko, in && xv[mt]);
+    if constexpr (DT == F32) {
+        for (int kc = kc0; kc < kc1; kc += U) {
+            Frag<DT> fa[U], fb[U], fx[U][MT];
+    #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool in = kc + u < kc1;
+                const long ko = (long)(kc + u) * 32;
+                frag_load<DT, true>(fa[u], tm.w, baseA + ko, in && vA);
+                if constexpr (!SB) frag_load<DT, true>(fb[u], tm.wb, baseB + ko, in && vB);
+    #pragma unroll
+                for (int mt = 0; mt < MT; ++mt) frag_load<DT>(fx[u][mt], g.act, xbase[mt] + ko, in && xv[mt]);
+            }
+    #pragma unroll
+            for (int u = 0; u < U; ++u) {
+    #pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    acc[mt][0] = frag_mma<DT>(fa[u], fx[u][mt], acc[mt][0]);
+                    if constexpr (!SB) acc[mt][1] = frag_mma<DT>(fb[u], fx[u][mt], acc[mt][1]);
+                }
+            }
         }
+    } else {
+        // fp16 / bf16: the weights are read four rows x 256 bytes per wave instruction (lane l: row
+        // l / 16 of the four, elements 8 (l % 16) .. +7 of a 128-element block), a pattern that streams
+        // as fast as whole-row reads where the MFMA operand layout (16 rows x 64 bytes) does not. Each
+        // block passes through a wave-private LDS slab and is read back as MFMA A fragments.
+        // Blocks of 128 reduction elements = 4 k-steps; the next block's loads are in flight while
+        // the current one is multiplied.
+        unsigned char* my = lds + wave * SLAB;
+        const bool stream = gridDim.x == 1;  // one row group: every weight byte is used once
+        const int rr = lane >> 4, cc = lane & 15;  // R4 layout: row in the group of four, 16-byte column
+        long rowoff[NB][4];
+        bool rowv[NB][4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                acc[mt][0] = frag_mma<DT>(fa[u], fx[u][mt], acc[mt][0]);
-                acc[mt][1] = frag_mma<DT>(fb[u], fx[u][mt], acc[mt][1]);
+            for (int j = 0; j < 4; ++j) {
+                const int row = (bl ? tm.rowB : tm.rowA) + 4 * j + rr;
+                rowv[bl][j] = row < tm.nrows;
+                rowoff[bl][j] = (long)(rowv[bl][j] ? row : 0) * g.K + 8 * cc;
+            }
+        const uint16_t* wA = reinterpret_cast<const uint16_t*>(tm.w);
+        const uint16_t* wB = reinterpret_cast<const uint16_t*>(tm.wb);
+        auto load_block = [&](uint4(&wv)[NB][4], int kc) {
+            // lanes past the wave's slice load in-bounds data that the mask below clears
+            const bool kin = kc + (cc >> 2) < kc1;
+            const long ko = kin ? (long)kc * 32 : -(long)(8 * cc);  // masked lanes read their row's start
+#pragma unroll
+            for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint16_t* src = (bl ? wB : wA) + rowoff[bl][j] + ko;
+                    const uint4 v = stream ? load_stream16(src) : *reinterpret_cast<const uint4*>(src);
+                    const uint32_t keep = (kin && rowv[bl][j]) ? 0xFFFFFFFFu : 0u;
+                    wv[bl][j] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+                }
+        };
+        auto load_x = [&](Frag<DT>(&fx)[4][MT], int kc) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    frag_load<DT>(fx[ks][mt], g.act, xbase[mt] + (long)(kc + ks) * 32, kc + ks < kc1 && xv[mt]);
+        };
+        auto multiply = [&](const uint4(&wv)[NB][4], const Frag<DT>(&fx)[4][MT]) {
+#pragma unroll
+            for (int bl = 0; bl < NB; ++bl)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<uint4*>(my + bl * 16 * ROWB + (4 * j + rr) * ROWB + 16 * cc) = wv[bl][j];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                Frag<DT> fa, fb;
+                fa.a = *reinterpret_cast<const uint4*>(my + l16 * ROWB + 64 * ks + 16 * (lane >> 4));
+                if constexpr (!SB)
+                    fb.a = *reinterpret_cast<const uint4*>(my + 16 * ROWB + l16 * ROWB + 64 * ks + 16 * (lane >> 4));
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    acc[mt][0] = frag_mma<DT>(fa, fx[ks][mt], acc[mt][0]);
+                    if constexpr (!SB) acc[mt][1] = frag_mma<DT>(fb, fx[ks][mt], acc[mt][1]);
+                }
+            }
+        };
+        uint4 w0[NB][4], w1[NB][4];
+        if constexpr (MT <= 2) {  // weights and activations of the next block both in flight
+            Frag<DT> x0[4][MT], x1[4][MT];
+            if (kc0 < kc1) {
+                load_block(w0, kc0);
+                load_x(x0, kc0);
+            }
+            for (int kc = kc0; kc < kc1; kc += 8) {
+                if (kc + 4 < kc1) {
+                    load_block(w1, kc + 4);
+                    load_x(x1, kc + 4);
+                }
+                multiply(w0, x0);
+                if (kc + 4 >= kc1) break;
+                if (kc + 8 < kc1) {
+                    load_block(w0, kc + 8);
+                    load_x(x0, kc + 8);
+                }
+                multiply(w1, x1);
+            }
+        } else {  // three or four row blocks: only the weights run ahead (registers)
+            Frag<DT> xf[4][MT];
+            if (kc0 < kc1) load_block(w0, kc0);
+            for (int kc = kc0; kc < kc1; kc += 8) {
+                if (kc + 4 < kc1) load_block(w1, kc + 4);
+                load_x(xf, kc);
+                multiply(w0, xf);
+                if (kc + 4 >= kc1) break;
+                if (kc + 8 < kc1) load_block(w0, kc + 8);
+                load_x(xf, kc + 4);
+                multiply(w1, xf);
             }
         }
     }
 
     // fixed-order tree reduction of the NW partial tiles into wave 0
     if constexpr (NW > 1) {
-        __shared__ float red[(NW / 2) * MT * 8 * 64];
+        float* red = reinterpret_cast<float*>(lds);
+        __syncthreads();  // every wave is done with its slab
 #pragma unroll
         for (int s = 1; s < NW; s <<= 1) {
             if ((wave & (2 * s - 1)) == s) {
@@ -362,7 +469,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int b = 0; b < 2; ++b)
+                    for (int b = 0; b < NB; ++b)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) dst[((mt * 2 + b) * 4 + r) * 64 + lane] = acc[mt][b][r];
             }
@@ -372,7 +479,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                    for (int b = 0; b < 2; ++b)
+                    for (int b = 0; b < NB; ++b)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) acc[mt][b][r] += src[((mt * 2 + b) * 4 + r) * 64 + lane];
             }

@@ -59,6 +59,9 @@ struct GemvArgs {
     int n_splits;
     int M;                // batch rows (<= MR)
     int n_units, units_per_wg;
+    // X_PLAIN rows too long for LDS: stage X k_phase elements at a time (0 = all of K at once);
+    // requires one unit per wave (units_per_wg <= waves) and a multiple of one burst
+    int k_phase;
     // rotary + K/V write (EPI_QKV)
     void* q_out;
     void* kv_base;
@@ -320,7 +323,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs g) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) xs[e0 + e] = St<DT>::from_f(l > 0.f ? o[e] / l : 0.f);
         }
-    } else {
+    } else if (g.k_phase == 0) {  // a phased X is staged inside the main loop
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             if (m >= g.M) break;
@@ -343,6 +346,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs g) {
     for (int r = 0; r < RU; ++r)
 #pragma unroll
         for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
+    int xk0 = 0, xkx = K;  // X in LDS: columns [xk0, xk0 + xkx) of every row, row stride xkx
     auto consume = [&](const uint4(&cur)[RU][CG], int t) {
         const int uj = t / NG, gi = t - uj * NG;
 #pragma unroll
@@ -353,7 +357,8 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs g) {
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
                 if (m < g.M) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(smem + ((long)m * K + (keep ? k : 0)) * St<DT>::bytes);
+                    const uint4 v = *reinterpret_cast<const uint4*>(
+                        smem + ((long)m * xkx + (keep ? k - xk0 : 0)) * St<DT>::bytes);
                     xf[m] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
                 }
             }
@@ -384,7 +389,47 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs g) {
         const int uj = t / NG;
         issue(dst, unit_map<EPI>(g, u_begin + wave + NW * uj), t - uj * NG);
     };
-    if constexpr (RU == 1) {
+    bool phased = false;
+    if constexpr (XM == X_PLAIN && RU == 1) {
+        if (g.k_phase > 0) {
+            // X staged one phase of k_phase columns at a time; the wave's single unit streams on,
+            // its next burst already in flight across each phase change
+            phased = true;
+            const int KP = g.k_phase;
+            const int BPP = KP / (CG * CE);  // bursts per phase
+            const bool has = my_units > 0;
+            uint4 buf2[RU][CG];
+            auto stage = [&](int ph) {
+                __syncthreads();  // every wave is done with the previous phase
+                const int k0 = ph * KP;
+                const long nbytes = (long)min(KP, K - k0) * St<DT>::bytes;
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    if (m >= g.M) break;
+                    const int src = g.act_rows ? g.act_rows[m] : m;
+                    const char* ar =
+                        reinterpret_cast<const char*>(g.act) + ((long)src * g.act_ld + k0) * St<DT>::bytes;
+                    char* xs = reinterpret_cast<char*>(smem) + (long)m * KP * St<DT>::bytes;
+                    for (long off = tid * 16; off < nbytes; off += NW * 64 * 16)
+                        *reinterpret_cast<uint4*>(xs + off) = *reinterpret_cast<const uint4*>(ar + off);
+                }
+                __syncthreads();
+                xk0 = k0;
+                xkx = KP;
+            };
+            for (int t = 0; t < NG; t += 2) {
+                if (has && t + 1 < NG) issue_t(buf2, t + 1);
+                if (t % BPP == 0) stage(t / BPP);
+                if (has) consume(buf, t);
+                if (t + 1 >= NG) break;
+                if (has && t + 2 < NG) issue_t(buf, t + 2);
+                if ((t + 1) % BPP == 0) stage((t + 1) / BPP);
+                if (has) consume(buf2, t + 1);
+            }
+        }
+    }
+    if (phased) {
+    } else if constexpr (RU == 1) {
         uint4 buf2[RU][CG];
         for (int t = 0; t < total; t += 2) {
             if (t + 1 < total) issue_t(buf2, t + 1);

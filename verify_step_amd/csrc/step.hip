@@ -61,20 +61,25 @@ void launch1(int kind, void (*kern)(T), dim3 grid, dim3 block, size_t lds, hipSt
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Rows of a step at which the row-streaming GEMV gives way to the MFMA tiles,
+// Rows of a step at which the row-streaming GEMV gives way to the MFMA tiles (beyond four rows the
+// GEMV's LDS reads of the batch rows outrun the weight stream),
 // and the LDS the GEMV may use for its batch rows.
-constexpr int kGemvMaxRows = 8;
+constexpr int kGemvMaxRows = 4;
 constexpr size_t kGemvMaxLds = 96 * 1024;
+// A plain-input product whose rows exceed this much LDS stages X in phases, so that two
+// workgroups still fit on a CU.
+constexpr size_t kGemvPhaseLds = 64 * 1024;
 // Waves per attention workgroup (fewer where more rows per sequence need more registers),
 // and the workgroups the key splits aim for (one per CU).
 int attn_waves(int rmax, int dt) { return rmax == 1 || (rmax == 2 && dt != VS_F32) ? 8 : 4; }
-constexpr long kAttnTargetWgs = 256;
+constexpr long kAttnTargetWaves = 2048;  // eight-wave workgroups: 256 (one per CU)
+constexpr long kAttnTargetWgsFew = 256;  // four-wave workgroups (several rows per sequence) stay at one per CU
 // Output units per workgroup of the output GEMV when it merges the key splits itself.
 constexpr int kGemvMergeUnits = 16;
 
 struct Plan {
     int B, M, M_log, D, H, Hkv, Dh, F, V, L, dt, esz;
-    int n_splits, split_pages, rmax, attn_waves;
+    int n_splits, split_pages, rmax, attn_waves, rg_blocks;
     bool gemv;      // the row-streaming path serves every product of the step
     bool merge_in_o; // the output product's prologue merges the key splits (no merge kernel)
     int n_lm_parts; // argmax partials per logit row
@@ -106,9 +111,9 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     if (!d || !m || !p) return vs_fail(VS_ERR_INVALID, "null argument");
     vs_status st = check_dims(m);
     if (st != VS_OK) return st;
-    if (d->B < 1 || d->M < 0 || d->M_log < 0 || d->M_log > d->M || d->max_rows < 1 || d->max_ctx < 1 ||
-        d->max_blocks < 1)
-        return vs_fail(VS_ERR_INVALID, "batch sizes out of range (B >= 1, 0 <= M_log <= M, max_* >= 1)");
+    if (d->B < 1 || d->B > 65535 || d->M < 0 || d->M_log < 0 || d->M_log > d->M || d->max_rows < 1 ||
+        d->max_ctx < 1 || d->max_blocks < 1)
+        return vs_fail(VS_ERR_INVALID, "batch sizes out of range (1 <= B <= 65535, 0 <= M_log <= M, max_* >= 1)");
     if ((long)d->max_blocks * kPageTokens < d->max_ctx)
         return vs_fail(VS_ERR_SHAPE, "max_blocks * 16 must cover max_ctx");
     p->B = d->B;
@@ -124,18 +129,24 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->dt = m->dtype;
     p->esz = m->dtype == VS_F32 ? 4 : 2;
     // key splits: about one workgroup per CU over B x heads, at least two pages per wave of a split
-    p->rmax = d->max_rows <= 1 ? 1 : d->max_rows <= 2 ? 2 : d->max_rows <= 4 ? 4 : 8;
+    // rows per attention row group (5: a verify pass of five drafts fits one group exactly)
+    p->rmax = d->max_rows <= 1 ? 1 : d->max_rows <= 2 ? 2 : d->max_rows <= 4 ? 4 : d->max_rows <= 5 ? 5 : 8;
     p->attn_waves = attn_waves(p->rmax, m->dtype);
     const int max_pages = (d->max_ctx + kPageTokens - 1) / kPageTokens;
     const long pairs = (long)d->B * m->n_heads;
+    // row groups of a sequence go to separate workgroups (a prompt chunk's groups run in parallel)
+    const int rg_needed = (d->max_rows + p->rmax - 1) / p->rmax;
+    p->rg_blocks = (int)std::max<long>(1, std::min<long>(rg_needed, 65535L / d->B));
+    const long wgs_target = p->attn_waves == 8 ? kAttnTargetWaves / 8 : kAttnTargetWgsFew;
     const int ns = (int)std::min<long>(std::max(1, max_pages / (2 * p->attn_waves)),
-                                       std::max<long>(1, (kAttnTargetWgs + pairs - 1) / pairs));
+                                       std::max<long>(1, (wgs_target + pairs - 1) / pairs));
     p->split_pages = (max_pages + ns - 1) / ns;
     p->n_splits = (max_pages + p->split_pages - 1) / p->split_pages;
-    const size_t kmax = (size_t)std::max(p->D, p->F);
-    p->gemv = d->M <= kGemvMaxRows && (size_t)std::max(d->M, 1) * kmax * p->esz <= kGemvMaxLds;
+    // the row-streaming GEMV serves steps of up to kGemvMaxRows rows (beyond, the products' VALU work
+    // outgrows the weight stream); RMSNorm-input products stage all of X, plain-input ones may phase it
+    p->gemv = d->M <= kGemvMaxRows && (size_t)std::max(d->M, 1) * p->D * p->esz <= kGemvMaxLds;
     p->merge_in_o = p->gemv && p->n_splits > 1 && p->n_splits <= kMergeMaxSplits;
-    p->n_lm_parts = p->gemv ? (p->V + gemv_units_per_wg(p->V) - 1) / gemv_units_per_wg(p->V) : (p->V + 31) / 32;
+    p->n_lm_parts = p->gemv ? (p->V + gemv_units_per_wg(p->V) - 1) / gemv_units_per_wg(p->V) : (p->V + 15) / 16;
     const size_t M = (size_t)std::max(d->M, 1), ML = (size_t)std::max(d->M_log, 1);
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -163,9 +174,8 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
 template <int DT, int MT, int EPI>
 void launch_gemm_mt(int kind, const GemmArgs& g, int NW, int n_mgroups, hipStream_t s) {
     constexpr int U = (DT == F32 ? 4 : 8) / MT > 0 ? (DT == F32 ? 4 : 8) / MT : 1;
-    dim3 grid(g.n_tiles, n_mgroups);
-    if (NW >= 16) launch1(kind, gemm_skinny_kernel<DT, MT, 16, EPI, U>, grid, dim3(16 * 64), 0, s, g);
-    else if (NW >= 8) launch1(kind, gemm_skinny_kernel<DT, MT, 8, EPI, U>, grid, dim3(8 * 64), 0, s, g);
+    dim3 grid(n_mgroups, g.n_tiles);
+    if (NW >= 8) launch1(kind, gemm_skinny_kernel<DT, MT, 8, EPI, U>, grid, dim3(8 * 64), 0, s, g);
     else launch1(kind, gemm_skinny_kernel<DT, MT, 4, EPI, U>, grid, dim3(4 * 64), 0, s, g);
 }
 
@@ -173,21 +183,21 @@ template <int DT, int EPI>
 void launch_gemm(int kind, const GemmArgs& g, hipStream_t s) {
     const int M = g.M;
     if (M <= 0) return;
-    const int n_mgroups = (M + 63) / 64;
-    const int rows = std::min(M, 64);
-    const int MT = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
+    const int MT = std::min((M + 15) / 16, 4);  // row blocks of 16 per group
+    const int n_mgroups = (M + 16 * MT - 1) / (16 * MT);
     const long wgs = (long)g.n_tiles * n_mgroups;
-    int NW = wgs < 256 ? 16 : wgs < 512 ? 8 : 4;
+    int NW = wgs < 1024 ? 8 : 4;
     const int KC = g.K / 32;
     while (NW > 4 && NW > KC) NW >>= 1;
     if (MT == 1) launch_gemm_mt<DT, 1, EPI>(kind, g, NW, n_mgroups, s);
     else if (MT == 2) launch_gemm_mt<DT, 2, EPI>(kind, g, NW, n_mgroups, s);
+    else if (MT == 3) launch_gemm_mt<DT, 3, EPI>(kind, g, NW, n_mgroups, s);
     else launch_gemm_mt<DT, 4, EPI>(kind, g, NW, n_mgroups, s);
 }
 
 template <int DT, int MR, int XM, int EPI>
 void launch_gemv_mr(int kind, const GemvArgs& g, hipStream_t s) {
-    const size_t lds = (size_t)g.M * g.K * St<DT>::bytes;
+    const size_t lds = (size_t)g.M * (g.k_phase > 0 ? g.k_phase : g.K) * St<DT>::bytes;
     static bool attr_set = false;  // per instantiation: allow more than 64 KB of dynamic LDS
     if (!attr_set) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<DT, MR, XM, EPI>),
@@ -202,6 +212,13 @@ template <int DT, int XM, int EPI>
 void launch_gemv(int kind, GemvArgs g, hipStream_t s, int units_per_wg = 0) {
     if (g.M <= 0) return;
     g.units_per_wg = units_per_wg > 0 ? units_per_wg : gemv_units_per_wg(g.n_units);
+    g.k_phase = 0;
+    if (XM == X_PLAIN && (size_t)g.M * g.K * St<DT>::bytes > kGemvPhaseLds) {
+        // phases of whole bursts (kGemvChunks 1 KB chunks), one unit per wave
+        const int burst = kGemvChunks * (1024 / St<DT>::bytes);
+        g.k_phase = (int)(kGemvPhaseLds / ((size_t)g.M * St<DT>::bytes)) / burst * burst;
+        g.units_per_wg = std::min(g.units_per_wg, kGemvWaves);
+    }
     if (g.M <= 1) launch_gemv_mr<DT, 1, XM, EPI>(kind, g, s);
     else if (g.M <= 2) launch_gemv_mr<DT, 2, XM, EPI>(kind, g, s);
     else if (g.M <= 4) launch_gemv_mr<DT, 4, XM, EPI>(kind, g, s);
@@ -212,7 +229,7 @@ void launch_gemv(int kind, GemvArgs g, hipStream_t s, int units_per_wg = 0) {
 // needs none; the output GEMV can merge them in its prologue).
 template <int DT, int DH>
 void launch_attention(const AttnArgs& a, int B, int M, int rmax, bool merge_kernel, hipStream_t s) {
-    dim3 grid(a.n_splits, a.n_heads, B);
+    dim3 grid(a.n_splits, a.n_heads, B * a.rg_blocks);
     const int nw = attn_waves(rmax, DT);
     dim3 block(nw * 64);
     switch (rmax) {
@@ -227,6 +244,7 @@ void launch_attention(const AttnArgs& a, int B, int M, int rmax, bool merge_kern
             launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 2, 4>, grid, block, 0, s, a);
             break;
         case 4: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 4, 4>, grid, block, 0, s, a); break;
+        case 5: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 5, 4>, grid, block, 0, s, a); break;
         default: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 8, 4>, grid, block, 0, s, a); break;
     }
     if (merge_kernel && a.n_splits > 1)
@@ -312,6 +330,8 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     a.ctx_len = d->ctx_len;
     a.n_splits = p.n_splits;
     a.split_pages = p.split_pages;
+    a.B = p.B;
+    a.rg_blocks = p.rg_blocks;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.Dh));
     a.part = part;
     a.out = attn;
@@ -378,7 +398,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             o.K = p.H * p.Dh;
             o.act = attn;
             o.act_ld = p.H * p.Dh;
-            o.n_tiles = (p.D + 31) / 32;
+            o.n_tiles = (p.D + 15) / 16;
             o.x = x;
             o.x_ld = p.D;
             launch_gemm<DT, EPI_RESID>(VS_KERNEL_OPROJ, o, s);
@@ -430,7 +450,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             dn.K = p.F;
             dn.act = hmid;
             dn.act_ld = p.F;
-            dn.n_tiles = (p.D + 31) / 32;
+            dn.n_tiles = (p.D + 15) / 16;
             dn.x = x;
             dn.x_ld = p.D;
             launch_gemm<DT, EPI_RESID>(VS_KERNEL_DOWN, dn, s);
