@@ -263,3 +263,24 @@ def test_verify_accept_entry_point_against_the_rule():
         s, e = int(q_start[b]), int(q_start[b + 1])
         want = oracle.accept_greedy(drafts[s:e].tolist(), int(g0[b]), argmax[s:e].tolist())
         assert (acc[b], bon[b]) == want, (b, drafts[s:e].tolist(), int(g0[b]), argmax[s:e].tolist())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tiny_long_mlp_rows_stage_in_phases(dtype):
+    """An MLP 8192 wide with 4 rows: the down product's input rows (4 x 8192 values) exceed the
+    GEMV's LDS budget and are staged in phases, one unit per wave."""
+    _say(f"tiny phased down product {dtype}")
+    dims = W.ModelDims("tiny-ffn8192", 256, 4, 4, 64, 8192, 1000, 1, dtype)
+    ctxs, k = [9, 40], [2, 2]
+    sb, ref, so, pool, rows = run_case(dims, ctxs, k, gains="random")
+    check_case(dims, sb, ref, so, pool, rows, ctxs, k)
+
+
+def test_tiny_many_key_splits_use_the_merge_kernel():
+    """Few heads and a 3000-token context: more key splits than the output GEMV's prologue merges
+    (eight), so the row-streaming path falls back to the standalone merge kernel."""
+    _say("tiny 3000-token context, many splits")
+    dims = W.TINY.with_dtype("f16")
+    ctxs, k = [3000], [1]
+    sb, ref, so, pool, rows = run_case(dims, ctxs, k, pool_pages=200)
+    check_case(dims, sb, ref, so, pool, rows, ctxs, k)

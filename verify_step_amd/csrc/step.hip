@@ -73,7 +73,7 @@ constexpr size_t kGemvPhaseLds = 64 * 1024;
 // and the workgroups the key splits aim for (one per CU).
 int attn_waves(int rmax, int dt) { return rmax == 1 || (rmax == 2 && dt != VS_F32) ? 8 : 4; }
 constexpr long kAttnTargetWaves = 2048;  // eight-wave workgroups: 256 (one per CU)
-constexpr long kAttnTargetWgsFew = 256;  // four-wave workgroups (several rows per sequence) stay at one per CU
+constexpr long kAttnTargetWgsFew = 512;  // four-wave workgroups (several rows per sequence): two per CU
 // Output units per workgroup of the output GEMV when it merges the key splits itself.
 constexpr int kGemvMergeUnits = 16;
 
