@@ -16,7 +16,8 @@ import torch.nn.functional as F
 import oracle
 from oracle import layers as L
 from oracle.accept import (accept_greedy, expected_tokens_per_pass, rejection_accept_probs,
-                           rejection_output_dist, rejection_residual)
+                           rejection_output_dist, rejection_residual, rejection_verify, sample_index,
+                           softmax_t)
 from oracle.model import kv_bytes_per_token, param_count, streamed_weight_bytes
 from synth.workloads import LLAMA7B
 
@@ -304,6 +305,85 @@ def test_rejection_output_is_target_for_random_distributions():
         p = rng.dirichlet(np.ones(6)).tolist()
         q = rng.dirichlet(np.ones(6) * 0.3).tolist()
         assert rejection_output_dist(p, q) == pytest.approx(p, abs=1e-12)
+
+
+def _emitted_distribution(p0_logits, row_logits, q_rows, K, N=4000):
+    """Distribution of the first emitted token of rejection_verify, with d_1 ~ q_1: the accept test
+    is probed on both sides of its threshold (u just below a keeps d_1, u at a rejects it) and the
+    replacement draw is integrated over a midpoint grid of N values of v (error <= 1/N per token)."""
+    V = len(p0_logits)
+    p0 = softmax_t(p0_logits)
+    dist = [0.0] * V
+    tail = [0.5] * (K - 1)
+    for d in range(V):
+        w = q_rows[0][d]
+        if w == 0:
+            continue
+        a = min(1.0, p0[d] / w)
+        if a > 0:
+            n, x, _ = rejection_verify(p0_logits, row_logits, q_rows, [d] + [0] * (K - 1), [a * (1 - 1e-9)] + tail, 0.5)
+            assert n >= 1, "u below min(1, p/q) keeps the draft"
+            dist[d] += w * a
+        if a < 1:
+            for iv in range(N):
+                n, x, _ = rejection_verify(p0_logits, row_logits, q_rows, [d] + [0] * (K - 1), [a] + tail, (iv + 0.5) / N)
+                assert n == 0, "u at min(1, p/q) rejects the draft"
+                dist[x] += w * (1 - a) / N
+    return dist
+
+
+@pytest.mark.parametrize("which", ["example_31_3", "exercise_3"])
+def test_rejection_verify_reproduces_the_printed_examples(which):
+    """The whole procedure (accept test, residual draw) integrated over its random numbers gives
+    the printed final distribution: the emitted token follows the target, not the draft."""
+    g = golden("rejection_examples.json")[which]
+    lp = [math.log(x) for x in g["p"]]
+    dist = _emitted_distribution(lp, [[0.0, 0.0]], [g["q"]], 1)
+    assert dist == pytest.approx(g["final"], abs=1e-3)
+
+
+def test_rejection_verify_is_lossless_for_random_distributions():
+    """First emitted token ~ p_0 for random p_0, q_1 over 5 tokens, whatever happens after it; the
+    token after an accepted d_1 follows p_1; the token after two accepted drafts follows p_2."""
+    rng = np.random.default_rng(5)
+    for _ in range(4):
+        V, K = 5, 2
+        p0 = rng.normal(0, 1.5, V).tolist()
+        rows = [rng.normal(0, 1.5, V).tolist() for _ in range(K)]
+        qs = [rng.dirichlet(np.ones(V) * 0.5).tolist() for _ in range(K)]
+        assert _emitted_distribution(p0, rows, qs, K) == pytest.approx(softmax_t(p0), abs=1e-3)
+        # with d_1 kept (u_1 = 0), the token after it follows p_1: the same check one position on,
+        # feeding p_1's logits as the "previous" distribution of the shifted pass
+        assert _emitted_distribution(rows[0], rows[1:], qs[1:], 1) == pytest.approx(softmax_t(rows[0]), abs=1e-3)
+        n, _, _ = rejection_verify(p0, rows, qs, [0, 0], [0.0, 0.0], 0.5)
+        assert n >= 1 or softmax_t(p0)[0] == 0
+        # all drafts kept: the extra token is drawn from p_K by inverse CDF
+        ok = [rejection_verify(p0, rows, qs, [0, 0], [0.0, 0.0], (iv + 0.5) / 400) for iv in range(400)]
+        if all(n == 2 for n, _, _ in ok):
+            emp = np.bincount([x for _, x, _ in ok], minlength=V) / 400
+            assert emp.tolist() == pytest.approx(softmax_t(rows[1]), abs=1.0 / 400 + 1e-12)
+
+
+def test_sample_index_is_the_inverse_cdf():
+    rng = np.random.default_rng(9)
+    for _ in range(200):
+        w = rng.random(17) * (rng.random(17) > 0.3)
+        if w.sum() == 0:
+            continue
+        v = float(rng.random())
+        x, margin = sample_index(w.tolist(), v)
+        c = np.cumsum(w)
+        assert x == int(np.searchsorted(c, v * c[-1], side="right"))
+        assert w[x] > 0 and margin >= 0
+
+
+def test_softmax_t_matches_library_and_temperature_sharpens():
+    rng = np.random.default_rng(2)
+    z = rng.normal(0, 3, 50)
+    for T in (0.5, 1.0, 2.0):
+        ref = torch.softmax(torch.tensor(z / T, dtype=torch.float64), 0).tolist()
+        assert softmax_t(z.tolist(), T) == pytest.approx(ref, rel=1e-12)
+    assert max(softmax_t(z.tolist(), 0.5)) > max(softmax_t(z.tolist(), 2.0))
 
 
 # ---------------------------------------------------------------- byte accounting
