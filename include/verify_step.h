@@ -18,10 +18,10 @@
  * Ownership. The caller owns every device buffer: the KV pool's memory, the
  * weights, the batch arrays, the outputs and the workspace. The library owns
  * only host-side pool metadata. Nothing on the step path allocates device
- * memory, synchronises the device, or issues a memset, so decode_step and
- * verify_accept may be captured into a HIP graph.
+ * memory, synchronises the device, or issues a memset, so decode_step,
+ * verify_accept and verify_sample may be captured into a HIP graph.
  *
- * Asynchrony. decode_step, verify_accept and the copy that kv_append may
+ * Asynchrony. decode_step, verify_accept, verify_sample and the copy that kv_append may
  * enqueue are asynchronous on the stream passed in; their inputs must stay
  * valid until the stream reaches them. Argument errors are reported before
  * anything is enqueued. A device fault surfaces as VS_ERR_HIP at a later
@@ -228,6 +228,38 @@ vs_status decode_step(const vs_batch_desc* desc, const int32_t* block_tables, co
 vs_status verify_accept(int32_t B, const int32_t* q_start, const int32_t* drafts, const int32_t* g0,
                         const int32_t* argmax, int32_t* accept_len, int32_t* bonus, hipStream_t stream);
 
+/* Stochastic acceptance of a verify pass by modified rejection sampling
+ * ([Serving Efficiency] section 31.5, Example 31.3; [Spending the Idle]
+ * section 12.4; [Serving] "Lossless"; [KV Cache] section 08). The output
+ * tokens follow the target distribution exactly, whatever the draft
+ * distribution was.
+ *
+ * Sequence b has rows r0 = q_start[b] .. r0+K-1 carrying drafts d_1..d_K
+ * (drafts[r0+j-1]), drawn by the draft model from q_j = q_probs[r0+j-1][.].
+ * Target distributions, softmax(z / temperature) in fp32: p_0 from
+ * p0_logits[b][.] (the previous pass's logits for the position of d_1), p_j
+ * from logits[r0+j-1][.] (this pass's row j-1). In draft order, d_j is kept
+ * when u[r0+j-1] < min(1, p_{j-1}(d_j) / q_j(d_j)); a draft with q_j(d_j) = 0
+ * or an id outside [0, V) is rejected. At the first rejection (n = j-1 kept)
+ * token[b] is drawn from norm(max(0, p_n - q_{n+1})) -- from p_n itself if
+ * that is all zero -- and if every draft is kept (n = K), from p_K. The draw
+ * is the inverse CDF in token-id order: the smallest x whose cumulative weight
+ * exceeds v[b] times the total. accept_len[b] = n.
+ *
+ * Layouts (all device, fp32 row-major, row stride V): p0_logits [B][V],
+ * logits [M][V] indexed by batch row (decode_step's logits when every row
+ * produces logits, M_log = M), q_probs [M][V] (each row a distribution),
+ * u [M] and v [B] uniforms in [0, 1) that the caller draws. Rows must have a
+ * finite maximum; -inf entries are allowed. temperature > 0 and finite.
+ * ws: device workspace of at least 8 * (B + M) bytes, 8-byte aligned, holding
+ * the per-row softmax maximum and normaliser between the two kernels. Rows
+ * past M named by q_start are not read. Draws are deterministic: the same
+ * inputs give the same outputs. */
+vs_status verify_sample(int32_t B, int32_t M, int32_t V, const int32_t* q_start, const int32_t* drafts,
+                        const float* p0_logits, const float* logits, const float* q_probs, const float* u,
+                        const float* v, float temperature, int32_t* accept_len, int32_t* token, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ instrumentation */
 
 /* Kernel kinds of one step, for timing. */
@@ -239,9 +271,11 @@ vs_status verify_accept(int32_t B, const int32_t* q_start, const int32_t* drafts
 #define VS_KERNEL_GATEUP 5    /* gate/up product + SwiGLU */
 #define VS_KERNEL_DOWN 6      /* down product + residual */
 #define VS_KERNEL_LMHEAD 7    /* LM head + argmax partials */
+#define VS_KERNEL_SMSTATS 8   /* verify_sample: per-row softmax maximum and normaliser */
+#define VS_KERNEL_SAMPLE 9    /* verify_sample: accept tests and the draw */
 
 /* Measurement aid, not part of the step's function. While armed, every
- * launch of kernel kind `kind` in decode_step is dispatched with
+ * launch of kernel kind `kind` in decode_step or verify_sample is dispatched with
  * hipExtLaunchKernel so that start_events[i] and stop_events[i] take the
  * dispatch's own start and end times, i = 0, 1, ... up to `capacity` launches
  * (later launches are not timed). The events are caller-created hipEvent_t

@@ -115,7 +115,7 @@ def rejection_verify(p0_logits, row_logits, q_rows, drafts, u, v, temperature: f
     Target distributions: p_0 = softmax(p0_logits / T) for the position of d_1 (from the previous
     pass), p_j = softmax(row_logits[j - 1] / T) after d_j. u[j - 1] in [0, 1) decides draft j
     (kept when u < min(1, p/q)); v in [0, 1) drives the one inverse-CDF draw. A draft with
-    q_j(d_j) = 0 is rejected (it could not have been drawn).
+    q_j(d_j) = 0 is rejected (it could not have been drawn), and so is an id outside the vocabulary.
 
     Returns (n_accepted, token, margin): margin is the smallest distance from any decision taken
     to its boundary (|u - a| for the tests made, the draw's bracketing distance for the sample).
@@ -126,7 +126,7 @@ def rejection_verify(p0_logits, row_logits, q_rows, drafts, u, v, temperature: f
     for j in range(1, K + 1):
         d = drafts[j - 1]
         q = q_rows[j - 1]
-        a = rejection_accept_probs([p[j - 1][d]], [q[d]])[0]
+        a = rejection_accept_probs([p[j - 1][d]], [q[d]])[0] if 0 <= d < len(q) else 0.0
         margin = min(margin, abs(u[j - 1] - a))
         if not u[j - 1] < a:
             res = [max(0.0, pi - qi) for pi, qi in zip(p[j - 1], q)]

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["kv_alloc", "kv_free", "kv_share", "kv_append", "decode_step", "verify_accept",
+    for n in ["kv_alloc", "kv_free", "kv_share", "kv_append", "decode_step", "verify_accept", "verify_sample",
               "decode_step_workspace_bytes", "kv_pool_create", "vs_last_error"]:
         assert n in names
     assert set(names) == set(vs.EXPORTS)
@@ -38,6 +38,23 @@ def test_header_declares_the_boundary():
 def test_every_declared_symbol_is_exported(L):
     for n in declared_functions():
         assert hasattr(L, n), n
+
+
+def declared_arity():
+    """Parameter count of every prototype in the header (a lone `void` counts as none)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(([^;{]*?)\)\s*;", text, flags=re.M):
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_signatures_match_the_header(L):
+    arity = declared_arity()
+    assert set(arity) == set(vs.EXPORTS)
+    for n, k in arity.items():
+        assert len(getattr(L, n).argtypes) == k, f"{n}: binding has {len(getattr(L, n).argtypes)} arguments, header {k}"
 
 
 def test_binding_has_the_same_names():

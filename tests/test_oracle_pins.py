@@ -409,3 +409,21 @@ def test_7b_parameter_count_matches_printed_weights():
 def test_oracle_package_exports():
     for name in ["decode_step", "accept_greedy", "rmsnorm", "rope", "attention_standard", "PoolModel"]:
         assert hasattr(oracle, name)
+
+
+def test_rejection_verify_rejects_drafts_that_cannot_have_been_drawn():
+    """A draft the draft model gives zero probability, or an id outside the vocabulary, is never kept
+    (u = 0 keeps any draft with positive acceptance probability), and the replacement comes from
+    norm(max(0, p - q)); where p <= q everywhere there is nothing to correct and the draw is from p itself."""
+    lp = [0.0, math.log(2.0), math.log(5.0)]  # p = (1/8, 2/8, 5/8)
+    q = [0.5, 0.5, 0.0]
+    n, x, _ = rejection_verify(lp, [[0.0] * 3], [q], [2], [0.0], 0.0)
+    assert n == 0 and x == 2, "q(d) = 0: rejected; the residual (0, 0, 5/8) puts everything on token 2"
+    n, _, _ = rejection_verify(lp, [[0.0] * 3], [q], [0], [0.0], 0.0)
+    assert n == 1, "u = 0 keeps a draft with positive acceptance probability"
+    for bad in (-1, 3):
+        n, x, _ = rejection_verify(lp, [[0.0] * 3], [q], [bad], [0.0], 0.0)
+        assert n == 0 and x == 2
+    one_hot = [-math.inf, 0.0, -math.inf]  # p = q = (0, 1, 0); draft 0 has q = 0 and is rejected
+    n, x, _ = rejection_verify(one_hot, [[0.0] * 3], [[0.0, 1.0, 0.0]], [0], [0.0], 0.9)
+    assert n == 0 and x == 1, "p <= q everywhere: the residual is zero, so the draw falls back to p"

@@ -13,6 +13,7 @@
 #include "gemm.h"
 #include "gemv.h"
 #include "misc.h"
+#include "sample.h"
 
 const vs_pool_desc* vs_pool_geometry(const vs_pool* pool);
 
@@ -557,9 +558,38 @@ extern "C" vs_status verify_accept(int32_t B, const int32_t* q_start, const int3
     return vs_ok();
 }
 
+extern "C" vs_status verify_sample(int32_t B, int32_t M, int32_t V, const int32_t* q_start, const int32_t* drafts,
+                                   const float* p0_logits, const float* logits, const float* q_probs, const float* u,
+                                   const float* v, float temperature, int32_t* accept_len, int32_t* token, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+    if (B < 0 || M < 0) return vs_fail(VS_ERR_INVALID, "verify_sample: B < 0 or M < 0");
+    if (B == 0) return vs_ok();
+    if (V < 1) return vs_fail(VS_ERR_INVALID, "verify_sample: V < 1");
+    if (!(temperature > 0.f) || !std::isfinite(temperature))
+        return vs_fail(VS_ERR_INVALID, "verify_sample: temperature must be positive and finite");
+    if (!q_start || !p0_logits || !v || !accept_len || !token || !ws)
+        return vs_fail(VS_ERR_INVALID, "verify_sample: null argument");
+    if (M > 0 && (!drafts || !logits || !q_probs || !u))
+        return vs_fail(VS_ERR_INVALID, "verify_sample: drafts, logits, q_probs and u are required when M > 0");
+    if ((int64_t)B + M > INT32_MAX) return vs_fail(VS_ERR_SHAPE, "verify_sample: B + M too large");
+    const size_t need = sizeof(float2) * (size_t)(B + M);
+    if (ws_bytes < need) return vs_fail(VS_ERR_SHAPE, "verify_sample: workspace needs " + std::to_string(need) + " bytes");
+    if (reinterpret_cast<uintptr_t>(ws) % alignof(float2))
+        return vs_fail(VS_ERR_INVALID, "verify_sample: workspace must be 8-byte aligned");
+    float2* stats = static_cast<float2*>(ws);
+    const float inv_t = 1.f / temperature;
+    launch1(VS_KERNEL_SMSTATS, softmax_stats_kernel, dim3(B + M), dim3(kSampleThreads), 0, stream,
+            StatsArgs{p0_logits, logits, B, V, inv_t, stats});
+    launch1(VS_KERNEL_SAMPLE, sample_pick_kernel, dim3(B), dim3(kSampleThreads), 0, stream,
+            SampleArgs{B, M, V, q_start, drafts, p0_logits, logits, q_probs, u, v, stats, inv_t, accept_len, token});
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return vs_fail(VS_ERR_HIP, std::string("verify_sample launch: ") + hipGetErrorString(e));
+    return vs_ok();
+}
+
 extern "C" vs_status vs_time_kernel(int32_t kind, void* const* start_events, void* const* stop_events,
                                     int32_t capacity) {
-    if (kind < VS_KERNEL_NONE || kind > VS_KERNEL_LMHEAD) return vs_fail(VS_ERR_INVALID, "vs_time_kernel: bad kind");
+    if (kind < VS_KERNEL_NONE || kind > VS_KERNEL_SAMPLE) return vs_fail(VS_ERR_INVALID, "vs_time_kernel: bad kind");
     if (kind != VS_KERNEL_NONE && (capacity < 0 || (capacity > 0 && (!start_events || !stop_events))))
         return vs_fail(VS_ERR_INVALID, "vs_time_kernel: events required");
     g_timer.kind = kind;
