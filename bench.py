@@ -79,12 +79,13 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly instead of replaying a graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with plain device copies of known size (reference dispatches for HBM byte counters)")
-    ap.add_argument("--workload", default="decode-b1", choices=["decode-b1"] + sorted(OTHER_WORKLOADS),
+    ap.add_argument("--workload", default="decode-b1",
+                    choices=["decode-b1"] + sorted(OTHER_WORKLOADS) + sorted(SAMPLE_WORKLOADS),
                     help="decode-b1 is the headline line; the others measure the remaining step shapes")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the step is one GPU's share; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU: the step runs on one GPU's share of a batch, and --gpus {args.gpus} "
+              "(several GPUs) is not supported", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -99,6 +100,8 @@ def main():
         vsbuild.build()
     vs.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload in SAMPLE_WORKLOADS:
+        return sample_workload(args)
     if args.workload != "decode-b1":
         return other_workload(args)
     dev = torch.device("cuda:0")
@@ -381,6 +384,87 @@ def other_workload(args):
         "step_bytes": step_bytes, "step_TBps": round(step_bytes / (ms * 1e-3) / 1e12, 4),
         "step_frac_of_hbm_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "contexts": [min(ctxs), max(ctxs)], "prompt_chunk_rows": chunk,
+    }
+    print(json.dumps(result), flush=True)
+
+
+SAMPLE_WORKLOADS = {
+    # name: (sequences, drafts per sequence); the 7B vocabulary, fp32 logits
+    "sample-b8k5": (8, 5),
+    "sample-b64k1": (64, 1),
+}
+
+
+def sample_workload(args):
+    """verify_sample alone on resident inputs: target logits N(0, 4^2) over 32000 tokens (a peaked
+    distribution), draft distributions softmax(target logits at the same position + N(0, 1)), drafts
+    drawn from them, uniforms u and v. Reports the time per call and each kernel's algorithmic bytes
+    against the HBM peak: the statistics kernel reads every target row once; the pick kernel reads,
+    per sequence, the target row of the draw and, after a rejection, that draft row (plus a few scalars
+    per draft)."""
+    import torch
+
+    import synth
+    import verify_step_amd as vs
+
+    B, K = SAMPLE_WORKLOADS[args.workload]
+    V, M, T = 32000, B * K, 1.0
+    dev = torch.device("cuda")
+    k = synth.key(9001, B, K)
+    p0 = synth.normal(synth.key(k, 1), 0, B * V, 0.0, 4.0).view(B, V).to(dev)
+    logits = synth.normal(synth.key(k, 2), 0, M * V, 0.0, 4.0).view(M, V).to(dev)
+    noise = synth.normal(synth.key(k, 3), 0, M * V, 0.0, 1.0).view(M, V).to(dev)
+    prev = torch.cat([p0.view(B, 1, V), logits.view(B, K, V)[:, :K - 1]], dim=1).reshape(M, V)
+    q = torch.softmax((prev + noise).double(), dim=1).float().contiguous()
+    w = torch.from_numpy(synth.uniform(synth.key(k, 4), 0, M)).to(dev)
+    cdf = torch.cumsum(q.double(), dim=1)
+    drafts = torch.searchsorted(cdf, (w * cdf[:, -1]).view(M, 1), right=True).clamp(max=V - 1).view(M).int()
+    u = torch.from_numpy(synth.uniform(synth.key(k, 5), 0, M)).float().to(dev)
+    v = torch.from_numpy(synth.uniform(synth.key(k, 6), 0, B)).float().to(dev)
+    q_start = torch.arange(0, M + 1, K, dtype=torch.int32, device=dev)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty(B, dtype=torch.int32, device=dev)
+    nb = vs.verify_sample_workspace_bytes(B, M, V)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call():
+        vs.verify_sample(B, M, V, q_start, drafts, p0, logits, q, u, v, T, acc, tok, ws, nb, stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        call()
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    n_kept = acc.cpu().tolist()
+    rejected = sum(1 for n in n_kept if n < K)
+    n_seg = -(-V // 2048)  # 2048-token segments of the statistics kernel, one partial (8 B) each
+    stats_bytes = (B + M) * V * 4 + (B + M) * n_seg * 8
+    pick_bytes = (B + rejected) * V * 4 + (M + B) * n_seg * 8 + M * 4 * 4 + B * (4 + 2 * 4)
+    kern = {}
+    for name, nbytes in (("smstats", stats_bytes), ("sample", pick_bytes)):
+        n = min(args.steps, 64)
+        ev = HipEvents(n)
+        vs.vs_time_kernel(vs.VS_KERNEL[name], ev.start, ev.stop, n)
+        for _ in range(n):
+            call()
+        torch.cuda.synchronize()
+        done = vs.vs_timed_launches()
+        vs.vs_time_kernel(0, None, None, 0)
+        d_us = sum(ev.elapsed_ms(i) for i in range(done)) / done * 1e3
+        ev.close()
+        gbps = nbytes / (d_us * 1e-6) / 1e9
+        kern[name] = {"avg_launch_us": round(d_us, 3), "bytes_per_launch": nbytes, "achieved_GBps": round(gbps, 1),
+                      "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    result = {
+        "workload": args.workload, "sequences": B, "drafts_per_seq": K, "vocab": V, "steps": args.steps,
+        "us_per_call": round(us, 3), "accepted": n_kept, "kernels": kern,
+        "timing": "call: torch events around the timed calls; kernels: dispatch events of each launch",
     }
     print(json.dumps(result), flush=True)
 

@@ -251,10 +251,13 @@ vs_status verify_accept(int32_t B, const int32_t* q_start, const int32_t* drafts
  * produces logits, M_log = M), q_probs [M][V] (each row a distribution),
  * u [M] and v [B] uniforms in [0, 1) that the caller draws. Rows must have a
  * finite maximum; -inf entries are allowed. temperature > 0 and finite.
- * ws: device workspace of at least 8 * (B + M) bytes, 8-byte aligned, holding
- * the per-row softmax maximum and normaliser between the two kernels. Rows
- * past M named by q_start are not read. Draws are deterministic: the same
- * inputs give the same outputs. */
+ * ws: device workspace of at least verify_sample_workspace_bytes(B, M, V)
+ * bytes, 8-byte aligned, holding per-row softmax maxima and normalisers of
+ * 2048-token segments between the two kernels. Rows past M named by q_start
+ * are not read. Draws are deterministic: the same inputs give the same
+ * outputs. 16-byte aligned logit rows (V a multiple of 4) take the vector
+ * path; any V works. */
+vs_status verify_sample_workspace_bytes(int32_t B, int32_t M, int32_t V, size_t* bytes);
 vs_status verify_sample(int32_t B, int32_t M, int32_t V, const int32_t* q_start, const int32_t* drafts,
                         const float* p0_logits, const float* logits, const float* q_probs, const float* u,
                         const float* v, float temperature, int32_t* accept_len, int32_t* token, void* ws,

@@ -99,7 +99,7 @@ class Case:
                       logits=t(self.logits), q=t(self.q), u=t(self.u), v=t(self.v))
         acc = torch.full((self.B,), -7, dtype=torch.int32, device=dev)
         tok = torch.full((self.B,), -7, dtype=torch.int32, device=dev)
-        nb = vs.verify_sample_workspace_bytes(self.B, self.M)
+        nb = vs.verify_sample_workspace_bytes(self.B, self.M, self.V)
         ws = torch.empty(max(nb, 8), dtype=torch.uint8, device=dev)
         g = self.g
         vs.verify_sample(self.B, self.M, self.V, g["q_start"], g["drafts"], g["p0"], g["logits"], g["q"], g["u"],

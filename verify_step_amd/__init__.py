@@ -23,7 +23,7 @@ DTYPE_CODE = {"f32": VS_F32, "f16": VS_F16, "bf16": VS_BF16}
 EXPORTS = [
     "vs_last_error", "kv_page_bytes", "kv_pool_create", "kv_pool_destroy", "kv_alloc", "kv_share", "kv_free",
     "kv_append", "kv_num_free", "kv_refcount", "kv_pool_base", "decode_step_workspace_bytes", "decode_step",
-    "verify_accept", "verify_sample", "vs_time_kernel", "vs_timed_launches",
+    "verify_accept", "verify_sample_workspace_bytes", "verify_sample", "vs_time_kernel", "vs_timed_launches",
 ]
 
 VS_KERNEL = {"none": 0, "qkv": 1, "attn": 2, "merge": 3, "oproj": 4, "gateup": 5, "down": 6, "lmhead": 7,
@@ -107,6 +107,8 @@ def lib() -> ctypes.CDLL:
                                   c_void_p, c_size_t, c_void_p]
         L.verify_accept.restype = c_int32
         L.verify_accept.argtypes = [c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.verify_sample_workspace_bytes.restype = c_int32
+        L.verify_sample_workspace_bytes.argtypes = [c_int32, c_int32, c_int32, POINTER(c_size_t)]
         L.verify_sample.restype = c_int32
         L.verify_sample.argtypes = [c_int32, c_int32, c_int32] + [c_void_p] * 7 + [c_float, c_void_p, c_void_p,
                                                                                      c_void_p, c_size_t, c_void_p]
@@ -211,9 +213,10 @@ def verify_accept(B: int, q_start, drafts, g0, argmax, accept_len, bonus, stream
                                c_void_p(stream)))
 
 
-def verify_sample_workspace_bytes(B: int, M: int) -> int:
-    """Workspace verify_sample needs: one (maximum, normaliser) float pair per target row."""
-    return 8 * (B + M)
+def verify_sample_workspace_bytes(B: int, M: int, V: int) -> int:
+    n = c_size_t()
+    _check(lib().verify_sample_workspace_bytes(B, M, V, ctypes.byref(n)))
+    return int(n.value)
 
 
 def verify_sample(B: int, M: int, V: int, q_start, drafts, p0_logits, logits, q_probs, u, v, temperature: float,

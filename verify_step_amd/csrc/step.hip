@@ -558,6 +558,13 @@ extern "C" vs_status verify_accept(int32_t B, const int32_t* q_start, const int3
     return vs_ok();
 }
 
+extern "C" vs_status verify_sample_workspace_bytes(int32_t B, int32_t M, int32_t V, size_t* bytes) {
+    if (!bytes) return vs_fail(VS_ERR_INVALID, "verify_sample_workspace_bytes: null output");
+    if (B < 0 || M < 0 || V < 1) return vs_fail(VS_ERR_INVALID, "verify_sample_workspace_bytes: bad sizes");
+    *bytes = sizeof(float2) * (size_t)((int64_t)B + M) * (size_t)stats_segments(V);
+    return vs_ok();
+}
+
 extern "C" vs_status verify_sample(int32_t B, int32_t M, int32_t V, const int32_t* q_start, const int32_t* drafts,
                                    const float* p0_logits, const float* logits, const float* q_probs, const float* u,
                                    const float* v, float temperature, int32_t* accept_len, int32_t* token, void* ws,
@@ -572,16 +579,26 @@ extern "C" vs_status verify_sample(int32_t B, int32_t M, int32_t V, const int32_
     if (M > 0 && (!drafts || !logits || !q_probs || !u))
         return vs_fail(VS_ERR_INVALID, "verify_sample: drafts, logits, q_probs and u are required when M > 0");
     if ((int64_t)B + M > INT32_MAX) return vs_fail(VS_ERR_SHAPE, "verify_sample: B + M too large");
-    const size_t need = sizeof(float2) * (size_t)(B + M);
+    const int n_seg = stats_segments(V);
+    if (n_seg > 65535) return vs_fail(VS_ERR_SHAPE, "verify_sample: V too large");
+    const size_t need = sizeof(float2) * (size_t)(B + M) * (size_t)n_seg;
     if (ws_bytes < need) return vs_fail(VS_ERR_SHAPE, "verify_sample: workspace needs " + std::to_string(need) + " bytes");
     if (reinterpret_cast<uintptr_t>(ws) % alignof(float2))
         return vs_fail(VS_ERR_INVALID, "verify_sample: workspace must be 8-byte aligned");
-    float2* stats = static_cast<float2*>(ws);
+    auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+    const bool vec4 = V % 4 == 0 && a16(p0_logits) && a16(logits) && a16(q_probs);
+    float2* part = static_cast<float2*>(ws);
     const float inv_t = 1.f / temperature;
-    launch1(VS_KERNEL_SMSTATS, softmax_stats_kernel, dim3(B + M), dim3(kSampleThreads), 0, stream,
-            StatsArgs{p0_logits, logits, B, V, inv_t, stats});
-    launch1(VS_KERNEL_SAMPLE, sample_pick_kernel, dim3(B), dim3(kSampleThreads), 0, stream,
-            SampleArgs{B, M, V, q_start, drafts, p0_logits, logits, q_probs, u, v, stats, inv_t, accept_len, token});
+    const StatsArgs sa{p0_logits, logits, B, V, n_seg, inv_t, part};
+    const SampleArgs pa{B, M, V, n_seg, q_start, drafts, p0_logits, logits, q_probs, u, v, part, inv_t, accept_len, token};
+    const dim3 sgrid(B + M, n_seg);
+    if (vec4) {
+        launch1(VS_KERNEL_SMSTATS, softmax_stats_kernel<true>, sgrid, dim3(kStatsThreads), 0, stream, sa);
+        launch1(VS_KERNEL_SAMPLE, sample_pick_kernel<true>, dim3(B), dim3(kSampleThreads), 0, stream, pa);
+    } else {
+        launch1(VS_KERNEL_SMSTATS, softmax_stats_kernel<false>, sgrid, dim3(kStatsThreads), 0, stream, sa);
+        launch1(VS_KERNEL_SAMPLE, sample_pick_kernel<false>, dim3(B), dim3(kSampleThreads), 0, stream, pa);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return vs_fail(VS_ERR_HIP, std::string("verify_sample launch: ") + hipGetErrorString(e));
     return vs_ok();
