@@ -306,14 +306,20 @@ OTHER_WORKLOADS = {
     "batch-bf16-b64": ("bf16", 64, 1, "uniform", 0),
     "verify-f16-b8k5": ("f16", 8, 5, "1024", 0),
     "mixed-f16-64+512": ("f16", 64, 1, "prefix", 512),
+    # grouped K/V heads (32 query heads over 8 K/V heads, the widths of Llama 3.1 8B)
+    "gqa8b-f16-b1": ("f16", 1, 1, "2048", 0),
+    "gqa8b-f16-b8k5": ("f16", 8, 5, "1024", 0),
+    "gqa8b-bf16-b64": ("bf16", 64, 1, "uniform", 0),
 }
 
 
 def other_workload(args):
     """One step of another shape, repeated: continuous batching of B sequences with contexts uniform in
     128..4096 (bf16), an 8 x 5 verify pass at context 1024, or 64 decode rows on shared 1024-token
-    prefixes plus a 512-row prompt chunk. Every repetition rewrites the same K/V rows, so the work per
-    step is fixed. K/V contents are arbitrary normals (timing does not depend on them)."""
+    prefixes plus a 512-row prompt chunk; the gqa8b shapes run the grouped-K/V model (32 query heads
+    over 8 K/V heads) at batch 1 (context 2048), 8 x 5 verify and batch 64. Every repetition rewrites
+    the same K/V rows, so the work per step is fixed. K/V contents are arbitrary normals (timing does
+    not depend on them)."""
     import torch
 
     import synth
@@ -322,15 +328,16 @@ def other_workload(args):
     from synth import workloads as W
 
     dt, B, K, ctx_rule, chunk = OTHER_WORKLOADS[args.workload]
-    dims = W.LLAMA7B.with_dtype(dt)
-    wl = 3 if args.workload.startswith("batch") else 4 if args.workload.startswith("verify") else 5
+    gqa = args.workload.startswith("gqa")
+    dims = (W.GQA8B if gqa else W.LLAMA7B).with_dtype(dt)
+    wl = 6 if gqa else 3 if args.workload.startswith("batch") else 4 if args.workload.startswith("verify") else 5
     t0 = time.time()
     model = GpuModel(dims, seed=1000 * wl + 1)
     log(f"weights ready in {time.time() - t0:.1f}s")
     if ctx_rule == "uniform":
         ctxs = [int(c) for c in synth.uniform_int(synth.key(1000 * wl + 4, B), 0, B, 128, 4097)]
-    elif ctx_rule == "1024":
-        ctxs = [1024] * B
+    elif ctx_rule in ("1024", "2048"):
+        ctxs = [int(ctx_rule)] * B
     else:
         ctxs = [1024 + int(s) for s in synth.uniform_int(synth.key(1000 * wl + 4, 1), 0, B, 16, 513)]
     max_blocks = -(-(max(ctxs + [chunk]) + K) // 16)
@@ -383,7 +390,7 @@ def other_workload(args):
         "ms_per_step": round(ms, 4), "rows_per_s": round(M * 1000.0 / ms, 1),
         "step_bytes": step_bytes, "step_TBps": round(step_bytes / (ms * 1e-3) / 1e12, 4),
         "step_frac_of_hbm_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "contexts": [min(ctxs), max(ctxs)], "prompt_chunk_rows": chunk,
+        "contexts": [min(ctxs), max(ctxs)], "prompt_chunk_rows": chunk, "model_shape": dims.name,
     }
     print(json.dumps(result), flush=True)
 

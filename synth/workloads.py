@@ -52,6 +52,9 @@ class ModelDims:
 
 TINY = ModelDims("tiny-1L-d256-4x64-ffn1024-v1000", 256, 4, 4, 64, 1024, 1000, 1, "f32")
 LLAMA7B = ModelDims("7B-MHA-32L-d4096-32x128-ffn11008-v32000", 4096, 32, 32, 128, 11008, 32000, 32, "f16")
+# grouped K/V heads at Llama 3.1 8B's widths: 32 query heads over 8 K/V heads of 128, MLP 14336,
+# vocabulary 128256 (the block otherwise as above: RMSNorm, rotary with theta 10000, SwiGLU)
+GQA8B = ModelDims("8B-GQA-32L-d4096-32q8kv128-ffn14336-v128256", 4096, 32, 8, 128, 14336, 128256, 32, "f16")
 
 # per-layer weight tensors in a fixed order; tags 1..10 name them in the seed scheme
 LAYER_TENSORS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd")

@@ -1,7 +1,9 @@
 """Full-width, one-layer parity under the strict bounds: every row within 1e-2, greedy tokens exact.
 
-The 7B shape's widths (d_model 4096, 32 heads x 128, MLP 11008, vocab 32000)
-with a single layer, in fp16 and bf16: one layer keeps the rounding
+The 7B shape's widths (d_model 4096, 32 heads x 128, MLP 11008, vocab 32000),
+and the grouped-K/V widths of Llama 3.1 8B (32 query heads over 8 K/V heads of
+128, MLP 14336, vocab 128256; [KV Cache] section 03), with a single layer, in
+fp16 and bf16: one layer keeps the rounding
 differences at the storage points from compounding, so the fixed bounds hold
 as stated -- logits and K/V rows within a maximum relative error of 1e-2, and
 every greedy token and accepted length exact except where the oracle's top-1
@@ -30,11 +32,15 @@ def _say(msg):
     print(f"[gpu-case] {msg}", flush=True)
 
 
+MODELS = {"7B": W.LLAMA7B, "8B-GQA": W.GQA8B}
+
+
+@pytest.mark.parametrize("shape", ["7B", "8B-GQA"])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("B,K", [(4, 1), (8, 5)])
-def test_7b_width_one_layer_strict(dtype, B, K):
-    dims = dataclasses.replace(W.LLAMA7B.with_dtype(dtype), n_layers=1, name="7B-width-1L")
-    _say(f"7B width, 1 layer, {dtype}, B={B} K={K}")
+def test_7b_width_one_layer_strict(shape, dtype, B, K):
+    dims = dataclasses.replace(MODELS[shape].with_dtype(dtype), n_layers=1, name=f"{shape}-width-1L")
+    _say(f"{shape} width, 1 layer, {dtype}, B={B} K={K}")
     w_cpu = W.make_weights(dims, SEED_W, gains="random")
     model = GpuModel(dims, weights_cpu=w_cpu)
     ctxs = [int(c) for c in synth.uniform_int(synth.key(SEED_CHURN, B, K), 0, B, 1, 3000)]
@@ -81,6 +87,6 @@ def test_7b_width_one_layer_strict(dtype, B, K):
             if (acc[b], bon[b]) != want:
                 assert first_divergence_is_near_tie(am[rs], ref.argmax[rs], ref.gap[rs], [NEAR_TIE] * K)
     e_abs = max(float((sb.logits[r].cpu().double() - ref.logits[r]).abs().max()) for r in range(M))
-    _say(f"7B width 1 layer {dtype} B={B} K={K}: worst logits {worst:.2e} relative, {e_abs:.2e} absolute, "
+    _say(f"{shape} width 1 layer {dtype} B={B} K={K}: worst logits {worst:.2e} relative, {e_abs:.2e} absolute, "
          f"{n_tie} near-tie rows")
     pool.close()

@@ -147,6 +147,29 @@ def test_tiny_grouped_kv_heads():
     check_case(dims, sb, ref, so, pool, rows, ctxs, k)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("n_kv,rows", [(4, [1, 1, 1]), (2, [1, 1]), (2, [2, 3, 1]), (2, [5, 5]), (1, [1, 1, 1]),
+                                       (1, [2, 1]), (4, [2, 1])])
+def test_tiny_grouped_heads_share_kv_loads(dtype, n_kv, rows):
+    """8 query heads over 4, 2 or 1 K/V heads: a workgroup takes several query heads of one K/V head
+    (up to 8 (row, head) states), for decode, short verify passes and five-row passes."""
+    _say(f"tiny GQA 8/{n_kv} rows={rows} dtype={dtype}")
+    dims = W.ModelDims(f"tiny-gqa-8x{n_kv}", 512, 8, n_kv, 64, 1024, 1000, 1, dtype)
+    ctxs = [37, 0, 70][:len(rows)]
+    sb, ref, so, pool, rows_ = run_case(dims, ctxs, rows, gains="random")
+    check_case(dims, sb, ref, so, pool, rows_, ctxs, rows)
+
+
+def test_tiny_grouped_heads_head_dim_128_long_context():
+    """Head dim 128, 8 query heads over 1 K/V head, 2 layers, a 900-token context (many pages and
+    key splits) and a 3-row pass."""
+    _say("tiny GQA 8/1 head_dim 128, 2 layers, ctx 900")
+    dims = W.ModelDims("tiny-gqa-8x1-dh128", 1024, 8, 1, 128, 1024, 1000, 2, "bf16")
+    ctxs, k = [900, 33], [3, 1]
+    sb, ref, so, pool, rows = run_case(dims, ctxs, k, gains="random", pool_pages=128)
+    check_case(dims, sb, ref, so, pool, rows, ctxs, k)
+
+
 def test_tiny_rows_without_logits_and_long_context():
     """A long sequence spanning many splits, one sequence without logits, head_dim 128."""
     _say("tiny head_dim 128, long context, no-logit sequence")

@@ -22,8 +22,11 @@
 // LDS and the workgroup's state is stored; a merge kernel then combines the
 // splits and writes the attention output in the storage type. All rows of one sequence (up to RMAX
 // at a time) share each K/V load; row i at position ctx + i keeps keys
-// 0..ctx + i (causal across the rows of a pass). Scores are kept in the log2
-// domain (q pre-scaled by log2(e)/sqrt(DH)).
+// 0..ctx + i (causal across the rows of a pass). With grouped K/V heads
+// ([KV Cache] section 03: GQA), a workgroup takes HG query heads of one K/V
+// head, so each K/V load also serves HG heads: the workgroup carries RMAX x HG
+// online-softmax states, state (row i, head j) at index i * HG + j. Scores are
+// kept in the log2 domain (q pre-scaled by log2(e)/sqrt(DH)).
 #pragma once
 
 #include "common.h"
@@ -56,18 +59,19 @@ constexpr int kPartO = 4;  // offset of o in a split's statistics
 // o / l; a row with no visible key (l = 0, only if the block table is cut short) gives 0
 __device__ __forceinline__ float safe_div(float o, float l) { return l > 0.f ? o / l : 0.f; }
 
-template <int DT, int DH, int RMAX, int NW>
+template <int DT, int DH, int RMAX, int NW, int HG>
 __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
     constexpr int DPL = DH / 16;  // dims per lane
+    constexpr int NS = RMAX * HG;  // online-softmax states: (row, head) pairs
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int g = lane >> 4;  // key slot within a group of four
     const int c = lane & 15;  // dim chunk
-    const int s = blockIdx.x, h = blockIdx.y;
+    const int s = blockIdx.x, h0 = blockIdx.y * HG;  // query heads h0 .. h0 + HG - 1 share K/V head hk
     const int b = blockIdx.z % a.B, rgb = blockIdx.z / a.B;
     const int group = a.n_heads / a.n_kv_heads;
-    const int hk = h / group;
+    const int hk = h0 / group;
 
     const int r0 = min(max(a.q_start[b], 0), a.M);
     const int R = min(max(a.q_start[b + 1] - r0, 0), a.M - r0);
@@ -81,7 +85,7 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
     const int QLD = a.n_heads * DH;
     const char* kvb = reinterpret_cast<const char*>(a.kv_base);
 
-    __shared__ float wst[NW][RMAX][DH + 2];  // per-wave (m, l, o) of each row
+    __shared__ float wst[NW][NS][DH + 2];  // per-wave (m, l, o) of each state
 
     // row groups of RMAX rows: this workgroup takes groups rgb, rgb + rg_blocks, ...; a group's last
     // row sits at position ctx + rg + nr - 1, so the group reads only the pages up to there
@@ -89,24 +93,25 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
         const int nr = min(RMAX, R - rg);
         const int n_pages = min((ctx + rg + nr + T - 1) / T, a.max_blocks);
         const int p_end = min(p_begin + a.split_pages, n_pages);
-        float qr[RMAX][DPL];
-        float o[RMAX][DPL];
-        float m[RMAX], l[RMAX];
+        float qr[NS][DPL];
+        float o[NS][DPL];
+        float m[NS], l[NS];
 #pragma unroll
-        for (int i = 0; i < RMAX; ++i) {
-            m[i] = -INFINITY;
-            l[i] = 0.f;
+        for (int st = 0; st < NS; ++st) {
+            const int i = st / HG, j = st % HG;
+            m[st] = -INFINITY;
+            l[st] = 0.f;
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) o[i][e] = 0.f;
+            for (int e = 0; e < DPL; ++e) o[st][e] = 0.f;
             if (i < nr) {
                 load_widen<DT, DPL>(reinterpret_cast<const char*>(a.q) +
-                                        ((long)(r0 + rg + i) * QLD + (long)h * DH + c * DPL) * St<DT>::bytes,
-                                    qr[i]);
+                                        ((long)(r0 + rg + i) * QLD + (long)(h0 + j) * DH + c * DPL) * St<DT>::bytes,
+                                    qr[st]);
 #pragma unroll
-                for (int e = 0; e < DPL; ++e) qr[i][e] *= a.scale_log2;
+                for (int e = 0; e < DPL; ++e) qr[st][e] *= a.scale_log2;
             } else {
 #pragma unroll
-                for (int e = 0; e < DPL; ++e) qr[i][e] = 0.f;
+                for (int e = 0; e < DPL; ++e) qr[st][e] = 0.f;
             }
         }
 
@@ -122,7 +127,8 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
         };
         auto reduce_page = [&](const RawVec<DT, DPL>(&kk)[4], const RawVec<DT, DPL>(&vv)[4], int p) {
 #pragma unroll
-            for (int i = 0; i < RMAX; ++i) {
+            for (int st = 0; st < NS; ++st) {
+                const int i = st / HG;
                 if (i >= nr) break;
                 const int qpos = ctx + rg + i;
                 float sc[4];
@@ -130,7 +136,7 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
                 for (int u = 0; u < 4; ++u) {
                     float d = 0.f;
 #pragma unroll
-                    for (int e = 0; e < DPL; ++e) d += qr[i][e] * raw_at<DT, DPL>(kk[u], e);
+                    for (int e = 0; e < DPL; ++e) d += qr[st][e] * raw_at<DT, DPL>(kk[u], e);
                     d = row16_sum(d);  // the 16 lanes of a key slot hold its 16 dim chunks
                     const int kp = p * T + 4 * u + g;
                     sc[u] = (kp <= qpos) ? d : -INFINITY;
@@ -138,9 +144,9 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
                 float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
                 pm = fmaxf(pm, shfl_xor(pm, 16));
                 pm = fmaxf(pm, shfl_xor(pm, 32));
-                const float mn = fmaxf(m[i], pm);
+                const float mn = fmaxf(m[st], pm);
                 if (mn == -INFINITY) continue;  // no visible key for this row yet
-                const float alpha = exp2f(m[i] - mn);
+                const float alpha = exp2f(m[st] - mn);
                 float ps = 0.f;
                 float pu[4];
 #pragma unroll
@@ -150,15 +156,15 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
                 }
                 ps += shfl_xor(ps, 16);
                 ps += shfl_xor(ps, 32);
-                l[i] = l[i] * alpha + ps;
+                l[st] = l[st] * alpha + ps;
 #pragma unroll
                 for (int e = 0; e < DPL; ++e) {
-                    float acc = o[i][e] * alpha;
+                    float acc = o[st][e] * alpha;
 #pragma unroll
                     for (int u = 0; u < 4; ++u) acc += pu[u] * raw_at<DT, DPL>(vv[u], e);
-                    o[i][e] = acc;
+                    o[st][e] = acc;
                 }
-                m[i] = mn;
+                m[st] = mn;
             }
         };
         const int p0 = p_begin + wave;
@@ -176,26 +182,27 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
         }
         // this wave's state: sum the four key slots' outputs, park it in LDS
 #pragma unroll
-        for (int i = 0; i < RMAX; ++i) {
-            if (i >= nr) break;
+        for (int st = 0; st < NS; ++st) {
+            if (st / HG >= nr) break;
 #pragma unroll
             for (int e = 0; e < DPL; ++e) {
-                o[i][e] += shfl_xor(o[i][e], 16);
-                o[i][e] += shfl_xor(o[i][e], 32);
+                o[st][e] += shfl_xor(o[st][e], 16);
+                o[st][e] += shfl_xor(o[st][e], 32);
             }
             if (lane == 0) {
-                wst[wave][i][0] = m[i];
-                wst[wave][i][1] = l[i];
+                wst[wave][st][0] = m[st];
+                wst[wave][st][1] = l[st];
             }
             if (g == 0) {
 #pragma unroll
-                for (int e = 0; e < DPL; ++e) wst[wave][i][2 + c * DPL + e] = o[i][e];
+                for (int e = 0; e < DPL; ++e) wst[wave][st][2 + c * DPL + e] = o[st][e];
             }
         }
         __syncthreads();
-        // merge the waves in wave order; thread t takes (row, dim) pairs
-        for (int idx = tid; idx < nr * DH; idx += NW * 64) {
-            const int i = idx / DH, d = idx % DH;
+        // merge the waves in wave order; thread t takes (state, dim) pairs
+        for (int idx = tid; idx < nr * HG * DH; idx += NW * 64) {
+            const int i = idx / DH, d = idx % DH;  // i: state index
+            const int row = r0 + rg + i / HG, h = h0 + i % HG;
             float mx = -INFINITY;
 #pragma unroll
             for (int w = 0; w < NW; ++w) mx = fmaxf(mx, wst[w][i][0]);
@@ -211,9 +218,9 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
                 }
             }
             if (a.n_splits == 1) {  // the only split: the state is final
-                store_round<DT>(a.out, (long)(r0 + rg + i) * a.n_heads * DH + (long)h * DH + d, safe_div(os, ls));
+                store_round<DT>(a.out, (long)row * a.n_heads * DH + (long)h * DH + d, safe_div(os, ls));
             } else {
-                float* dst = a.part + (((long)(r0 + rg + i) * a.n_heads + h) * a.n_splits + s) * part_stride(DH);
+                float* dst = a.part + (((long)row * a.n_heads + h) * a.n_splits + s) * part_stride(DH);
                 if (d == 0) {
                     dst[0] = mx;
                     dst[1] = ls;

@@ -72,7 +72,7 @@ constexpr size_t kGemvMaxLds = 96 * 1024;
 constexpr size_t kGemvPhaseLds = 64 * 1024;
 // Waves per attention workgroup (fewer where more rows per sequence need more registers),
 // and the workgroups the key splits aim for (one per CU).
-int attn_waves(int rmax, int dt) { return rmax == 1 || (rmax == 2 && dt != VS_F32) ? 8 : 4; }
+int attn_waves(int states, int dt) { return states == 1 || (states == 2 && dt != VS_F32) ? 8 : 4; }
 constexpr long kAttnTargetWaves = 2048;  // eight-wave workgroups: 256 (one per CU)
 constexpr long kAttnTargetWgsFew = 512;  // four-wave workgroups (several rows per sequence): two per CU
 // Output units per workgroup of the output GEMV when it merges the key splits itself.
@@ -80,7 +80,7 @@ constexpr int kGemvMergeUnits = 16;
 
 struct Plan {
     int B, M, M_log, D, H, Hkv, Dh, F, V, L, dt, esz;
-    int n_splits, split_pages, rmax, attn_waves, rg_blocks;
+    int n_splits, split_pages, rmax, attn_hg, attn_waves, rg_blocks;
     bool gemv;      // the row-streaming path serves every product of the step
     bool merge_in_o; // the output product's prologue merges the key splits (no merge kernel)
     int n_lm_parts; // argmax partials per logit row
@@ -132,9 +132,26 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     // key splits: about one workgroup per CU over B x heads, at least two pages per wave of a split
     // rows per attention row group (5: a verify pass of five drafts fits one group exactly)
     p->rmax = d->max_rows <= 1 ? 1 : d->max_rows <= 2 ? 2 : d->max_rows <= 4 ? 4 : d->max_rows <= 5 ? 5 : 8;
-    p->attn_waves = attn_waves(p->rmax, m->dtype);
+    p->attn_hg = 1;
+    {
+        // grouped K/V heads: a workgroup may take HG query heads of one K/V head (rows x HG <= 8 states);
+        // pick the (rows, HG) that reads each K/V page the fewest times, the plain row groups on a tie
+        const int group = m->n_heads / m->n_kv_heads;
+        auto reads = [&](int r, int hg) { return (long)((d->max_rows + r - 1) / r) * (group / hg); };
+        long best = reads(p->rmax, 1);
+        for (int hg : {2, 4, 8}) {
+            if (group % hg) continue;
+            for (int r : {1, 2, 4}) {
+                if (r * hg > 8 || reads(r, hg) >= best) continue;
+                best = reads(r, hg);
+                p->rmax = r;
+                p->attn_hg = hg;
+            }
+        }
+    }
+    p->attn_waves = attn_waves(p->rmax * p->attn_hg, m->dtype);
     const int max_pages = (d->max_ctx + kPageTokens - 1) / kPageTokens;
-    const long pairs = (long)d->B * m->n_heads;
+    const long pairs = (long)d->B * (m->n_heads / p->attn_hg);
     // row groups of a sequence go to separate workgroups (a prompt chunk's groups run in parallel)
     const int rg_needed = (d->max_rows + p->rmax - 1) / p->rmax;
     p->rg_blocks = (int)std::max<long>(1, std::min<long>(rg_needed, 65535L / d->B));
@@ -229,24 +246,29 @@ void launch_gemv(int kind, GemvArgs g, hipStream_t s, int units_per_wg = 0) {
 // The split pass, then the merge kernel unless the splits are merged elsewhere (one split
 // needs none; the output GEMV can merge them in its prologue).
 template <int DT, int DH>
-void launch_attention(const AttnArgs& a, int B, int M, int rmax, bool merge_kernel, hipStream_t s) {
-    dim3 grid(a.n_splits, a.n_heads, B * a.rg_blocks);
-    const int nw = attn_waves(rmax, DT);
+void launch_attention(const AttnArgs& a, int B, int M, int rmax, int hg, bool merge_kernel, hipStream_t s) {
+    dim3 grid(a.n_splits, a.n_heads / hg, B * a.rg_blocks);
+    const int nw = attn_waves(rmax * hg, DT);
     dim3 block(nw * 64);
-    switch (rmax) {
-        case 1: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 1, 8>, grid, block, 0, s, a); break;
-        case 2:
-            if constexpr (DT != F32) {
-                if (nw == 8) {
-                    launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 2, 8>, grid, block, 0, s, a);
-                    break;
-                }
-            }
-            launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 2, 4>, grid, block, 0, s, a);
+    auto go = [&](auto kern) { launch1(VS_KERNEL_ATTN, kern, grid, block, 0, s, a); };
+    switch (hg * 16 + rmax) {
+        case 16 + 1: go(attn_split_kernel<DT, DH, 1, 8, 1>); break;
+        case 16 + 2:
+            if (nw == 8) go(attn_split_kernel<DT, DH, 2, DT == F32 ? 4 : 8, 1>);
+            else go(attn_split_kernel<DT, DH, 2, 4, 1>);
             break;
-        case 4: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 4, 4>, grid, block, 0, s, a); break;
-        case 5: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 5, 4>, grid, block, 0, s, a); break;
-        default: launch1(VS_KERNEL_ATTN, attn_split_kernel<DT, DH, 8, 4>, grid, block, 0, s, a); break;
+        case 16 + 4: go(attn_split_kernel<DT, DH, 4, 4, 1>); break;
+        case 16 + 5: go(attn_split_kernel<DT, DH, 5, 4, 1>); break;
+        case 32 + 1:
+            if (nw == 8) go(attn_split_kernel<DT, DH, 1, DT == F32 ? 4 : 8, 2>);
+            else go(attn_split_kernel<DT, DH, 1, 4, 2>);
+            break;
+        case 32 + 2: go(attn_split_kernel<DT, DH, 2, 4, 2>); break;
+        case 32 + 4: go(attn_split_kernel<DT, DH, 4, 4, 2>); break;
+        case 64 + 1: go(attn_split_kernel<DT, DH, 1, 4, 4>); break;
+        case 64 + 2: go(attn_split_kernel<DT, DH, 2, 4, 4>); break;
+        case 128 + 1: go(attn_split_kernel<DT, DH, 1, 4, 8>); break;
+        default: go(attn_split_kernel<DT, DH, 8, 4, 1>); break;
     }
     if (merge_kernel && a.n_splits > 1)
         launch1(VS_KERNEL_MERGE, attn_merge_kernel<DT, DH>, dim3(M, a.n_heads), dim3(DH), 0, s, a);
@@ -371,8 +393,8 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
         }
 
         a.layer = l;
-        if (p.Dh == 128) launch_attention<DT, 128>(a, p.B, p.M, p.rmax, !p.merge_in_o, s);
-        else launch_attention<DT, 64>(a, p.B, p.M, p.rmax, !p.merge_in_o, s);
+        if (p.Dh == 128) launch_attention<DT, 128>(a, p.B, p.M, p.rmax, p.attn_hg, !p.merge_in_o, s);
+        else launch_attention<DT, 64>(a, p.B, p.M, p.rmax, p.attn_hg, !p.merge_in_o, s);
 
         // x += W_o attn
         if (p.gemv) {
