@@ -151,8 +151,9 @@ def test_tiny_grouped_kv_heads():
 @pytest.mark.parametrize("n_kv,rows", [(4, [1, 1, 1]), (2, [1, 1]), (2, [2, 3, 1]), (2, [5, 5]), (1, [1, 1, 1]),
                                        (1, [2, 1]), (4, [2, 1])])
 def test_tiny_grouped_heads_share_kv_loads(dtype, n_kv, rows):
-    """8 query heads over 4, 2 or 1 K/V heads: a workgroup takes several query heads of one K/V head
-    (up to 8 (row, head) states), for decode, short verify passes and five-row passes."""
+    """8 query heads over 4, 2 or 1 K/V heads: a workgroup takes 2 or 4 query heads of one K/V head
+    (up to 4 (row, head) states) for decode and short verify passes; five-row passes keep plain row
+    groups."""
     _say(f"tiny GQA 8/{n_kv} rows={rows} dtype={dtype}")
     dims = W.ModelDims(f"tiny-gqa-8x{n_kv}", 512, 8, n_kv, 64, 1024, 1000, 1, dtype)
     ctxs = [37, 0, 70][:len(rows)]

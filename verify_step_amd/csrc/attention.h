@@ -16,9 +16,12 @@
 // row groups run in parallel. Lane l owns dims [(l%16)*DH/16, +DH/16) of key slot
 // (l/16) within each group of four keys, so one page of 16 keys is four loads
 // per lane for K and four for V, and the 16 lanes that share a key finish its
-// dot product with DPP row sums. Every K/V byte is used by exactly one wave, so
+// dot product with DPP row sums. Each group of 16 lanes (one key slot) keeps its
+// own online-softmax state over the keys it sees; the four are merged once at the
+// end of the split. Every K/V byte is used by exactly one wave, so
 // it goes from HBM straight to registers; each wave keeps a ring of three
-// pages, two in flight while one is reduced. The four waves' states are merged through
+// pages, two in flight while one is reduced (two pages, one in flight, for
+// workgroups with four or more states, to leave registers for them). The four waves' states are merged through
 // LDS and the workgroup's state is stored; a merge kernel then combines the
 // splits and writes the attention output in the storage type. All rows of one sequence (up to RMAX
 // at a time) share each K/V load; row i at position ctx + i keeps keys
@@ -115,7 +118,7 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
             }
         }
 
-        // a ring of three pages per wave: two are in flight while one is reduced
+        // a ring of pages per wave: while one is reduced, the next ones are in flight
         RawVec<DT, DPL> ka[4], va[4], kb[4], vb[4], kc[4], vc[4];
         auto load_page = [&](RawVec<DT, DPL>(&kk)[4], RawVec<DT, DPL>(&vv)[4], int p) {
             const long pb = (long)min(max(bt[p], 0), a.num_pages - 1) * a.page_elems;
@@ -141,11 +144,11 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
                     const int kp = p * T + 4 * u + g;
                     sc[u] = (kp <= qpos) ? d : -INFINITY;
                 }
-                float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-                pm = fmaxf(pm, shfl_xor(pm, 16));
-                pm = fmaxf(pm, shfl_xor(pm, 32));
+                // each key slot g keeps its own (m, l, o) over its keys; the four are merged once
+                // per split, so a page needs no cross-lane exchange beyond the dot products
+                const float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
                 const float mn = fmaxf(m[st], pm);
-                if (mn == -INFINITY) continue;  // no visible key for this row yet
+                if (mn == -INFINITY) continue;  // no visible key for this slot yet
                 const float alpha = exp2f(m[st] - mn);
                 float ps = 0.f;
                 float pu[4];
@@ -154,8 +157,6 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
                     pu[u] = exp2f(sc[u] - mn);
                     ps += pu[u];
                 }
-                ps += shfl_xor(ps, 16);
-                ps += shfl_xor(ps, 32);
                 l[st] = l[st] * alpha + ps;
 #pragma unroll
                 for (int e = 0; e < DPL; ++e) {
@@ -168,30 +169,49 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
             }
         };
         const int p0 = p_begin + wave;
-        if (p0 < p_end) load_page(ka, va, p0);
-        if (p0 + NW < p_end) load_page(kb, vb, p0 + NW);
-        for (int p = p0; p < p_end; p += 3 * NW) {
-            if (p + 2 * NW < p_end) load_page(kc, vc, p + 2 * NW);
-            reduce_page(ka, va, p);
-            if (p + NW >= p_end) break;
-            if (p + 3 * NW < p_end) load_page(ka, va, p + 3 * NW);
-            reduce_page(kb, vb, p + NW);
-            if (p + 2 * NW >= p_end) break;
-            if (p + 4 * NW < p_end) load_page(kb, vb, p + 4 * NW);
-            reduce_page(kc, vc, p + 2 * NW);
+        if constexpr (NS >= 4) {  // many states: a ring of two pages leaves registers for them
+            if (p0 < p_end) load_page(ka, va, p0);
+            for (int p = p0; p < p_end; p += 2 * NW) {
+                if (p + NW < p_end) load_page(kb, vb, p + NW);
+                reduce_page(ka, va, p);
+                if (p + NW >= p_end) break;
+                if (p + 2 * NW < p_end) load_page(ka, va, p + 2 * NW);
+                reduce_page(kb, vb, p + NW);
+            }
+        } else {
+            if (p0 < p_end) load_page(ka, va, p0);
+            if (p0 + NW < p_end) load_page(kb, vb, p0 + NW);
+            for (int p = p0; p < p_end; p += 3 * NW) {
+                if (p + 2 * NW < p_end) load_page(kc, vc, p + 2 * NW);
+                reduce_page(ka, va, p);
+                if (p + NW >= p_end) break;
+                if (p + 3 * NW < p_end) load_page(ka, va, p + 3 * NW);
+                reduce_page(kb, vb, p + NW);
+                if (p + 2 * NW >= p_end) break;
+                if (p + 4 * NW < p_end) load_page(kb, vb, p + 4 * NW);
+                reduce_page(kc, vc, p + 2 * NW);
+            }
         }
-        // this wave's state: sum the four key slots' outputs, park it in LDS
+        // this wave's state: merge the four key slots' states (rescaled to their common maximum),
+        // park it in LDS
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
             if (st / HG >= nr) break;
+            float mx = fmaxf(m[st], shfl_xor(m[st], 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            const float f = m[st] == -INFINITY ? 0.f : exp2f(m[st] - mx);
+            float ls = l[st] * f;
+            ls += shfl_xor(ls, 16);
+            ls += shfl_xor(ls, 32);
 #pragma unroll
             for (int e = 0; e < DPL; ++e) {
+                o[st][e] *= f;
                 o[st][e] += shfl_xor(o[st][e], 16);
                 o[st][e] += shfl_xor(o[st][e], 32);
             }
             if (lane == 0) {
-                wst[wave][st][0] = m[st];
-                wst[wave][st][1] = l[st];
+                wst[wave][st][0] = mx;
+                wst[wave][st][1] = ls;
             }
             if (g == 0) {
 #pragma unroll

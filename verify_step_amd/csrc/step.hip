@@ -134,15 +134,16 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->rmax = d->max_rows <= 1 ? 1 : d->max_rows <= 2 ? 2 : d->max_rows <= 4 ? 4 : d->max_rows <= 5 ? 5 : 8;
     p->attn_hg = 1;
     {
-        // grouped K/V heads: a workgroup may take HG query heads of one K/V head (rows x HG <= 8 states);
-        // pick the (rows, HG) that reads each K/V page the fewest times, the plain row groups on a tie
+        // grouped K/V heads: a workgroup may take HG query heads of one K/V head, up to 4 (row, head)
+        // states (more leave one wave per SIMD, which measured slower than plain row groups); pick
+        // the (rows, HG) that reads each K/V page the fewest times, the plain row groups on a tie
         const int group = m->n_heads / m->n_kv_heads;
         auto reads = [&](int r, int hg) { return (long)((d->max_rows + r - 1) / r) * (group / hg); };
         long best = reads(p->rmax, 1);
-        for (int hg : {2, 4, 8}) {
+        for (int hg : {2, 4}) {
             if (group % hg) continue;
-            for (int r : {1, 2, 4}) {
-                if (r * hg > 8 || reads(r, hg) >= best) continue;
+            for (int r : {1, 2}) {
+                if (r * hg > 4 || reads(r, hg) >= best) continue;
                 best = reads(r, hg);
                 p->rmax = r;
                 p->attn_hg = hg;
@@ -151,10 +152,10 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     }
     p->attn_waves = attn_waves(p->rmax * p->attn_hg, m->dtype);
     const int max_pages = (d->max_ctx + kPageTokens - 1) / kPageTokens;
-    const long pairs = (long)d->B * (m->n_heads / p->attn_hg);
     // row groups of a sequence go to separate workgroups (a prompt chunk's groups run in parallel)
     const int rg_needed = (d->max_rows + p->rmax - 1) / p->rmax;
     p->rg_blocks = (int)std::max<long>(1, std::min<long>(rg_needed, 65535L / d->B));
+    const long pairs = (long)d->B * (m->n_heads / p->attn_hg) * p->rg_blocks;  // workgroups per split
     const long wgs_target = p->attn_waves == 8 ? kAttnTargetWaves / 8 : kAttnTargetWgsFew;
     const int ns = (int)std::min<long>(std::max(1, max_pages / (2 * p->attn_waves)),
                                        std::max<long>(1, (wgs_target + pairs - 1) / pairs));
@@ -264,10 +265,7 @@ void launch_attention(const AttnArgs& a, int B, int M, int rmax, int hg, bool me
             else go(attn_split_kernel<DT, DH, 1, 4, 2>);
             break;
         case 32 + 2: go(attn_split_kernel<DT, DH, 2, 4, 2>); break;
-        case 32 + 4: go(attn_split_kernel<DT, DH, 4, 4, 2>); break;
         case 64 + 1: go(attn_split_kernel<DT, DH, 1, 4, 4>); break;
-        case 64 + 2: go(attn_split_kernel<DT, DH, 2, 4, 4>); break;
-        case 128 + 1: go(attn_split_kernel<DT, DH, 1, 4, 8>); break;
         default: go(attn_split_kernel<DT, DH, 8, 4, 1>); break;
     }
     if (merge_kernel && a.n_splits > 1)
