@@ -2,7 +2,7 @@
 
 The 7B shape's widths (d_model 4096, 32 heads x 128, MLP 11008, vocab 32000),
 and the grouped-K/V widths of Llama 3.1 8B (32 query heads over 8 K/V heads of
-128, MLP 14336, vocab 128256; [KV Cache] section 03), with a single layer, in
+128, MLP 14336, vocab 128256; [KV Cache] sections 03 and 04), with a single layer, in
 fp16 and bf16: one layer keeps the rounding
 differences at the storage points from compounding, so the fixed bounds hold
 as stated -- logits and K/V rows within a maximum relative error of 1e-2, and

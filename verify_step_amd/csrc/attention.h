@@ -26,7 +26,7 @@
 // splits and writes the attention output in the storage type. All rows of one sequence (up to RMAX
 // at a time) share each K/V load; row i at position ctx + i keeps keys
 // 0..ctx + i (causal across the rows of a pass). With grouped K/V heads
-// ([KV Cache] section 03: GQA), a workgroup takes HG query heads of one K/V
+// ([KV Cache] section 04: GQA), a workgroup takes HG query heads of one K/V
 // head, so each K/V load also serves HG heads: the workgroup carries RMAX x HG
 // online-softmax states, state (row i, head j) at index i * HG + j. Scores are
 // kept in the log2 domain (q pre-scaled by log2(e)/sqrt(DH)).
