@@ -41,6 +41,31 @@ def round_to(x: torch.Tensor, dt: str) -> torch.Tensor:
     return x.to(_STORAGE[dt]).to(F64)
 
 
+# OCP 8-bit floats: (exponent bits, mantissa bits, exponent bias, largest finite magnitude)
+FP8_FORMATS = {"e4m3": (4, 3, 7, 448.0), "e5m2": (5, 2, 15, 57344.0)}
+
+
+def round_fp8(x: torch.Tensor, fmt: str) -> torch.Tensor:
+    """Round float64 values to an 8-bit float and return them as float64.
+
+    [KV Cache] section 03 (end): a K/V cache may store K and V in FP8, one byte
+    per value, in the e4m3 or e5m2 format. Written from the formats'
+    definition: a value in the binade [2^e, 2^(e+1)) is a multiple of
+    2^(e - mantissa bits); below the smallest normal binade (e < 1 - bias) the
+    spacing stays at the subnormal step 2^(1 - bias - mantissa bits). Rounding
+    is to the nearest multiple, ties to even; magnitudes beyond the largest
+    finite value saturate to it (the reading taken here: a cache entry stays
+    finite).
+    """
+    _, mb, bias, vmax = FP8_FORMATS[fmt]
+    a = x.to(F64).abs().clamp(max=vmax)
+    _, ex = torch.frexp(a)  # a = f * 2^ex with f in [0.5, 1), so a lies in [2^(ex-1), 2^ex)
+    e = (ex.to(F64) - 1).clamp(min=1 - bias)
+    step = torch.exp2(e - mb)
+    r = (torch.round(a / step) * step).clamp(max=vmax)  # torch.round: half to even
+    return torch.copysign(r, x.to(F64))
+
+
 def linear(x: torch.Tensor, w: torch.Tensor, cdt: torch.dtype = F64) -> torch.Tensor:
     """y = x W^T for a weight stored row-major as [out][in] (a float64 product by default).
 

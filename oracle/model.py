@@ -29,7 +29,8 @@ Storage points (the only places values are rounded):
   * the inputs of every weight product (normalised activations, the attention
     output, the gated MLP activation) are stored in the model's dtype;
   * q, and the k and v written to the cache, are stored in the model's dtype
-    after rotation;
+    after rotation; with an 8-bit cache ([KV Cache] section 03: e4m3 or e5m2)
+    k and v are rounded once, from the rotated value, to that format;
   * logits are fp32 and the argmax is taken on the fp32 values.
 Everything between two storage points is float64.
 
@@ -47,7 +48,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-from .layers import F64, argmax_lowest, attention_standard, linear, rmsnorm, rope, round_to, swiglu
+from .layers import F64, argmax_lowest, attention_standard, linear, rmsnorm, rope, round_fp8, round_to, swiglu
 
 
 @dataclass
@@ -80,6 +81,7 @@ def decode_step(dims, weights: dict, seqs: list[SeqState], layer_hook=None, comp
     """Run one step for all rows of all sequences; updates each seq.kv in place."""
     cdt = {"f64": F64, "f32": torch.float32}[compute]
     dt = dims.dtype
+    kv8 = getattr(dims, "kv_dtype", None)  # "e4m3" / "e5m2" for an 8-bit K/V cache, else None
     H, Hkv, Dh = dims.n_heads, dims.n_kv_heads, dims.head_dim
     group = H // Hkv  # query heads per KV head (1 for MHA)
     rows = [(b, i) for b, s in enumerate(seqs) for i in range(len(s.tokens))]
@@ -103,8 +105,12 @@ def decode_step(dims, weights: dict, seqs: list[SeqState], layer_hook=None, comp
         k = linear(xn, lw["wk"], cdt).reshape(M, Hkv, Dh)
         v = linear(xn, lw["wv"], cdt).reshape(M, Hkv, Dh)
         q = round_to(rope(q, pos, dims.rope_theta, cdt), dt)
-        k = round_to(rope(k, pos, dims.rope_theta, cdt), dt)
-        v = round_to(v, dt)
+        if kv8:  # an 8-bit cache: k and v go once from the rotated value to the cache's format
+            k = round_fp8(rope(k, pos, dims.rope_theta, cdt), kv8)
+            v = round_fp8(v, kv8)
+        else:
+            k = round_to(rope(k, pos, dims.rope_theta, cdt), dt)
+            v = round_to(v, dt)
         for r, (b, i) in enumerate(rows):  # append this step's K/V rows to each cache
             p = int(pos[r])
             seqs[b].kv[l, 0, p] = k[r].to(seqs[b].kv.dtype)

@@ -19,6 +19,7 @@ import synth
 STREAM_WEIGHTS, STREAM_KV, STREAM_TOKENS, STREAM_CHURN, STREAM_DRAFTS, STREAM_PAGES = 1, 2, 3, 4, 5, 6
 
 _TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+_KV_TDT = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}  # OCP 8-bit floats
 
 
 @dataclass(frozen=True)
@@ -33,10 +34,11 @@ class ModelDims:
     ffn: int
     vocab: int
     n_layers: int
-    dtype: str  # storage type of weights and KV cache: "f32", "f16" or "bf16"
+    dtype: str  # storage type of weights (and of the KV cache unless kv_dtype says otherwise)
     rope_theta: float = 10000.0
     eps: float = 1e-5
     page_tokens: int = 16
+    kv_dtype: str | None = None  # KV cache storage: None (= dtype) or an 8-bit float, "e4m3" / "e5m2"
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -46,8 +48,23 @@ class ModelDims:
     def elem_bytes(self) -> int:
         return 4 if self.dtype == "f32" else 2
 
+    @property
+    def kv_type(self) -> str:
+        return self.kv_dtype or self.dtype
+
+    @property
+    def kv_torch_dtype(self) -> torch.dtype:
+        return _KV_TDT.get(self.kv_type) or _TDT[self.kv_type]
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        return 1 if self.kv_type in _KV_TDT else self.elem_bytes
+
     def with_dtype(self, dtype: str) -> "ModelDims":
         return dataclasses.replace(self, dtype=dtype)
+
+    def with_kv(self, kv_dtype: str | None) -> "ModelDims":
+        return dataclasses.replace(self, kv_dtype=kv_dtype, name=f"{self.name}-kv{kv_dtype}" if kv_dtype else self.name)
 
 
 TINY = ModelDims("tiny-1L-d256-4x64-ffn1024-v1000", 256, 4, 4, 64, 1024, 1000, 1, "f32")
@@ -110,21 +127,24 @@ def make_weights(dims: ModelDims, seed: int, gains: str = "one") -> dict:
 def kv_block(dims: ModelDims, seed: int, content: int, p0: int, p1: int, std: float = 1.0) -> torch.Tensor:
     """Synthetic cached K/V for positions [p0, p1) of one content stream.
 
-    Returns [n_layers][2][p1 - p0][n_kv_heads][head_dim] in the storage dtype,
-    values N(0, std) read as post-rotary K and V. Element (content, layer, k/v,
-    pos, head, dim) is a pure function of the seed, so two sequences that share
-    an exact prefix use the same content id and get the same bits.
+    Returns [n_layers][2][p1 - p0][n_kv_heads][head_dim] in the KV cache's storage
+    dtype, values N(0, std) read as post-rotary K and V. Element (content, layer,
+    k/v, pos, head, dim) is a pure function of the seed, so two sequences that
+    share an exact prefix use the same content id and get the same bits. An
+    8-bit cache takes the fp32 draws through the library's float8 cast (values
+    N(0, 1) stay far inside both formats' range).
     """
     L, H, Dh = dims.n_layers, dims.n_kv_heads, dims.head_dim
     n = p1 - p0
-    out = torch.empty((L, 2, n, H, Dh), dtype=dims.torch_dtype)
+    fp8 = dims.kv_elem_bytes == 1
+    out = torch.empty((L, 2, n, H, Dh), dtype=torch.float32 if fp8 else dims.torch_dtype)
     if n <= 0:
-        return out
+        return out.to(dims.kv_torch_dtype)
     for l in range(L):
         for t in range(2):
             k = synth.key(seed, STREAM_KV, content, l, t)
             synth.normal_into(out[l, t].reshape(-1), k, p0 * H * Dh, 0.0, std)
-    return out
+    return out.to(dims.kv_torch_dtype) if fp8 else out
 
 
 def token_ids(seed: int, tag: int, n: int, vocab: int) -> list[int]:

@@ -21,7 +21,7 @@ SEED = 1001  # tiny workload, weight stream
 
 def seq(dims, content, ctx, tokens, cap=None, want=True, kv_seed=1002):
     cap = cap or ctx + len(tokens)
-    kv = torch.zeros(dims.n_layers, 2, cap, dims.n_kv_heads, dims.head_dim, dtype=dims.torch_dtype)
+    kv = torch.zeros(dims.n_layers, 2, cap, dims.n_kv_heads, dims.head_dim, dtype=dims.kv_torch_dtype)
     kv[:, :, :ctx] = W.kv_block(dims, kv_seed, content, 0, ctx)
     return SeqState(kv, ctx, list(tokens), want)
 
@@ -259,3 +259,30 @@ def test_fp32_realisation_agrees_to_rounding(model):
         x, y = s64.kv.double(), s32.kv.double()
         d = (x - y).abs().amax(dim=(3, 4))
         assert bool((d <= step * x.abs().amax(dim=(3, 4))).all())
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_cache_holds_the_16_bit_cache_rounded_to_a_neighbour(fmt):
+    """[KV Cache] section 03: an 8-bit cache stores the same K and V in one byte each. Every K/V
+    element the step writes is one of the two values of the format (decoded from its bit fields)
+    that bracket the fp16 cache's element for the same step; the logits move, but only by the
+    quantisation."""
+    from test_oracle_pins import _fp8_table
+
+    base = W.TINY.with_dtype("f16")
+    d8 = base.with_kv(fmt)
+    w = W.make_weights(base, SEED, gains="random")
+    toks = W.token_ids(1003, 9, 3, base.vocab)
+    s16, s8 = seq(base, 3, 20, toks), seq(d8, 3, 20, toks)
+    r16, r8 = decode_step(base, w, [s16]), decode_step(d8, w, [s8])
+    new16, new8 = s16.kv[:, :, 20:23].double().flatten(), s8.kv[:, :, 20:23].double().flatten()
+    vals = torch.tensor(sorted(v for v, _ in _fp8_table(fmt)), dtype=torch.float64)
+    i = torch.searchsorted(vals, new16)
+    lo = vals[(i - 1).clamp(min=0)]
+    hi = vals[i.clamp(max=len(vals) - 1)]
+    exact = vals[i.clamp(max=len(vals) - 1)] == new16
+    ok = exact & (new8 == new16) | (new8 == lo) | (new8 == hi)
+    assert bool(ok.all()), f"{int((~ok).sum())} K/V elements are not a neighbour of the fp16 value"
+    assert not torch.equal(new8, new16), "the 8-bit cache rounds"
+    for a, b in zip(r8.logits, r16.logits):
+        assert 0 < rel(a, b) < 0.2

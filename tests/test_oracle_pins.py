@@ -427,3 +427,59 @@ def test_rejection_verify_rejects_drafts_that_cannot_have_been_drawn():
     one_hot = [-math.inf, 0.0, -math.inf]  # p = q = (0, 1, 0); draft 0 has q = 0 and is rejected
     n, x, _ = rejection_verify(one_hot, [[0.0] * 3], [[0.0, 1.0, 0.0]], [0], [0.0], 0.9)
     assert n == 0 and x == 1, "p <= q everywhere: the residual is zero, so the draw falls back to p"
+
+
+def _fp8_table(fmt):
+    """Every finite value of an OCP 8-bit float, decoded from its bit fields, with its code's mantissa."""
+    eb, mb, bias = {"e4m3": (4, 3, 7), "e5m2": (5, 2, 15)}[fmt]
+    vals = []
+    for code in range(256):
+        sgn, E, M = code >> 7, (code >> mb) & ((1 << eb) - 1), code & ((1 << mb) - 1)
+        if fmt == "e4m3" and E == 15 and M == 7:
+            continue  # NaN
+        if fmt == "e5m2" and E == 31:
+            continue  # infinities and NaNs
+        mag = (M / 2 ** mb) * 2.0 ** (1 - bias) if E == 0 else (1 + M / 2 ** mb) * 2.0 ** (E - bias)
+        vals.append((-mag if sgn else mag, M))
+    return vals
+
+
+@pytest.mark.parametrize("fmt,n_finite,vmax", [("e4m3", 254, 448.0), ("e5m2", 248, 57344.0)])
+def test_round_fp8_is_nearest_even_over_the_format(fmt, n_finite, vmax):
+    """Brute force over the decoded format: every midpoint between neighbours (a tie: the even
+    mantissa wins), points just either side of it, random values across the whole range including
+    subnormals, and saturation beyond the largest finite value."""
+    from oracle.layers import round_fp8
+
+    table = _fp8_table(fmt)
+    assert len(table) == n_finite and max(v for v, _ in table) == vmax
+    pos = sorted({(v, m) for v, m in table if v >= 0})
+    xs, want = [], []
+    for (a, ma), (b, mb_) in zip(pos, pos[1:]):
+        mid = (a + b) / 2
+        xs += [mid, math.nextafter(mid, 0), math.nextafter(mid, math.inf)]
+        want += [a if ma % 2 == 0 else b, a, b]
+    rng = np.random.default_rng(8)
+    rand = np.exp(rng.uniform(math.log(2.0 ** -20), math.log(vmax), 4000)).astype(np.float32).astype(np.float64)
+    vals = np.array([v for v, _ in pos])
+    mant = dict(pos)
+    for x in rand:
+        i = int(np.searchsorted(vals, x))
+        lo, hi = vals[max(i - 1, 0)], vals[min(i, len(vals) - 1)]
+        xs.append(float(x))
+        if x - lo != hi - x:
+            want.append(lo if x - lo < hi - x else hi)
+        else:
+            want.append(lo if mant[float(lo)] % 2 == 0 else hi)
+    xs += [vmax * 1.01, vmax * 1e3]
+    want += [vmax, vmax]
+    x = torch.tensor(xs, dtype=torch.float64)
+    got = round_fp8(x, fmt)
+    assert torch.equal(got, torch.tensor(want, dtype=torch.float64))
+    assert torch.equal(round_fp8(-x, fmt), -got), "rounding is symmetric in the sign"
+    # inside the range the library's float8 cast (also nearest-even) agrees on fp32 inputs (it
+    # converts a double through fp32 first, so points a hair off a midpoint are left out)
+    lib_dt = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[fmt]
+    inside = x[(x <= vmax) & (x.to(torch.float32).to(torch.float64) == x)]
+    assert len(inside) > 3000
+    assert torch.equal(round_fp8(inside, fmt), inside.to(lib_dt).to(torch.float64))
