@@ -310,6 +310,10 @@ OTHER_WORKLOADS = {
     "gqa8b-f16-b1": ("f16", 1, 1, "2048", 0),
     "gqa8b-f16-b8k5": ("f16", 8, 5, "1024", 0),
     "gqa8b-bf16-b64": ("bf16", 64, 1, "uniform", 0),
+    # 8-bit K/V cache (a name ending in -e4m3 / -e5m2 sets the cache's format)
+    "batch-bf16-b64-e4m3": ("bf16", 64, 1, "uniform", 0),
+    "gqa8b-bf16-b64-e4m3": ("bf16", 64, 1, "uniform", 0),
+    "verify-f16-b8k5-e4m3": ("f16", 8, 5, "1024", 0),
 }
 
 
@@ -329,7 +333,8 @@ def other_workload(args):
 
     dt, B, K, ctx_rule, chunk = OTHER_WORKLOADS[args.workload]
     gqa = args.workload.startswith("gqa")
-    dims = (W.GQA8B if gqa else W.LLAMA7B).with_dtype(dt)
+    kv8 = args.workload.rsplit("-", 1)[-1] if args.workload.endswith(("-e4m3", "-e5m2")) else None
+    dims = (W.GQA8B if gqa else W.LLAMA7B).with_dtype(dt).with_kv(kv8)
     wl = 6 if gqa else 3 if args.workload.startswith("batch") else 4 if args.workload.startswith("verify") else 5
     t0 = time.time()
     model = GpuModel(dims, seed=1000 * wl + 1)
@@ -343,7 +348,10 @@ def other_workload(args):
     max_blocks = -(-(max(ctxs + [chunk]) + K) // 16)
     n_pages = sum(-(-(c + K) // 16) for c in ctxs) + -(-chunk // 16) + 16
     pool = GpuPool(dims, n_pages)
-    pool.view().normal_()
+    if kv8:
+        pool.mem.fill_(0x30)  # every cached value 0.5 (e4m3) or 0.125 (e5m2): finite, timing-neutral
+    else:
+        pool.view().normal_()
     ids = vs.kv_alloc(pool.handle, n_pages)
     perm = synth.permutation(synth.key(1000 * wl + 6), n_pages)
     vs.kv_free(pool.handle, [ids[int(i)] for i in perm])
@@ -382,7 +390,7 @@ def other_workload(args):
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
     M = sum(len(s.tokens) for s in specs)
-    kvpt = 2 * dims.n_layers * dims.n_kv_heads * dims.head_dim * dims.elem_bytes
+    kvpt = 2 * dims.n_layers * dims.n_kv_heads * dims.head_dim * dims.kv_elem_bytes
     kv_read = sum(s.ctx + len(s.tokens) for s in specs) * kvpt  # logical K/V bytes the attention reads
     step_bytes = streamed_weight_bytes(dims) + kv_read + M * kvpt
     result = {
@@ -391,6 +399,7 @@ def other_workload(args):
         "step_bytes": step_bytes, "step_TBps": round(step_bytes / (ms * 1e-3) / 1e12, 4),
         "step_frac_of_hbm_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "contexts": [min(ctxs), max(ctxs)], "prompt_chunk_rows": chunk, "model_shape": dims.name,
+        "kv_cache": dims.kv_type,
     }
     print(json.dumps(result), flush=True)
 

@@ -57,7 +57,7 @@ class GpuPool:
     def __init__(self, dims: W.ModelDims, num_pages: int, device: str = "cuda"):
         self.dims = dims
         self.desc = vs.vs_pool_desc(num_pages, PAGE, dims.n_layers, dims.n_kv_heads, dims.head_dim,
-                                    vs.DTYPE_CODE[dims.dtype])
+                                    vs.DTYPE_CODE[dims.kv_type])
         self.page_bytes = vs.kv_page_bytes(self.desc)
         self.num_pages = num_pages
         self.mem = torch.zeros(num_pages * self.page_bytes, dtype=torch.uint8, device=device)
@@ -74,10 +74,12 @@ class GpuPool:
         except Exception:
             pass
 
-    def view(self) -> torch.Tensor:
-        """[page][layer][K|V][kv_head][slot][dim] view of the pool in the storage dtype."""
+    def view(self, raw: bool = False) -> torch.Tensor:
+        """[page][layer][K|V][kv_head][slot][dim] view of the pool in the cache's storage dtype (as
+        bytes for an 8-bit cache when raw is set)."""
         d = self.dims
-        return self.mem.view(d.torch_dtype).view(self.num_pages, d.n_layers, 2, d.n_kv_heads, PAGE, d.head_dim)
+        t = self.mem if raw and d.kv_elem_bytes == 1 else self.mem.view(d.kv_torch_dtype)
+        return t.view(self.num_pages, d.n_layers, 2, d.n_kv_heads, PAGE, d.head_dim)
 
     def write(self, row: list[int], p0: int, kv: torch.Tensor) -> None:
         """Store contiguous K/V [layer][2][n][kv_head][dim] at positions p0.. of a sequence."""
@@ -88,7 +90,10 @@ class GpuPool:
         pos = torch.arange(p0, p0 + n)
         pages = torch.tensor(row, dtype=torch.int64)[pos // PAGE].to(dev)
         slots = (pos % PAGE).to(dev)
-        self.view()[pages, :, :, :, slots, :] = kv.to(dev).permute(2, 0, 1, 3, 4)
+        if self.dims.kv_elem_bytes == 1:  # 8-bit floats move as bytes
+            self.view(raw=True)[pages, :, :, :, slots, :] = kv.view(torch.uint8).to(dev).permute(2, 0, 1, 3, 4)
+        else:
+            self.view()[pages, :, :, :, slots, :] = kv.to(dev).permute(2, 0, 1, 3, 4)
 
     def read(self, row: list[int], p0: int, p1: int) -> torch.Tensor:
         """Gather positions [p0, p1) of a sequence back to contiguous [layer][2][n][kv_head][dim] (CPU)."""
@@ -96,6 +101,9 @@ class GpuPool:
         pos = torch.arange(p0, p1)
         pages = torch.tensor(row, dtype=torch.int64)[pos // PAGE].to(dev)
         slots = (pos % PAGE).to(dev)
+        if self.dims.kv_elem_bytes == 1:
+            g = self.view(raw=True)[pages, :, :, :, slots, :].permute(1, 2, 0, 3, 4).contiguous().cpu()
+            return g.view(self.dims.kv_torch_dtype)
         return self.view()[pages, :, :, :, slots, :].permute(1, 2, 0, 3, 4).cpu()
 
 

@@ -76,3 +76,25 @@ def first_divergence_is_near_tie(gpu_argmax: list, ref_argmax: list, ref_gap: li
         if g != r:
             return not math.isnan(gap) and gap < s
     return True
+
+
+def check_kv8(got, want, what: str, max_frac: float = 0.01) -> int:
+    """K/V rows of an 8-bit cache. Both sides round the rotated value once to the format; their
+    pre-rounding values differ by fp32-versus-float64 rounding, so an element may land on the
+    neighbouring value of the format where the value sits on a rounding boundary. Every element
+    must be equal or one value of the format apart, and at most max_frac of them may differ.
+    Returns the number of differing elements."""
+    import torch
+
+    g, w = got.flatten(), want.flatten()
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(g.dtype).double()
+    table = torch.unique(codes[torch.isfinite(codes)])  # every finite value of the format, sorted
+    gd, wd = g.double(), w.double()
+    diff = gd != wd
+    n = int(diff.sum())
+    if n:
+        ig = torch.searchsorted(table, gd[diff])
+        iw = torch.searchsorted(table, wd[diff])
+        assert bool(((ig - iw).abs() <= 1).all()), f"{what}: an element is more than one value of the format off"
+        assert n <= max_frac * g.numel(), f"{what}: {n} of {g.numel()} elements differ"
+    return n

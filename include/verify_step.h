@@ -53,6 +53,12 @@ const char* vs_last_error(void);
 #define VS_F32 0
 #define VS_F16 1
 #define VS_BF16 2
+/* KV cache only: OCP 8-bit floats, one byte per value ([KV Cache] section 03:
+ * an FP8 cache in the e4m3 or e5m2 format halves the K/V bytes). K and V are
+ * rounded once from their rotated fp32 values, to nearest with ties to even,
+ * saturating at the largest finite magnitude (448 for e4m3, 57344 for e5m2). */
+#define VS_FP8_E4M3 3
+#define VS_FP8_E5M2 4
 
 /* ------------------------------------------------------------------ model */
 
@@ -106,14 +112,15 @@ typedef struct vs_weights {
  *   page p, layer l, K (0) or V (1), KV head h, slot s, dim e at element
  *   ((((p*n_layers + l)*2 + kv)*n_kv_heads + h)*page_tokens + s)*head_dim + e
  * so one (page, layer, K|V, head) block of page_tokens*head_dim values is
- * contiguous (4 KiB for 16 x 128 fp16). */
+ * contiguous (4 KiB for 16 x 128 fp16, 2 KiB in an 8-bit cache). */
 typedef struct vs_pool_desc {
     int32_t num_pages;
     int32_t page_tokens; /* 16 */
     int32_t n_layers;
     int32_t n_kv_heads;
     int32_t head_dim;
-    int32_t dtype;
+    int32_t dtype; /* VS_F32, VS_F16, VS_BF16: the model's dtype; or VS_FP8_E4M3 / VS_FP8_E5M2 with
+                      an fp16 or bf16 model whose head_dim is 128 */
 } vs_pool_desc;
 
 typedef struct vs_pool vs_pool;

@@ -20,7 +20,7 @@ import oracle
 import synth
 import verify_step_amd as vs
 from harness import GpuModel, GpuPool, SeqSpec, make_step
-from harness.compare import NEAR_TIE, TOL, check_argmax, check_rows, first_divergence_is_near_tie
+from harness.compare import NEAR_TIE, TOL, check_argmax, check_kv8, check_rows, first_divergence_is_near_tie
 from synth import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -39,8 +39,20 @@ MODELS = {"7B": W.LLAMA7B, "8B-GQA": W.GQA8B}
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("B,K", [(4, 1), (8, 5)])
 def test_7b_width_one_layer_strict(shape, dtype, B, K):
-    dims = dataclasses.replace(MODELS[shape].with_dtype(dtype), n_layers=1, name=f"{shape}-width-1L")
-    _say(f"{shape} width, 1 layer, {dtype}, B={B} K={K}")
+    _run(shape, dtype, None, B, K)
+
+
+@pytest.mark.parametrize("shape,dtype,kv8,B,K", [("7B", "f16", "e4m3", 4, 1), ("7B", "bf16", "e5m2", 8, 5),
+                                                ("8B-GQA", "f16", "e4m3", 8, 5), ("8B-GQA", "bf16", "e4m3", 4, 1)])
+def test_width_one_layer_fp8_cache(shape, dtype, kv8, B, K):
+    """An 8-bit K/V cache at full width: K/V elements equal or one value of the format apart
+    (both sides round the rotated value once), logits and greedy tokens under the same bounds."""
+    _run(shape, dtype, kv8, B, K)
+
+
+def _run(shape, dtype, kv8, B, K):
+    dims = dataclasses.replace(MODELS[shape].with_dtype(dtype), n_layers=1, name=f"{shape}-width-1L").with_kv(kv8)
+    _say(f"{shape} width, 1 layer, {dtype}, cache {kv8 or dtype}, B={B} K={K}")
     w_cpu = W.make_weights(dims, SEED_W, gains="random")
     model = GpuModel(dims, weights_cpu=w_cpu)
     ctxs = [int(c) for c in synth.uniform_int(synth.key(SEED_CHURN, B, K), 0, B, 1, 3000)]
@@ -57,7 +69,7 @@ def test_7b_width_one_layer_strict(shape, dtype, B, K):
         r = vs.kv_append(pool.handle, r, max_blocks, ctxs[b], K)
         rows.append(r)
         toks = W.token_ids(SEED_TOK, 100 * K + b, K, dims.vocab)
-        full = torch.zeros(1, 2, ctxs[b] + K, dims.n_kv_heads, dims.head_dim, dtype=dims.torch_dtype)
+        full = torch.zeros(1, 2, ctxs[b] + K, dims.n_kv_heads, dims.head_dim, dtype=dims.kv_torch_dtype)
         full[:, :, :ctxs[b]] = kv
         states.append(oracle.SeqState(full, ctxs[b], list(toks)))
         specs.append(SeqSpec(ctxs[b], list(toks)))
@@ -75,6 +87,9 @@ def test_7b_width_one_layer_strict(shape, dtype, B, K):
     for r in range(M):  # the fixed near-tie rule: a differing token only where the oracle's gap < 1e-3
         n_tie += not check_argmax(am[r], ref.argmax[r], ref.logits[r], ref.gap[r], f"row {r}")
     for b in range(B):
+        if kv8:
+            check_kv8(pool.read(rows[b], ctxs[b], ctxs[b] + K), states[b].kv[:, :, ctxs[b]:ctxs[b] + K], f"seq {b} K/V")
+            continue
         got = pool.read(rows[b], ctxs[b], ctxs[b] + K).double()
         want = states[b].kv[:, :, ctxs[b]:ctxs[b] + K].double()
         check_rows([got[0, t, i] for t in range(2) for i in range(K)], [want[0, t, i] for t in range(2) for i in range(K)],
@@ -87,6 +102,6 @@ def test_7b_width_one_layer_strict(shape, dtype, B, K):
             if (acc[b], bon[b]) != want:
                 assert first_divergence_is_near_tie(am[rs], ref.argmax[rs], ref.gap[rs], [NEAR_TIE] * K)
     e_abs = max(float((sb.logits[r].cpu().double() - ref.logits[r]).abs().max()) for r in range(M))
-    _say(f"{shape} width 1 layer {dtype} B={B} K={K}: worst logits {worst:.2e} relative, {e_abs:.2e} absolute, "
+    _say(f"{shape} width 1 layer {dtype} cache {kv8 or dtype} B={B} K={K}: worst logits {worst:.2e} relative, {e_abs:.2e} absolute, "
          f"{n_tie} near-tie rows")
     pool.close()

@@ -11,7 +11,7 @@ import oracle
 import synth
 import verify_step_amd as vs
 from harness import GpuModel, GpuPool, SeqSpec, alloc_rows, make_step, run_step
-from harness.compare import TOL, check_argmax, check_rows
+from harness.compare import TOL, check_argmax, check_kv8, check_rows
 from synth import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -40,7 +40,7 @@ def run_case(dims, ctxs, rows_per_seq, gains="one", want=None, g0=None, pool_pag
         kv = W.kv_block(dims, SEED_KV, contents[b], 0, ctxs[b])
         pool.write(rows[b], 0, kv)
         full = torch.zeros(dims.n_layers, 2, ctxs[b] + rows_per_seq[b], dims.n_kv_heads, dims.head_dim,
-                           dtype=dims.torch_dtype)
+                           dtype=dims.kv_torch_dtype)
         full[:, :, :ctxs[b]] = kv
         seqs_o.append(oracle.SeqState(full, ctxs[b], list(tokens[b]), want[b]))
     sb = make_step(model, pool, [SeqSpec(c, list(t), wl) for c, t, wl in zip(ctxs, tokens, want)], rows, g0=g0)
@@ -71,12 +71,17 @@ def check_case(dims, sb, ref, seqs_o, pool, rows, ctxs, rows_per_seq):
     for b in range(len(ctxs)):
         got = pool.read(rows[b], ctxs[b], ctxs[b] + rows_per_seq[b]).double()
         want = seqs_o[b].kv[:, :, ctxs[b]:ctxs[b] + rows_per_seq[b]].double()
-        for l in range(dims.n_layers):
-            for t in range(2):
-                for i in range(rows_per_seq[b]):
-                    check_rows([got[l, t, i]], [want[l, t, i]], tol, f"kv seq {b} layer {l} {'KV'[t]} row {i}")
+        if dims.kv_elem_bytes == 1:
+            check_kv8(pool.read(rows[b], ctxs[b], ctxs[b] + rows_per_seq[b]),
+                      seqs_o[b].kv[:, :, ctxs[b]:ctxs[b] + rows_per_seq[b]], f"kv seq {b}")
+        else:
+            for l in range(dims.n_layers):
+                for t in range(2):
+                    for i in range(rows_per_seq[b]):
+                        check_rows([got[l, t, i]], [want[l, t, i]], tol, f"kv seq {b} layer {l} {'KV'[t]} row {i}")
         # the cached prefix is untouched
-        assert torch.equal(pool.read(rows[b], 0, ctxs[b]), seqs_o[b].kv[:, :, :ctxs[b]])
+        byte = (lambda t: t.view(torch.uint8)) if dims.kv_elem_bytes == 1 else (lambda t: t)
+        assert torch.equal(byte(pool.read(rows[b], 0, ctxs[b])), byte(seqs_o[b].kv[:, :, :ctxs[b]]))
     return n_exact
 
 
@@ -169,6 +174,20 @@ def test_tiny_grouped_heads_head_dim_128_long_context():
     ctxs, k = [900, 33], [3, 1]
     sb, ref, so, pool, rows = run_case(dims, ctxs, k, gains="random", pool_pages=128)
     check_case(dims, sb, ref, so, pool, rows, ctxs, k)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("heads,kv_heads,rows", [(2, 2, [1, 1, 1, 1]), (2, 2, [5, 3]), (8, 2, [1, 2])])
+def test_tiny_fp8_cache(fmt, dtype, heads, kv_heads, rows):
+    """An 8-bit K/V cache ([KV Cache] section 03): the step writes K/V as e4m3 / e5m2 and attention
+    reads them back, for decode, verify and grouped heads (head_dim 128)."""
+    _say(f"tiny fp8 cache {fmt} dtype={dtype} heads {heads}/{kv_heads} rows={rows}")
+    dims = W.ModelDims(f"tiny-dh128-{heads}x{kv_heads}", heads * 128, heads, kv_heads, 128, 1024, 1000, 1,
+                       dtype).with_kv(fmt)
+    ctxs = [45, 3, 16, 100][:len(rows)]
+    sb, ref, so, pool, rows_ = run_case(dims, ctxs, rows, gains="random")
+    check_case(dims, sb, ref, so, pool, rows_, ctxs, rows)
 
 
 def test_tiny_rows_without_logits_and_long_context():

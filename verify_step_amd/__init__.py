@@ -17,8 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libverify_step.so")
 
 VS_OK, VS_ERR_INVALID, VS_ERR_OOM, VS_ERR_SHAPE, VS_ERR_HIP = 0, -1, -2, -3, -4
-VS_F32, VS_F16, VS_BF16 = 0, 1, 2
-DTYPE_CODE = {"f32": VS_F32, "f16": VS_F16, "bf16": VS_BF16}
+VS_F32, VS_F16, VS_BF16, VS_FP8_E4M3, VS_FP8_E5M2 = 0, 1, 2, 3, 4
+DTYPE_CODE = {"f32": VS_F32, "f16": VS_F16, "bf16": VS_BF16, "e4m3": VS_FP8_E4M3, "e5m2": VS_FP8_E5M2}
 
 EXPORTS = [
     "vs_last_error", "kv_page_bytes", "kv_pool_create", "kv_pool_destroy", "kv_alloc", "kv_share", "kv_free",

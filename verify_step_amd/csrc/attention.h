@@ -62,7 +62,7 @@ constexpr int kPartO = 4;  // offset of o in a split's statistics
 // o / l; a row with no visible key (l = 0, only if the block table is cut short) gives 0
 __device__ __forceinline__ float safe_div(float o, float l) { return l > 0.f ? o / l : 0.f; }
 
-template <int DT, int DH, int RMAX, int NW, int HG>
+template <int DT, int DH, int RMAX, int NW, int HG, int KVT = DT>  // KVT: the cache's storage type
 __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
     constexpr int DPL = DH / 16;  // dims per lane
     constexpr int NS = RMAX * HG;  // online-softmax states: (row, head) pairs
@@ -119,16 +119,16 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
         }
 
         // a ring of pages per wave: while one is reduced, the next ones are in flight
-        RawVec<DT, DPL> ka[4], va[4], kb[4], vb[4], kc[4], vc[4];
-        auto load_page = [&](RawVec<DT, DPL>(&kk)[4], RawVec<DT, DPL>(&vv)[4], int p) {
+        RawVec<KVT, DPL> ka[4], va[4], kb[4], vb[4], kc[4], vc[4];
+        auto load_page = [&](RawVec<KVT, DPL>(&kk)[4], RawVec<KVT, DPL>(&vv)[4], int p) {
             const long pb = (long)min(max(bt[p], 0), a.num_pages - 1) * a.page_elems;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                load_raw<DT, DPL>(kk[u], kvb + (pb + kofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
-                load_raw<DT, DPL>(vv[u], kvb + (pb + vofs + (long)(4 * u + g) * DH) * St<DT>::bytes);
+                load_raw<KVT, DPL>(kk[u], kvb + (pb + kofs + (long)(4 * u + g) * DH) * St<KVT>::bytes);
+                load_raw<KVT, DPL>(vv[u], kvb + (pb + vofs + (long)(4 * u + g) * DH) * St<KVT>::bytes);
             }
         };
-        auto reduce_page = [&](const RawVec<DT, DPL>(&kk)[4], const RawVec<DT, DPL>(&vv)[4], int p) {
+        auto reduce_page = [&](const RawVec<KVT, DPL>(&kk)[4], const RawVec<KVT, DPL>(&vv)[4], int p) {
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
                 const int i = st / HG;
@@ -139,7 +139,7 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
                 for (int u = 0; u < 4; ++u) {
                     float d = 0.f;
 #pragma unroll
-                    for (int e = 0; e < DPL; ++e) d += qr[st][e] * raw_at<DT, DPL>(kk[u], e);
+                    for (int e = 0; e < DPL; ++e) d += qr[st][e] * raw_at<KVT, DPL>(kk[u], e);
                     d = row16_sum(d);  // the 16 lanes of a key slot hold its 16 dim chunks
                     const int kp = p * T + 4 * u + g;
                     sc[u] = (kp <= qpos) ? d : -INFINITY;
@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
                 for (int e = 0; e < DPL; ++e) {
                     float acc = o[st][e] * alpha;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) acc += pu[u] * raw_at<DT, DPL>(vv[u], e);
+                    for (int u = 0; u < 4; ++u) acc += pu[u] * raw_at<KVT, DPL>(vv[u], e);
                     o[st][e] = acc;
                 }
                 m[st] = mn;

@@ -10,7 +10,7 @@ namespace vs {
 
 constexpr int kWave = 64;
 
-enum DType { F32 = 0, F16 = 1, BF16 = 2 };
+enum DType { F32 = 0, F16 = 1, BF16 = 2, E4M3 = 3, E5M2 = 4 };  // the last two: 8-bit K/V cache only
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -74,6 +74,51 @@ template <> struct St<BF16> {
     __device__ static __forceinline__ raw from_f(float f) { return float_to_bf16_bits(f); }
 };
 
+// OCP 8-bit floats through gfx950's conversion instructions: widening is exact;
+// narrowing rounds to nearest even, after a clamp to the largest finite value
+// (the instructions would otherwise give NaN for e4m3 and inf for e5m2).
+template <> struct St<E4M3> {
+    typedef uint8_t raw;
+    static constexpr int bytes = 1;
+    static constexpr float vmax = 448.f;
+    __device__ static __forceinline__ float to_f(raw v) { return __builtin_amdgcn_cvt_f32_fp8((int)v, 0); }
+    __device__ static __forceinline__ raw from_f(float f) {
+        f = fminf(fmaxf(f, -vmax), vmax);
+        return (raw)(__builtin_amdgcn_cvt_pk_fp8_f32(f, 0.f, 0, false) & 0xFF);
+    }
+};
+template <> struct St<E5M2> {
+    typedef uint8_t raw;
+    static constexpr int bytes = 1;
+    static constexpr float vmax = 57344.f;
+    __device__ static __forceinline__ float to_f(raw v) { return __builtin_amdgcn_cvt_f32_bf8((int)v, 0); }
+    __device__ static __forceinline__ raw from_f(float f) {
+        f = fminf(fmaxf(f, -vmax), vmax);
+        return (raw)(__builtin_amdgcn_cvt_pk_bf8_f32(f, 0.f, 0, false) & 0xFF);
+    }
+};
+
+// byte b (a constant after unrolling) of a word of four 8-bit floats, widened
+template <int DT>
+__device__ __forceinline__ float fp8_byte(uint32_t w, int b) {
+    const int x = (int)w;
+    if constexpr (DT == E4M3) {
+        switch (b & 3) {
+            case 0: return __builtin_amdgcn_cvt_f32_fp8(x, 0);
+            case 1: return __builtin_amdgcn_cvt_f32_fp8(x, 1);
+            case 2: return __builtin_amdgcn_cvt_f32_fp8(x, 2);
+            default: return __builtin_amdgcn_cvt_f32_fp8(x, 3);
+        }
+    } else {
+        switch (b & 3) {
+            case 0: return __builtin_amdgcn_cvt_f32_bf8(x, 0);
+            case 1: return __builtin_amdgcn_cvt_f32_bf8(x, 1);
+            case 2: return __builtin_amdgcn_cvt_f32_bf8(x, 2);
+            default: return __builtin_amdgcn_cvt_f32_bf8(x, 3);
+        }
+    }
+}
+
 // Load n contiguous storage elements (n * bytes a multiple of 4) and widen.
 template <int DT, int N>
 __device__ __forceinline__ void load_widen(const void* p, float* out) {
@@ -136,9 +181,10 @@ __device__ __forceinline__ void load_raw(RawVec<DT, N>& r, const void* p) {
         }
     } else {
         static_assert(W % 2 == 0, "");
+        typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
         for (int i = 0; i < W / 2; ++i) {
-            uint2 v = reinterpret_cast<const uint2*>(p)[i];
+            const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p) + i);
             r.w[2 * i + 0] = v.x;
             r.w[2 * i + 1] = v.y;
         }
@@ -149,6 +195,8 @@ template <int DT, int N>
 __device__ __forceinline__ float raw_at(const RawVec<DT, N>& r, int i) {
     if constexpr (St<DT>::bytes == 4) {
         return __uint_as_float(r.w[i]);
+    } else if constexpr (St<DT>::bytes == 1) {
+        return fp8_byte<DT>(r.w[i >> 2], i & 3);
     } else {
         const uint32_t w = r.w[i >> 1];
         return St<DT>::to_f((typename St<DT>::raw)((i & 1) ? (w >> 16) : (w & 0xFFFFu)));
@@ -158,6 +206,14 @@ __device__ __forceinline__ float raw_at(const RawVec<DT, N>& r, int i) {
 template <int DT>
 __device__ __forceinline__ void store_round(void* base, long idx, float v) {
     reinterpret_cast<typename St<DT>::raw*>(base)[idx] = St<DT>::from_f(v);
+}
+
+// One K or V element into the cache: the model's storage type, or an 8-bit float.
+template <int DT>
+__device__ __forceinline__ void store_kv(void* base, long idx, float v, int kv_dt) {
+    if (kv_dt == E4M3) reinterpret_cast<uint8_t*>(base)[idx] = St<E4M3>::from_f(v);
+    else if (kv_dt == E5M2) reinterpret_cast<uint8_t*>(base)[idx] = St<E5M2>::from_f(v);
+    else store_round<DT>(base, idx, v);
 }
 
 template <int DT>

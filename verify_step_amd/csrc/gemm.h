@@ -54,6 +54,7 @@ struct GemmArgs {
     void* kv_base;
     long page_elems;   // elements per page
     long layer_elems;  // elements per layer inside a page
+    int kv_dt;         // cache storage: DT, or E4M3 / E5M2
     int layer, head_dim, n_heads, n_kv_heads, page_tokens;
     const int* block_tables;
     int max_blocks;
@@ -291,8 +292,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, const TileMap& 
                         const long o = (long)page * g.page_elems + (long)g.layer * g.layer_elems +
                                        ((long)(tm.seg - 1) * g.n_kv_heads + tm.head) * g.page_tokens * g.head_dim +
                                        (long)slot * g.head_dim + i;
-                        store_round<DT>(g.kv_base, o, ra);
-                        store_round<DT>(g.kv_base, o + half, rb);
+                        store_kv<DT>(g.kv_base, o, ra, g.kv_dt);
+                        store_kv<DT>(g.kv_base, o + half, rb, g.kv_dt);
                     }
                 }
             }

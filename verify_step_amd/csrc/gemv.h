@@ -66,6 +66,7 @@ struct GemvArgs {
     void* q_out;
     void* kv_base;
     long page_elems, layer_elems;
+    int kv_dt;  // cache storage: DT, or E4M3 / E5M2
     int layer, head_dim, n_heads, n_kv_heads, page_tokens;
     const int* block_tables;
     int max_blocks, num_pages;
@@ -188,8 +189,8 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& g, int u, int m, f
             const long o = (long)page * g.page_elems + (long)g.layer * g.layer_elems +
                            ((long)(um.seg - 1) * g.n_kv_heads + um.head) * g.page_tokens * g.head_dim +
                            (long)(pos % g.page_tokens) * g.head_dim + um.i;
-            store_round<DT>(g.kv_base, o, ra);
-            store_round<DT>(g.kv_base, o + half, rb);
+            store_kv<DT>(g.kv_base, o, ra, g.kv_dt);
+            store_kv<DT>(g.kv_base, o + half, rb, g.kv_dt);
         }
     }
 }

@@ -22,7 +22,7 @@ struct vs_pool {
 
 extern "C" size_t kv_page_bytes(const vs_pool_desc* d) {
     if (!d) return 0;
-    const size_t elem = d->dtype == VS_F32 ? 4 : 2;
+    const size_t elem = d->dtype == VS_F32 ? 4 : (d->dtype == VS_FP8_E4M3 || d->dtype == VS_FP8_E5M2) ? 1 : 2;
     return (size_t)d->n_layers * 2 * d->n_kv_heads * d->page_tokens * d->head_dim * elem;
 }
 
@@ -32,7 +32,7 @@ extern "C" vs_status kv_pool_create(const vs_pool_desc* desc, void* dev_base, si
     if (desc->num_pages <= 0 || desc->page_tokens <= 0 || desc->n_layers <= 0 || desc->n_kv_heads <= 0 ||
         desc->head_dim <= 0)
         return vs_fail(VS_ERR_INVALID, "kv_pool_create: every size must be positive");
-    if (desc->dtype != VS_F32 && desc->dtype != VS_F16 && desc->dtype != VS_BF16)
+    if (desc->dtype < VS_F32 || desc->dtype > VS_FP8_E5M2)
         return vs_fail(VS_ERR_INVALID, "kv_pool_create: unknown dtype");
     const size_t pb = kv_page_bytes(desc);
     if (!dev_base || dev_bytes < pb * (size_t)desc->num_pages)

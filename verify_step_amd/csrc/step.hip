@@ -62,6 +62,8 @@ void launch1(int kind, void (*kern)(T), dim3 grid, dim3 block, size_t lds, hipSt
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+int kv_elem_bytes(int dtype) { return dtype == VS_F32 ? 4 : (dtype == VS_FP8_E4M3 || dtype == VS_FP8_E5M2) ? 1 : 2; }
+
 // Rows of a step at which the row-streaming GEMV gives way to the MFMA tiles (beyond four rows the
 // GEMV's LDS reads of the batch rows outrun the weight stream),
 // and the LDS the GEMV may use for its batch rows.
@@ -246,30 +248,42 @@ void launch_gemv(int kind, GemvArgs g, hipStream_t s, int units_per_wg = 0) {
 
 // The split pass, then the merge kernel unless the splits are merged elsewhere (one split
 // needs none; the output GEMV can merge them in its prologue).
-template <int DT, int DH>
-void launch_attention(const AttnArgs& a, int B, int M, int rmax, int hg, bool merge_kernel, hipStream_t s) {
+template <int DT, int DH, int KVT>
+void launch_attention_kv(const AttnArgs& a, int B, int M, int rmax, int hg, bool merge_kernel, hipStream_t s) {
     dim3 grid(a.n_splits, a.n_heads / hg, B * a.rg_blocks);
     const int nw = attn_waves(rmax * hg, DT);
     dim3 block(nw * 64);
     auto go = [&](auto kern) { launch1(VS_KERNEL_ATTN, kern, grid, block, 0, s, a); };
     switch (hg * 16 + rmax) {
-        case 16 + 1: go(attn_split_kernel<DT, DH, 1, 8, 1>); break;
+        case 16 + 1: go(attn_split_kernel<DT, DH, 1, 8, 1, KVT>); break;
         case 16 + 2:
-            if (nw == 8) go(attn_split_kernel<DT, DH, 2, DT == F32 ? 4 : 8, 1>);
-            else go(attn_split_kernel<DT, DH, 2, 4, 1>);
+            if (nw == 8) go(attn_split_kernel<DT, DH, 2, DT == F32 ? 4 : 8, 1, KVT>);
+            else go(attn_split_kernel<DT, DH, 2, 4, 1, KVT>);
             break;
-        case 16 + 4: go(attn_split_kernel<DT, DH, 4, 4, 1>); break;
-        case 16 + 5: go(attn_split_kernel<DT, DH, 5, 4, 1>); break;
+        case 16 + 4: go(attn_split_kernel<DT, DH, 4, 4, 1, KVT>); break;
+        case 16 + 5: go(attn_split_kernel<DT, DH, 5, 4, 1, KVT>); break;
         case 32 + 1:
-            if (nw == 8) go(attn_split_kernel<DT, DH, 1, DT == F32 ? 4 : 8, 2>);
-            else go(attn_split_kernel<DT, DH, 1, 4, 2>);
+            if (nw == 8) go(attn_split_kernel<DT, DH, 1, DT == F32 ? 4 : 8, 2, KVT>);
+            else go(attn_split_kernel<DT, DH, 1, 4, 2, KVT>);
             break;
-        case 32 + 2: go(attn_split_kernel<DT, DH, 2, 4, 2>); break;
-        case 64 + 1: go(attn_split_kernel<DT, DH, 1, 4, 4>); break;
-        default: go(attn_split_kernel<DT, DH, 8, 4, 1>); break;
+        case 32 + 2: go(attn_split_kernel<DT, DH, 2, 4, 2, KVT>); break;
+        case 64 + 1: go(attn_split_kernel<DT, DH, 1, 4, 4, KVT>); break;
+        default: go(attn_split_kernel<DT, DH, 8, 4, 1, KVT>); break;
     }
     if (merge_kernel && a.n_splits > 1)
         launch1(VS_KERNEL_MERGE, attn_merge_kernel<DT, DH>, dim3(M, a.n_heads), dim3(DH), 0, s, a);
+}
+
+// The cache's storage type picks the K/V loads: the model's type, or (fp16 / bf16 models with
+// head_dim 128) an 8-bit float.
+template <int DT, int DH>
+void launch_attention(const AttnArgs& a, int B, int M, int rmax, int hg, int kv_dt, bool merge_kernel,
+                      hipStream_t s) {
+    if constexpr (DT != F32 && DH == 128) {
+        if (kv_dt == E4M3) return launch_attention_kv<DT, DH, E4M3>(a, B, M, rmax, hg, merge_kernel, s);
+        if (kv_dt == E5M2) return launch_attention_kv<DT, DH, E5M2>(a, B, M, rmax, hg, merge_kernel, s);
+    }
+    launch_attention_kv<DT, DH, DT>(a, B, M, rmax, hg, merge_kernel, s);
 }
 
 // Common epilogue fields of both product paths.
@@ -283,7 +297,8 @@ void fill_epilogue(A& g, const Plan& p, const vs_batch_desc* d, const int32_t* b
     g.row_pos = row_pos;
     g.rope_cs = rope_cs;
     g.kv_base = kv_pool_base(d->pool);
-    g.page_elems = (long)(kv_page_bytes(pg) / p.esz);
+    g.kv_dt = pg->dtype;  // the pool's codes are the kernels' storage types
+    g.page_elems = (long)(kv_page_bytes(pg) / kv_elem_bytes(pg->dtype));
     g.layer_elems = 2L * p.Hkv * kPageTokens * p.Dh;
     g.head_dim = p.Dh;
     g.n_heads = p.H;
@@ -338,7 +353,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     AttnArgs a = {};
     a.q = qb;
     a.kv_base = kv_pool_base(d->pool);
-    a.page_elems = (long)(kv_page_bytes(pg) / p.esz);
+    a.page_elems = (long)(kv_page_bytes(pg) / kv_elem_bytes(pg->dtype));
     a.layer_elems = 2L * p.Hkv * kPageTokens * p.Dh;
     a.n_heads = p.H;
     a.n_kv_heads = p.Hkv;
@@ -391,8 +406,8 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
         }
 
         a.layer = l;
-        if (p.Dh == 128) launch_attention<DT, 128>(a, p.B, p.M, p.rmax, p.attn_hg, !p.merge_in_o, s);
-        else launch_attention<DT, 64>(a, p.B, p.M, p.rmax, p.attn_hg, !p.merge_in_o, s);
+        if (p.Dh == 128) launch_attention<DT, 128>(a, p.B, p.M, p.rmax, p.attn_hg, pg->dtype, !p.merge_in_o, s);
+        else launch_attention<DT, 64>(a, p.B, p.M, p.rmax, p.attn_hg, pg->dtype, !p.merge_in_o, s);
 
         // x += W_o attn
         if (p.gemv) {
@@ -552,9 +567,12 @@ extern "C" vs_status decode_step(const vs_batch_desc* desc, const int32_t* block
             return vs_fail(VS_ERR_INVALID, "decode_step: missing weight pointer in layer " + std::to_string(l));
     }
     const vs_pool_desc* pg = vs_pool_geometry(desc->pool);
-    if (pg->page_tokens != kPageTokens || pg->n_layers != p.L || pg->n_kv_heads != p.Hkv || pg->head_dim != p.Dh ||
-        pg->dtype != p.dt)
+    if (pg->page_tokens != kPageTokens || pg->n_layers != p.L || pg->n_kv_heads != p.Hkv || pg->head_dim != p.Dh)
         return vs_fail(VS_ERR_SHAPE, "decode_step: pool geometry does not match the model");
+    const bool kv8 = pg->dtype == VS_FP8_E4M3 || pg->dtype == VS_FP8_E5M2;
+    if (pg->dtype != p.dt && !(kv8 && p.dt != VS_F32 && p.Dh == 128))
+        return vs_fail(VS_ERR_SHAPE, "decode_step: the pool's dtype must be the model's, or an 8-bit float for an "
+                                     "fp16 / bf16 model with head_dim 128");
     if (!ws || ws_bytes < p.total)
         return vs_fail(VS_ERR_SHAPE, "decode_step: workspace needs " + std::to_string(p.total) + " bytes");
     char* w = static_cast<char*>(ws);
