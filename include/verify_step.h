@@ -167,6 +167,46 @@ int32_t kv_refcount(const vs_pool* pool, int32_t page); /* -1 for an out-of-rang
 /* Device address of the pool memory and the page geometry, for filling pages. */
 void* kv_pool_base(const vs_pool* pool);
 
+/* ------------------------------------------------------------------ prefix cache */
+
+/* Prefix caching ([KV Cache] section 05 "Prefix caching"; [Serving Efficiency]
+ * section 31.3): a full block is named by a hash of its own tokens and of the
+ * block before it, so the name covers the whole prefix up to it; a new
+ * sequence that finds the names of its leading blocks takes those pages
+ * instead of recomputing their K/V. The chain starts at a root that names the
+ * computation version (model and weights, adapters, positional conventions)
+ * and the access scope allowed to share, so different versions or scopes never
+ * match. Only full blocks are named.
+ *
+ * Hash: 64-bit FNV-1a (offset basis 0xcbf29ce484222325, prime 0x100000001b3).
+ * root = FNV-1a over the caller's key bytes; block i's hash = FNV-1a over the
+ * 8 little-endian bytes of the previous hash (the root for block 0) followed
+ * by the block's page_tokens token ids as 4 little-endian bytes each.
+ *
+ * The index lives with the pool (host memory) and holds one reference on each
+ * indexed page, so an indexed page stays allocated after every sequence has
+ * freed it, until kv_prefix_evict drops it. Not thread-safe, like the pool. */
+vs_status kv_prefix_root(const void* key, size_t len, uint64_t* root);
+/* hashes[i] for the floor(n_tokens / page_tokens) full blocks of tokens[0 .. n_tokens). */
+vs_status kv_prefix_chain(uint64_t root, const int32_t* tokens, int32_t n_tokens, int32_t page_tokens,
+                          uint64_t* hashes);
+/* Index the n_blocks leading full blocks of a sequence whose K/V are in pages[0 .. n_blocks) (call it
+ * once the step that wrote them has completed). hashes must be the chain of tokens under root
+ * (checked); a block already indexed keeps its page (the caller's copy is left alone). Each new entry
+ * takes one reference on its page. *n_added (may be NULL) = entries added. */
+vs_status kv_prefix_insert(vs_pool* pool, uint64_t root, const uint64_t* hashes, const int32_t* tokens,
+                           const int32_t* pages, int32_t n_blocks, int32_t* n_added);
+/* The longest run of leading blocks indexed under these hashes whose stored tokens (and parent
+ * hash) also match, *n_hit of them; pages_out[0 .. *n_hit) receive their pages, each with one
+ * reference taken for the caller (released with kv_free like any other page). Marks them used. */
+vs_status kv_prefix_lookup(vs_pool* pool, uint64_t root, const uint64_t* hashes, const int32_t* tokens,
+                           int32_t n_blocks, int32_t* pages_out, int32_t* n_hit);
+/* Drop up to n_pages entries whose page only the index still holds, least recently used first
+ * (deeper blocks of a chain first among equals), returning their pages to the free list.
+ * *n_freed (may be NULL) = pages freed. */
+vs_status kv_prefix_evict(vs_pool* pool, int32_t n_pages, int32_t* n_freed);
+int32_t kv_prefix_entries(const vs_pool* pool);
+
 /* ------------------------------------------------------------------ step */
 
 /* One step's batch ([Serving] "Continuous batching"; [KV Cache] section 06:

@@ -92,3 +92,100 @@ class PoolModel:
             table[-1] = new
         table.extend(got)
         return table, copies
+
+
+# ---- prefix caching ([KV Cache] section 05 "Prefix caching"; [Serving Efficiency] section 31.3)
+
+FNV64_OFFSET_BASIS = 0xCBF29CE484222325  # the published 64-bit FNV parameters
+FNV64_PRIME = 0x100000001B3
+
+
+def fnv1a64(data: bytes, h: int = FNV64_OFFSET_BASIS) -> int:
+    """64-bit FNV-1a: for each byte, xor it in, then multiply by the prime modulo 2^64."""
+    for byte in data:
+        h ^= byte
+        h = (h * FNV64_PRIME) % (1 << 64)
+    return h
+
+
+def prefix_root(key: bytes) -> int:
+    """The chain's root: a hash of the key naming the computation version and access scope
+    ([Serving Efficiency] section 31.3: the key must identify token content and computation
+    version, and reuse stays inside the allowed access boundary)."""
+    return fnv1a64(key)
+
+
+def block_hash(parent: int, tokens: list) -> int:
+    """A full block's name: the parent's hash (8 little-endian bytes) followed by the block's token
+    ids (4 little-endian bytes each), so it names the whole prefix up to the block ([KV Cache]
+    section 05: each full block is identified by its own content plus its parent block's hash)."""
+    data = parent.to_bytes(8, "little") + b"".join((t & 0xFFFFFFFF).to_bytes(4, "little") for t in tokens)
+    return fnv1a64(data)
+
+
+def prefix_chain(root: int, tokens: list, page_tokens: int) -> list:
+    """Hashes of the full blocks of a token sequence; a partial last block has none."""
+    out, h = [], root
+    for i in range(len(tokens) // page_tokens):
+        h = block_hash(h, tokens[i * page_tokens:(i + 1) * page_tokens])
+        out.append(h)
+    return out
+
+
+class PrefixIndex:
+    """The prefix-cache index of a PoolModel: chain hash -> the page holding that full block.
+
+    The index keeps one reference on every indexed page. Inserting names a sequence's leading full
+    blocks (a block already named keeps its page). Looking up returns the longest run of leading
+    blocks that are named, whose stored tokens and parent also match, and takes a reference on each
+    for the caller ([KV Cache] section 05: on a match, bump the reference count and skip that part
+    of the prefill). Evicting drops entries only the index still holds, least recently used first;
+    among entries last used together the deeper block goes first, so a chain is trimmed from its
+    end (the order a radix-tree cache evicts leaves first, [KV Cache] section 05).
+    """
+
+    def __init__(self, pool: PoolModel):
+        self.pool = pool
+        self.entries = {}  # hash -> [parent, tokens, page, depth, last_use]
+        self.clock = 0
+
+    def insert(self, root: int, hashes: list, tokens: list, pages: list):
+        T = self.pool.page_tokens
+        for i, (h, p) in enumerate(zip(hashes, pages)):
+            if not (0 <= p < self.pool.num_pages) or self.pool.ref[p] == 0:
+                return None
+            if block_hash(root if i == 0 else hashes[i - 1], tokens[i * T:(i + 1) * T]) != h:
+                return None
+        self.clock += 1
+        added = 0
+        for i, (h, p) in enumerate(zip(hashes, pages)):
+            if h in self.entries:
+                self.entries[h][4] = self.clock
+                continue
+            self.entries[h] = [root if i == 0 else hashes[i - 1], list(tokens[i * T:(i + 1) * T]), p, i, self.clock]
+            self.pool.ref[p] += 1
+            added += 1
+        return added
+
+    def lookup(self, root: int, hashes: list, tokens: list) -> list:
+        T = self.pool.page_tokens
+        self.clock += 1
+        hit = []
+        for i, h in enumerate(hashes):
+            e = self.entries.get(h)
+            if e is None or e[0] != (root if i == 0 else hashes[i - 1]) or e[1] != list(tokens[i * T:(i + 1) * T]):
+                break
+            hit.append(e)
+        for e in hit:
+            e[4] = self.clock
+            self.pool.ref[e[2]] += 1
+        return [e[2] for e in hit]
+
+    def evict(self, n_pages: int) -> int:
+        cands = sorted((e[4], -e[3], h) for h, e in self.entries.items() if self.pool.ref[e[2]] == 1)
+        freed = 0
+        for _, _, h in cands[:n_pages]:
+            page = self.entries.pop(h)[2]
+            self.pool.ref[page] = 0
+            freed += 1
+        return freed

@@ -190,6 +190,46 @@ def test_tiny_fp8_cache(fmt, dtype, heads, kv_heads, rows):
     check_case(dims, sb, ref, so, pool, rows_, ctxs, rows)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tiny_prefix_cache_hit_skips_the_shared_prefill(dtype):
+    """[KV Cache] section 05 "Prefix caching": request A prefills 40 tokens and indexes its two full
+    blocks; request B, equal to A for its first 32 tokens, finds both, takes those pages and runs
+    only its last 7 tokens. B's logits and every K/V row of its cache match the oracle running B
+    from scratch, its 32-token prefix included."""
+    _say(f"tiny prefix cache hit, dtype={dtype}")
+    dims = W.TINY.with_dtype(dtype)
+    w_cpu = W.make_weights(dims, SEED_W, gains="random")
+    model = GpuModel(dims, weights_cpu=w_cpu)
+    pool = GpuPool(dims, 16)
+    root = vs.kv_prefix_root(f"tiny;{dtype};weights={SEED_W};theta=10000".encode())
+    a = W.token_ids(SEED_TOK, 600, 40, dims.vocab)
+    b = a[:32] + W.token_ids(SEED_TOK, 601, 7, dims.vocab)
+    ra = vs.kv_append(pool.handle, [], 4, 0, 40)
+    run_step(model, make_step(model, pool, [SeqSpec(0, a, want_logits=False)], [ra], max_blocks=4))
+    torch.cuda.synchronize()
+    ha = vs.kv_prefix_chain(root, a, 16)
+    assert len(ha) == 2 and vs.kv_prefix_insert(pool.handle, root, ha, a[:32], ra[:2]) == 2
+    hb = vs.kv_prefix_chain(root, b, 16)
+    assert hb == ha, "the first 32 tokens are equal, so are the names of the two full blocks"
+    hit = vs.kv_prefix_lookup(pool.handle, root, hb, b[:32])
+    assert hit == ra[:2] and vs.kv_refcount(pool.handle, ra[0]) == 3  # A, the index, B
+    rb = vs.kv_append(pool.handle, hit, 4, 32, 7)
+    sb = make_step(model, pool, [SeqSpec(32, b[32:])], [rb], max_blocks=4)
+    run_step(model, sb)
+    torch.cuda.synchronize()
+    st = oracle.SeqState(torch.zeros(1, 2, 39, dims.n_kv_heads, dims.head_dim, dtype=dims.kv_torch_dtype), 0, list(b))
+    ref = oracle.decode_step(dims, w_cpu, [st])
+    tol = TOL[dtype]
+    check_rows([sb.logits[i].cpu() for i in range(7)], ref.logits[32:39], tol, "B's logits")
+    am = sb.argmax[:7].cpu().tolist()
+    for i in range(7):
+        check_argmax(am[i], ref.argmax[32 + i], ref.logits[32 + i], ref.gap[32 + i], f"B row {i}", sb.logits[i].cpu())
+    got, want = pool.read(rb, 0, 39).double(), st.kv.double()
+    check_rows([got[0, t, i] for t in range(2) for i in range(39)], [want[0, t, i] for t in range(2) for i in range(39)],
+               tol, "B's K/V (prefix written by A's step)")
+    pool.close()
+
+
 def test_tiny_rows_without_logits_and_long_context():
     """A long sequence spanning many splits, one sequence without logits, head_dim 128."""
     _say("tiny head_dim 128, long context, no-logit sequence")

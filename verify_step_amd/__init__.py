@@ -11,7 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, Structure, c_float, c_int32, c_size_t, c_void_p
+from ctypes import POINTER, Structure, c_float, c_int32, c_size_t, c_uint64, c_void_p
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libverify_step.so")
@@ -22,7 +22,9 @@ DTYPE_CODE = {"f32": VS_F32, "f16": VS_F16, "bf16": VS_BF16, "e4m3": VS_FP8_E4M3
 
 EXPORTS = [
     "vs_last_error", "kv_page_bytes", "kv_pool_create", "kv_pool_destroy", "kv_alloc", "kv_share", "kv_free",
-    "kv_append", "kv_num_free", "kv_refcount", "kv_pool_base", "decode_step_workspace_bytes", "decode_step",
+    "kv_append", "kv_num_free", "kv_refcount", "kv_pool_base", "kv_prefix_root", "kv_prefix_chain",
+    "kv_prefix_insert", "kv_prefix_lookup", "kv_prefix_evict", "kv_prefix_entries", "decode_step_workspace_bytes",
+    "decode_step",
     "verify_accept", "verify_sample_workspace_bytes", "verify_sample", "vs_time_kernel", "vs_timed_launches",
 ]
 
@@ -100,6 +102,19 @@ def lib() -> ctypes.CDLL:
         L.kv_refcount.argtypes = [c_void_p, c_int32]
         L.kv_pool_base.restype = c_void_p
         L.kv_pool_base.argtypes = [c_void_p]
+        u64p = POINTER(c_uint64)
+        L.kv_prefix_root.restype = c_int32
+        L.kv_prefix_root.argtypes = [c_void_p, c_size_t, u64p]
+        L.kv_prefix_chain.restype = c_int32
+        L.kv_prefix_chain.argtypes = [c_uint64, i32p, c_int32, c_int32, u64p]
+        L.kv_prefix_insert.restype = c_int32
+        L.kv_prefix_insert.argtypes = [c_void_p, c_uint64, u64p, i32p, i32p, c_int32, i32p]
+        L.kv_prefix_lookup.restype = c_int32
+        L.kv_prefix_lookup.argtypes = [c_void_p, c_uint64, u64p, i32p, c_int32, i32p, i32p]
+        L.kv_prefix_evict.restype = c_int32
+        L.kv_prefix_evict.argtypes = [c_void_p, c_int32, i32p]
+        L.kv_prefix_entries.restype = c_int32
+        L.kv_prefix_entries.argtypes = [c_void_p]
         L.decode_step_workspace_bytes.restype = c_int32
         L.decode_step_workspace_bytes.argtypes = [POINTER(vs_batch_desc), POINTER(vs_model_desc), POINTER(c_size_t)]
         L.decode_step.restype = c_int32
@@ -191,6 +206,49 @@ def kv_refcount(pool: int, page: int) -> int:
 
 def kv_pool_base(pool: int) -> int:
     return int(lib().kv_pool_base(c_void_p(pool)) or 0)
+
+
+def kv_prefix_root(key: bytes) -> int:
+    out = c_uint64()
+    _check(lib().kv_prefix_root(key, len(key), ctypes.byref(out)))
+    return int(out.value)
+
+
+def _u64_array(xs):
+    return (c_uint64 * max(1, len(xs)))(*xs)
+
+
+def kv_prefix_chain(root: int, tokens: list[int], page_tokens: int) -> list[int]:
+    n = len(tokens) // page_tokens
+    out = (c_uint64 * max(1, n))()
+    _check(lib().kv_prefix_chain(root, _i32_array(tokens), len(tokens), page_tokens, out))
+    return [int(h) for h in out[:n]]
+
+
+def kv_prefix_insert(pool: int, root: int, hashes: list[int], tokens: list[int], pages: list[int]) -> int:
+    added = c_int32()
+    _check(lib().kv_prefix_insert(c_void_p(pool), root, _u64_array(hashes), _i32_array(tokens), _i32_array(pages),
+                                  len(hashes), ctypes.byref(added)))
+    return int(added.value)
+
+
+def kv_prefix_lookup(pool: int, root: int, hashes: list[int], tokens: list[int]) -> list[int]:
+    """Pages of the longest indexed run of leading blocks (one reference taken on each for the caller)."""
+    pages = (c_int32 * max(1, len(hashes)))()
+    hit = c_int32()
+    _check(lib().kv_prefix_lookup(c_void_p(pool), root, _u64_array(hashes), _i32_array(tokens), len(hashes), pages,
+                                  ctypes.byref(hit)))
+    return list(pages[:hit.value])
+
+
+def kv_prefix_evict(pool: int, n_pages: int) -> int:
+    freed = c_int32()
+    _check(lib().kv_prefix_evict(c_void_p(pool), n_pages, ctypes.byref(freed)))
+    return int(freed.value)
+
+
+def kv_prefix_entries(pool: int) -> int:
+    return int(lib().kv_prefix_entries(c_void_p(pool)))
 
 
 # ---------------------------------------------------------------- step

@@ -1,10 +1,14 @@
 // Host-side bookkeeping of the paged KV cache: a free list, per-page reference
 // counts, block-table growth and copy-on-write of a shared, partly filled last
 // page ([KV Cache] section 05 "The block table" and "Block sharing and
-// copy-on-write"; [Serving Efficiency] section 31.3).
+// copy-on-write"; [Serving Efficiency] section 31.3), and the prefix-cache
+// index over full blocks ([KV Cache] section 05 "Prefix caching").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cstring>
 #include <string>
+#include <tuple>
 #include <unordered_map>
 #include <vector>
 
@@ -18,6 +22,15 @@ struct vs_pool {
     size_t page_bytes;
     std::vector<int32_t> ref;        // reference count per page
     std::vector<int32_t> free_list;  // stack of free page ids (top = back)
+    // prefix-cache index: chain hash of a full block -> the page holding it (one reference each)
+    struct Entry {
+        uint64_t parent;              // chain hash of the block before it (the root for block 0)
+        std::vector<int32_t> tokens;  // the block's token ids (a hash match must also match these)
+        int32_t page, depth;          // depth: the block's index in its chain
+        uint64_t last_use;
+    };
+    std::unordered_map<uint64_t, Entry> index;
+    uint64_t clock = 0;
 };
 
 extern "C" size_t kv_page_bytes(const vs_pool_desc* d) {
@@ -144,6 +157,136 @@ extern "C" int32_t kv_refcount(const vs_pool* pool, int32_t page) {
 }
 
 extern "C" void* kv_pool_base(const vs_pool* pool) { return pool ? pool->base : nullptr; }
+
+// ---- prefix-cache index ([KV Cache] section 05 "Prefix caching"; [Serving Efficiency] section 31.3)
+
+namespace {
+
+// 64-bit FNV-1a (Fowler, Noll, Vo): offset basis 0xcbf29ce484222325, prime 0x100000001b3.
+uint64_t fnv1a64(uint64_t h, const void* data, size_t n) {
+    const unsigned char* p = static_cast<const unsigned char*>(data);
+    for (size_t i = 0; i < n; ++i) {
+        h ^= p[i];
+        h *= 0x100000001b3ULL;
+    }
+    return h;
+}
+constexpr uint64_t kFnvBasis = 0xcbf29ce484222325ULL;
+
+// one block: FNV-1a over the parent's 8 little-endian bytes, then each token id's 4
+uint64_t block_hash(uint64_t parent, const int32_t* tokens, int32_t T) {
+    unsigned char buf[8];
+    for (int i = 0; i < 8; ++i) buf[i] = (unsigned char)(parent >> (8 * i));
+    uint64_t h = fnv1a64(kFnvBasis, buf, 8);
+    for (int32_t t = 0; t < T; ++t) {
+        const uint32_t v = (uint32_t)tokens[t];
+        const unsigned char b[4] = {(unsigned char)v, (unsigned char)(v >> 8), (unsigned char)(v >> 16),
+                                    (unsigned char)(v >> 24)};
+        h = fnv1a64(h, b, 4);
+    }
+    return h;
+}
+
+}  // namespace
+
+extern "C" vs_status kv_prefix_root(const void* key, size_t len, uint64_t* root) {
+    if (!root || (len > 0 && !key)) return vs_fail(VS_ERR_INVALID, "kv_prefix_root: null argument");
+    *root = fnv1a64(kFnvBasis, key, len);
+    return vs_ok();
+}
+
+extern "C" vs_status kv_prefix_chain(uint64_t root, const int32_t* tokens, int32_t n_tokens, int32_t page_tokens,
+                                     uint64_t* hashes) {
+    if (n_tokens < 0 || page_tokens <= 0) return vs_fail(VS_ERR_INVALID, "kv_prefix_chain: bad size");
+    const int32_t n = n_tokens / page_tokens;
+    if (n > 0 && (!tokens || !hashes)) return vs_fail(VS_ERR_INVALID, "kv_prefix_chain: null argument");
+    uint64_t h = root;
+    for (int32_t i = 0; i < n; ++i) hashes[i] = h = block_hash(h, tokens + (size_t)i * page_tokens, page_tokens);
+    return vs_ok();
+}
+
+extern "C" vs_status kv_prefix_insert(vs_pool* pool, uint64_t root, const uint64_t* hashes, const int32_t* tokens,
+                                      const int32_t* pages, int32_t n_blocks, int32_t* n_added) {
+    if (!pool || n_blocks < 0 || (n_blocks > 0 && (!hashes || !tokens || !pages)))
+        return vs_fail(VS_ERR_INVALID, "kv_prefix_insert: bad argument");
+    const int32_t T = pool->desc.page_tokens;
+    for (int32_t i = 0; i < n_blocks; ++i) {
+        if (!valid_id(pool, pages[i]) || pool->ref[pages[i]] == 0)
+            return vs_fail(VS_ERR_INVALID, "kv_prefix_insert: page " + std::to_string(pages[i]) + " is not in use");
+        const uint64_t parent = i == 0 ? root : hashes[i - 1];
+        if (block_hash(parent, tokens + (size_t)i * T, T) != hashes[i])
+            return vs_fail(VS_ERR_INVALID, "kv_prefix_insert: hash " + std::to_string(i) +
+                                               " is not the chain hash of its block");
+    }
+    const uint64_t now = ++pool->clock;
+    int32_t added = 0;
+    for (int32_t i = 0; i < n_blocks; ++i) {
+        auto it = pool->index.find(hashes[i]);
+        if (it != pool->index.end()) {  // already held (another sequence computed it first)
+            it->second.last_use = now;
+            continue;
+        }
+        vs_pool::Entry e;
+        e.parent = i == 0 ? root : hashes[i - 1];
+        e.tokens.assign(tokens + (size_t)i * T, tokens + (size_t)(i + 1) * T);
+        e.page = pages[i];
+        e.depth = i;
+        e.last_use = now;
+        pool->index.emplace(hashes[i], std::move(e));
+        pool->ref[pages[i]] += 1;  // the index's own reference
+        ++added;
+    }
+    if (n_added) *n_added = added;
+    return vs_ok();
+}
+
+extern "C" vs_status kv_prefix_lookup(vs_pool* pool, uint64_t root, const uint64_t* hashes, const int32_t* tokens,
+                                      int32_t n_blocks, int32_t* pages_out, int32_t* n_hit) {
+    if (!pool || !n_hit || n_blocks < 0 || (n_blocks > 0 && (!hashes || !tokens || !pages_out)))
+        return vs_fail(VS_ERR_INVALID, "kv_prefix_lookup: bad argument");
+    const int32_t T = pool->desc.page_tokens;
+    const uint64_t now = ++pool->clock;
+    int32_t hit = 0;
+    for (; hit < n_blocks; ++hit) {
+        auto it = pool->index.find(hashes[hit]);
+        if (it == pool->index.end()) break;
+        const vs_pool::Entry& e = it->second;
+        const uint64_t parent = hit == 0 ? root : hashes[hit - 1];
+        if (e.parent != parent || std::memcmp(e.tokens.data(), tokens + (size_t)hit * T, sizeof(int32_t) * T) != 0)
+            break;  // a hash collision: not this prefix
+    }
+    for (int32_t i = 0; i < hit; ++i) {
+        vs_pool::Entry& e = pool->index.find(hashes[i])->second;
+        e.last_use = now;
+        pool->ref[e.page] += 1;  // the caller's reference
+        pages_out[i] = e.page;
+    }
+    *n_hit = hit;
+    return vs_ok();
+}
+
+extern "C" vs_status kv_prefix_evict(vs_pool* pool, int32_t n_pages, int32_t* n_freed) {
+    if (!pool || n_pages < 0) return vs_fail(VS_ERR_INVALID, "kv_prefix_evict: bad argument");
+    // candidates: entries only the index still holds; least recently used first, deeper blocks first
+    std::vector<std::tuple<uint64_t, int32_t, uint64_t>> cand;  // (last_use, -depth, hash)
+    for (const auto& kv : pool->index)
+        if (pool->ref[kv.second.page] == 1) cand.emplace_back(kv.second.last_use, -kv.second.depth, kv.first);
+    std::sort(cand.begin(), cand.end());
+    int32_t freed = 0;
+    for (const auto& c : cand) {
+        if (freed >= n_pages) break;
+        auto it = pool->index.find(std::get<2>(c));
+        const int32_t page = it->second.page;
+        pool->index.erase(it);
+        pool->ref[page] = 0;
+        pool->free_list.push_back(page);
+        ++freed;
+    }
+    if (n_freed) *n_freed = freed;
+    return vs_ok();
+}
+
+extern "C" int32_t kv_prefix_entries(const vs_pool* pool) { return pool ? (int32_t)pool->index.size() : -1; }
 
 // internal accessors for the step
 const vs_pool_desc* vs_pool_geometry(const vs_pool* pool) { return &pool->desc; }
