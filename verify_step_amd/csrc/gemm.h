@@ -301,7 +301,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, const TileMap& 
     }
 }
 
-template <int DT, int MT, int NW, int EPI, int U>
+// STREAM: one row group (every weight byte is used once), so the weight loads carry the
+// nontemporal hint.
+template <int DT, int MT, int NW, int EPI, int U, bool STREAM>
 __global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
     constexpr bool SB = EPI == EPI_RESID || EPI == EPI_LOGITS;  // tiles of one 16-row block
     constexpr int NB = SB ? 1 : 2;
@@ -369,8 +371,10 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
         // block passes through a wave-private LDS slab and is read back as MFMA A fragments.
         // Blocks of 128 reduction elements = 4 k-steps; the next block's loads are in flight while
         // the current one is multiplied.
+        // Every load below is unconditional (out-of-range lanes read an in-bounds address and mask the
+        // result), so the loads of the next block stay in flight: with a branch around a load the
+        // compiler can only wait for all outstanding loads before the current block is used.
         unsigned char* my = lds + wave * SLAB;
-        const bool stream = gridDim.x == 1;  // one row group: every weight byte is used once
         const int rr = lane >> 4, cc = lane & 15;  // R4 layout: row in the group of four, 16-byte column
         long rowoff[NB][4];
         bool rowv[NB][4];
@@ -384,8 +388,17 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
             }
         const uint16_t* wA = reinterpret_cast<const uint16_t*>(tm.w);
         const uint16_t* wB = reinterpret_cast<const uint16_t*>(tm.wb);
-        auto load_block = [&](uint4(&wv)[NB][4], int kc) {
-            // lanes past the wave's slice load in-bounds data that the mask below clears
+        // Weights of k-steps outside the wave's slice (and of rows past the segment) are read from an
+        // in-bounds address and zeroed when written to the slab; the zero weights cancel whatever the
+        // activations hold there, so the activation loads need no mask: their out-of-slice k-steps
+        // read in-bounds activations of the same row, and batch rows past M (clamped to row 0) only
+        // reach output columns the epilogue does not store. No load result is touched before the
+        // multiply that needs it.
+        struct WBlock {
+            uint4 v[NB][4];
+            uint32_t keep[NB][4];
+        };
+        auto load_block = [&](WBlock& wb, int kc) {
             const bool kin = kc + (cc >> 2) < kc1;
             const long ko = kin ? (long)kc * 32 : -(long)(8 * cc);  // masked lanes read their row's start
 #pragma unroll
@@ -393,24 +406,31 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint16_t* src = (bl ? wB : wA) + rowoff[bl][j] + ko;
-                    const uint4 v = stream ? load_stream16(src) : *reinterpret_cast<const uint4*>(src);
-                    const uint32_t keep = (kin && rowv[bl][j]) ? 0xFFFFFFFFu : 0u;
-                    wv[bl][j] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+                    wb.v[bl][j] = STREAM ? load_stream16(src) : *reinterpret_cast<const uint4*>(src);
+                    wb.keep[bl][j] = (kin && rowv[bl][j]) ? 0xFFFFFFFFu : 0u;
                 }
         };
+        const long xlast = (long)(KC - 1) * 32;  // last k-step of a row: keeps clamped reads in bounds
         auto load_x = [&](Frag<DT>(&fx)[4][MT], int kc) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    frag_load<DT>(fx[ks][mt], g.act, xbase[mt] + (long)(kc + ks) * 32, kc + ks < kc1 && xv[mt]);
+                for (int mt = 0; mt < MT; ++mt) {
+                    const long ko = min((long)(kc + ks) * 32, xlast);
+                    fx[ks][mt].a = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(g.act) +
+                                                                    xbase[mt] + ko);
+                }
         };
-        auto multiply = [&](const uint4(&wv)[NB][4], const Frag<DT>(&fx)[4][MT]) {
+        auto multiply = [&](const WBlock& wb, const Frag<DT>(&fx)[4][MT]) {
 #pragma unroll
             for (int bl = 0; bl < NB; ++bl)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<uint4*>(my + bl * 16 * ROWB + (4 * j + rr) * ROWB + 16 * cc) = wv[bl][j];
+                for (int j = 0; j < 4; ++j) {
+                    const uint4 v = wb.v[bl][j];
+                    const uint32_t kp = wb.keep[bl][j];
+                    *reinterpret_cast<uint4*>(my + bl * 16 * ROWB + (4 * j + rr) * ROWB + 16 * cc) =
+                        make_uint4(v.x & kp, v.y & kp, v.z & kp, v.w & kp);
+                }
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 Frag<DT> fa, fb;
@@ -424,36 +444,34 @@ __global__ void __launch_bounds__(NW * 64) gemm_skinny_kernel(GemmArgs g) {
                 }
             }
         };
-        uint4 w0[NB][4], w1[NB][4];
-        if constexpr (MT <= 2) {  // weights and activations of the next block both in flight
+        WBlock w0, w1;
+        if constexpr (MT <= 2 || (SB && MT <= 4)) {  // weights and activations of the next block in flight
             Frag<DT> x0[4][MT], x1[4][MT];
-            if (kc0 < kc1) {
-                load_block(w0, kc0);
-                load_x(x0, kc0);
-            }
+            load_block(w0, kc0);
+            load_x(x0, kc0);
             for (int kc = kc0; kc < kc1; kc += 8) {
-                if (kc + 4 < kc1) {
-                    load_block(w1, kc + 4);
-                    load_x(x1, kc + 4);
-                }
+                load_block(w1, kc + 4);  // past the slice: masked, in-bounds reads
+                load_x(x1, kc + 4);
+                __builtin_amdgcn_sched_barrier(0);  // keep the next block's loads ahead of this multiply
                 multiply(w0, x0);
                 if (kc + 4 >= kc1) break;
-                if (kc + 8 < kc1) {
-                    load_block(w0, kc + 8);
-                    load_x(x0, kc + 8);
-                }
+                load_block(w0, kc + 8);
+                load_x(x0, kc + 8);
+                __builtin_amdgcn_sched_barrier(0);
                 multiply(w1, x1);
             }
-        } else {  // three or four row blocks: only the weights run ahead (registers)
+        } else {  // two weight blocks of three or four row blocks: only the weights run ahead (registers)
             Frag<DT> xf[4][MT];
-            if (kc0 < kc1) load_block(w0, kc0);
+            load_block(w0, kc0);
             for (int kc = kc0; kc < kc1; kc += 8) {
-                if (kc + 4 < kc1) load_block(w1, kc + 4);
-                load_x(xf, kc);
+                load_x(xf, kc);  // before the next weights, so that using it leaves those in flight
+                load_block(w1, kc + 4);
+                __builtin_amdgcn_sched_barrier(0);
                 multiply(w0, xf);
                 if (kc + 4 >= kc1) break;
-                if (kc + 8 < kc1) load_block(w0, kc + 8);
                 load_x(xf, kc + 4);
+                load_block(w0, kc + 8);
+                __builtin_amdgcn_sched_barrier(0);
                 multiply(w1, xf);
             }
         }

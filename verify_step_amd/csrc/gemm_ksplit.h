@@ -1,0 +1,183 @@
+// Split-K tile GEMM for the residual products (attention output and MLP down
+// projections) of steps with 17..64 rows (gfx950).
+//
+// x[m][n] += sum_k X[m][k] * W[n][k] ([KV Cache] section 02: every row passing
+// through a weight matrix shares one read of it). A workgroup of 8 waves owns
+// 128 output features (16 per wave) and one slice of at most 512 reduction
+// elements. It stages its slice of all the step's rows (X) in LDS once, with
+// coalesced loads, and every wave reads its MFMA B fragments from there: the
+// activation bytes fetched from L2 are 1/8 of what a 16-feature tile per
+// workgroup would fetch, where they cost as much as the weight stream itself.
+// Each wave streams its 16 weight rows four rows x 256 bytes per load through a
+// wave-private LDS slab (read back as MFMA A fragments), two 128-element blocks
+// ahead of the multiply. Workgroups along the reduction write fp32 partial sums
+// [slice][row][feature]; resid_reduce_kernel adds them to x in slice order, so
+// the result does not depend on timing.
+#pragma once
+
+#include "common.h"
+#include "gemm.h"
+
+namespace vs {
+
+constexpr int kKsRows = 128;  // output features per workgroup (8 waves x 16)
+constexpr int kKsXPad = 8;    // LDS row padding (elements): a fragment's 16 rows fall on different banks
+// most reduction elements per workgroup (measured: longer slices leave too few workgroups for the
+// 4096-feature products, shorter ones add partial sums)
+__host__ __device__ constexpr int ks_slice(int) { return 512; }
+
+struct KsplitArgs {
+    const void* w;  // [N][K] storage type
+    int N, K;       // K a multiple of 32
+    const void* act;  // [M][act_ld] storage type
+    int act_ld, M;    // M <= 16 * MT
+    int n_slices;     // workgroups along K (gridDim.y); every slice holds at most ks_slice(MT) elements
+    float* part;      // [n_slices][M][N] fp32
+};
+
+template <int DT, int MT, bool STREAM>
+__global__ void __launch_bounds__(512) gemm_ksplit_kernel(KsplitArgs g) {
+    constexpr int ROWB = 256 + 16;  // slab row stride in bytes
+    constexpr int SLAB = 16 * ROWB;
+    constexpr int XLD = ks_slice(MT) + kKsXPad;  // X row stride in LDS, elements
+    __shared__ __align__(16) uint16_t xs[MT * 16 * XLD];
+    __shared__ __align__(16) unsigned char slabs[8 * SLAB];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n0 = blockIdx.x * kKsRows + wave * 16;
+    const int sl = blockIdx.y;
+    const int KC = g.K / 32;
+    const int c0 = (int)(((long)sl * KC) / g.n_slices), c1 = (int)(((long)(sl + 1) * KC) / g.n_slices);
+    const int nsteps = c1 - c0;  // 32-element steps of this slice (<= ks_slice(MT) / 32)
+    const long kbase = (long)c0 * 32;
+
+    // ---- weights: 16 rows of this wave, blocks of 128 elements (4 steps), R4 layout
+    const int rr = lane >> 4, cc = lane & 15;
+    long rowoff[4];
+    bool rowv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = n0 + 4 * j + rr;
+        rowv[j] = row < g.N;
+        rowoff[j] = (long)(rowv[j] ? row : 0) * g.K + kbase + 8 * cc;
+    }
+    const uint16_t* W = reinterpret_cast<const uint16_t*>(g.w);
+    struct WBlock {
+        uint4 v[4];
+        uint32_t keep[4];
+    };
+    // out-of-slice steps read their row's first chunk and are zeroed on the way into the slab
+    auto load_block = [&](WBlock& wb, int b) {
+        const bool kin = 4 * b + (cc >> 2) < nsteps;
+        const long ko = kin ? (long)b * 128 : -(long)(8 * cc) - kbase;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint16_t* src = W + rowoff[j] + ko;
+            wb.v[j] = STREAM ? load_stream16(src) : *reinterpret_cast<const uint4*>(src);
+            wb.keep[j] = (kin && rowv[j]) ? 0xFFFFFFFFu : 0u;
+        }
+    };
+    WBlock w0, w1, w2;
+    load_block(w0, 0);
+    load_block(w1, 1);
+
+    // ---- stage X[row][kbase .. kbase + 32 * nsteps) (rows past M read row 0: their outputs are never stored)
+    {
+        const int cpr = nsteps * 4;  // 16-byte chunks per row
+        const uint16_t* A = reinterpret_cast<const uint16_t*>(g.act);
+        for (int c = threadIdx.x; c < MT * 16 * cpr; c += 512) {
+            const int r = c / cpr, q = c - r * cpr;
+            const int m = r < g.M ? r : 0;
+            const uint4 v = *reinterpret_cast<const uint4*>(A + (long)m * g.act_ld + kbase + 8 * q);
+            *reinterpret_cast<uint4*>(xs + r * XLD + 8 * q) = v;
+        }
+    }
+    __syncthreads();
+
+    float4_t acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    unsigned char* my = slabs + wave * SLAB;
+    const int l16 = lane & 15, kq = lane >> 4;
+    auto multiply = [&](const WBlock& wb, int b) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 v = wb.v[j];
+            const uint32_t kp = wb.keep[j];
+            *reinterpret_cast<uint4*>(my + (4 * j + rr) * ROWB + 16 * cc) =
+                make_uint4(v.x & kp, v.y & kp, v.z & kp, v.w & kp);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int kk = 4 * b + s;
+            if (kk >= nsteps) break;  // X past the slice is not staged
+            Frag<DT> fa, fx;
+            fa.a = *reinterpret_cast<const uint4*>(my + l16 * ROWB + 64 * s + 16 * kq);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                fx.a = *reinterpret_cast<const uint4*>(xs + (mt * 16 + l16) * XLD + kk * 32 + kq * 8);
+                acc[mt] = frag_mma<DT>(fa, fx, acc[mt]);
+            }
+        }
+    };
+    // three blocks in the ring: while one is multiplied, the next two are in flight
+    const int nb = (nsteps + 3) / 4;
+    for (int b = 0; b < nb; b += 3) {
+        load_block(w2, b + 2);
+        __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of this multiply
+        multiply(w0, b);
+        if (b + 1 >= nb) break;
+        load_block(w0, b + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        multiply(w1, b + 1);
+        if (b + 2 >= nb) break;
+        load_block(w1, b + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        multiply(w2, b + 2);
+    }
+
+    // ---- partial sums: lane holds C[feature n0 + 4 kq + r][row 16 mt + l16], r = 0..3
+    const int n = n0 + 4 * kq;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + l16;
+        if (m >= g.M) continue;
+        float* dst = g.part + ((long)sl * g.M + m) * g.N + n;
+        if (n + 3 < g.N) {
+            *reinterpret_cast<float4_t*>(dst) = acc[mt];
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (n + r < g.N) dst[r] = acc[mt][r];
+        }
+    }
+}
+
+// x[m][n] += sum over slices of part[slice][m][n], slices in order; four features per thread.
+__global__ void __launch_bounds__(256) resid_reduce_kernel(float* __restrict__ x, int x_ld,
+                                                           const float* __restrict__ part, int n_slices, int M,
+                                                           int N) {
+    const long i4 = (long)blockIdx.x * 256 + threadIdx.x;  // index of a group of four features
+    const int groups = (N + 3) / 4;
+    if (i4 >= (long)M * groups) return;
+    const int m = (int)(i4 / groups), n = (int)(i4 - (long)m * groups) * 4;
+    const long plane = (long)M * N;
+    const float* src = part + (long)m * N + n;
+    if (n + 3 < N) {
+        float4_t s = *reinterpret_cast<const float4_t*>(src);
+        for (int sl = 1; sl < n_slices; ++sl) s += *reinterpret_cast<const float4_t*>(src + sl * plane);
+        float* xr = x + (long)m * x_ld + n;
+        xr[0] += s[0];
+        xr[1] += s[1];
+        xr[2] += s[2];
+        xr[3] += s[3];
+    } else {
+        for (int r = 0; r < 4 && n + r < N; ++r) {
+            float s = src[r];
+            for (int sl = 1; sl < n_slices; ++sl) s += src[sl * plane + r];
+            x[(long)m * x_ld + n + r] += s;
+        }
+    }
+}
+
+}  // namespace vs

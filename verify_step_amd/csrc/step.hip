@@ -11,6 +11,7 @@
 #include "common.h"
 #include "error.h"
 #include "gemm.h"
+#include "gemm_ksplit.h"
 #include "gemv.h"
 #include "misc.h"
 #include "sample.h"
@@ -62,6 +63,9 @@ void launch1(int kind, void (*kern)(T), dim3 grid, dim3 block, size_t lds, hipSt
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// slices of a split-K residual product with MT row blocks: every slice at most ks_slice(MT) elements
+int ks_slices(int K, int MT) { return (K / 32 + ks_slice(MT) / 32 - 1) / (ks_slice(MT) / 32); }
+
 int kv_elem_bytes(int dtype) { return dtype == VS_F32 ? 4 : (dtype == VS_FP8_E4M3 || dtype == VS_FP8_E5M2) ? 1 : 2; }
 
 // Rows of a step at which the row-streaming GEMV gives way to the MFMA tiles (beyond four rows the
@@ -83,10 +87,13 @@ constexpr int kGemvMergeUnits = 16;
 struct Plan {
     int B, M, M_log, D, H, Hkv, Dh, F, V, L, dt, esz;
     int n_splits, split_pages, rmax, attn_hg, attn_waves, rg_blocks;
+    bool ksplit;  // residual products through the split-K tile GEMM
+    int ks_slices;  // most slices of one of them (sizes the partial sums)
     bool gemv;      // the row-streaming path serves every product of the step
     bool merge_in_o; // the output product's prologue merges the key splits (no merge kernel)
     int n_lm_parts; // argmax partials per logit row
-    size_t off_row_seq, off_row_pos, off_rope, off_x, off_xn, off_q, off_attn, off_h, off_part, off_xf, off_lmpart;
+    size_t off_row_seq, off_row_pos, off_rope, off_x, off_xn, off_q, off_attn, off_h, off_part, off_xf, off_lmpart,
+        off_ksp;
     size_t total;
 };
 
@@ -168,6 +175,11 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->gemv = d->M <= kGemvMaxRows && (size_t)std::max(d->M, 1) * p->D * p->esz <= kGemvMaxLds;
     p->merge_in_o = p->gemv && p->n_splits > 1 && p->n_splits <= kMergeMaxSplits;
     p->n_lm_parts = p->gemv ? (p->V + gemv_units_per_wg(p->V) - 1) / gemv_units_per_wg(p->V) : (p->V + 15) / 16;
+    // 17..64 rows in fp16 / bf16: the output and down products split K over workgroups (up to 16 rows
+    // the 16-feature tiles read no more activation bytes than weight bytes)
+    p->ksplit = !p->gemv && p->dt != VS_F32 && d->M > 16 && d->M <= 64;
+    const int ks_mt = (std::max(d->M, 1) + 15) / 16;
+    p->ks_slices = std::max(ks_slices(p->H * p->Dh, ks_mt), ks_slices(p->F, ks_mt));
     const size_t M = (size_t)std::max(d->M, 1), ML = (size_t)std::max(d->M_log, 1);
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -186,6 +198,7 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->off_part = take(M * p->H * p->n_splits * part_stride(p->Dh) * 4);
     p->off_xf = take(ML * p->D * p->esz);
     p->off_lmpart = take(ML * p->n_lm_parts * sizeof(ArgPart));
+    p->off_ksp = take(p->ksplit ? (size_t)p->ks_slices * M * p->D * 4 : 4);
     p->total = o;
     return vs_ok();
 }
@@ -196,8 +209,38 @@ template <int DT, int MT, int EPI>
 void launch_gemm_mt(int kind, const GemmArgs& g, int NW, int n_mgroups, hipStream_t s) {
     constexpr int U = (DT == F32 ? 4 : 8) / MT > 0 ? (DT == F32 ? 4 : 8) / MT : 1;
     dim3 grid(n_mgroups, g.n_tiles);
-    if (NW >= 8) launch1(kind, gemm_skinny_kernel<DT, MT, 8, EPI, U>, grid, dim3(8 * 64), 0, s, g);
-    else launch1(kind, gemm_skinny_kernel<DT, MT, 4, EPI, U>, grid, dim3(4 * 64), 0, s, g);
+    // one row group streams the weights (nontemporal); several share them through the caches
+    if constexpr (DT != F32) {
+        if (n_mgroups == 1) {
+            if (NW >= 8) launch1(kind, gemm_skinny_kernel<DT, MT, 8, EPI, U, true>, grid, dim3(8 * 64), 0, s, g);
+            else launch1(kind, gemm_skinny_kernel<DT, MT, 4, EPI, U, true>, grid, dim3(4 * 64), 0, s, g);
+            return;
+        }
+    }
+    if (NW >= 8) launch1(kind, gemm_skinny_kernel<DT, MT, 8, EPI, U, false>, grid, dim3(8 * 64), 0, s, g);
+    else launch1(kind, gemm_skinny_kernel<DT, MT, 4, EPI, U, false>, grid, dim3(4 * 64), 0, s, g);
+}
+
+// x += W a for 5..64 rows: the split-K tile GEMM writes per-slice partial sums, then they are added
+// to x in slice order.
+template <int DT>
+void launch_resid_ksplit(int kind, const void* w, int N, int K, const void* act, int act_ld, int M, float* x,
+                         int x_ld, float* part, hipStream_t s) {
+    if constexpr (DT == F32) {
+        return;  // fp32 models keep the tile GEMM (the plan never selects this for them)
+    } else {
+    const KsplitArgs a{w, N, K, act, act_ld, M, ks_slices(K, (M + 15) / 16), part};
+    const dim3 grid((N + kKsRows - 1) / kKsRows, a.n_slices), block(512);
+    switch ((M + 15) / 16) {
+        case 1: launch1(kind, gemm_ksplit_kernel<DT, 1, true>, grid, block, 0, s, a); break;
+        case 2: launch1(kind, gemm_ksplit_kernel<DT, 2, true>, grid, block, 0, s, a); break;
+        case 3: launch1(kind, gemm_ksplit_kernel<DT, 3, true>, grid, block, 0, s, a); break;
+        default: launch1(kind, gemm_ksplit_kernel<DT, 4, true>, grid, block, 0, s, a); break;
+    }
+    const long groups = (long)M * ((N + 3) / 4);
+    hipLaunchKernelGGL(resid_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, x, x_ld, part,
+                       a.n_slices, M, N);
+    }
 }
 
 template <int DT, int EPI>
@@ -321,6 +364,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     float* part = reinterpret_cast<float*>(ws + p.off_part);
     void* xf = ws + p.off_xf;
     ArgPart* lmpart = reinterpret_cast<ArgPart*>(ws + p.off_lmpart);
+    float* ksp = reinterpret_cast<float*>(ws + p.off_ksp);
     const float eps = w->dims.eps;
 
     PrepArgs pa;
@@ -437,7 +481,10 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             o.n_tiles = (p.D + 15) / 16;
             o.x = x;
             o.x_ld = p.D;
-            launch_gemm<DT, EPI_RESID>(VS_KERNEL_OPROJ, o, s);
+            if (p.ksplit)
+                launch_resid_ksplit<DT>(VS_KERNEL_OPROJ, lw.wo, p.D, p.H * p.Dh, attn, p.H * p.Dh, p.M, x, p.D, ksp, s);
+            else
+                launch_gemm<DT, EPI_RESID>(VS_KERNEL_OPROJ, o, s);
         }
 
         // RMSNorm(x) -> silu(gate) * up
@@ -489,7 +536,10 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             dn.n_tiles = (p.D + 15) / 16;
             dn.x = x;
             dn.x_ld = p.D;
-            launch_gemm<DT, EPI_RESID>(VS_KERNEL_DOWN, dn, s);
+            if (p.ksplit)
+                launch_resid_ksplit<DT>(VS_KERNEL_DOWN, lw.wd, p.D, p.F, hmid, p.F, p.M, x, p.D, ksp, s);
+            else
+                launch_gemm<DT, EPI_RESID>(VS_KERNEL_DOWN, dn, s);
         }
     }
 
