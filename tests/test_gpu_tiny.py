@@ -230,6 +230,17 @@ def test_tiny_prefix_cache_hit_skips_the_shared_prefill(dtype):
     pool.close()
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_tiny_prompt_chunk_of_more_than_64_rows(dtype):
+    """A 100-row prompt chunk from position 0 beside a decode row and a 5-row verify pass (M = 106):
+    steps of more than 64 rows run their products, LM head included, on the LDS-tiled MFMA GEMM."""
+    _say(f"tiny 106-row step dtype={dtype}")
+    dims = W.TINY.with_dtype(dtype)
+    ctxs, k = [0, 30, 7], [100, 1, 5]
+    sb, ref, so, pool, rows = run_case(dims, ctxs, k, gains="random")
+    check_case(dims, sb, ref, so, pool, rows, ctxs, k)
+
+
 def test_tiny_rows_without_logits_and_long_context():
     """A long sequence spanning many splits, one sequence without logits, head_dim 128."""
     _say("tiny head_dim 128, long context, no-logit sequence")

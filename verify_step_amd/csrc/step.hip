@@ -11,6 +11,7 @@
 #include "common.h"
 #include "error.h"
 #include "gemm.h"
+#include "gemm_big.h"
 #include "gemm_ksplit.h"
 #include "gemv.h"
 #include "misc.h"
@@ -247,6 +248,14 @@ template <int DT, int EPI>
 void launch_gemm(int kind, const GemmArgs& g, hipStream_t s) {
     const int M = g.M;
     if (M <= 0) return;
+    if constexpr (DT != F32) {
+        // more than 64 rows (a prompt chunk): LDS-tiled MFMA GEMM, two feature tiles x 128 rows per workgroup
+        if (M > 64 && g.K % kBigK == 0) {
+            const dim3 grid((M + kBigRows - 1) / kBigRows, (g.n_tiles + 1) / 2);
+            launch1(kind, gemm_big_kernel<DT, EPI>, grid, dim3(256), 0, s, g);
+            return;
+        }
+    }
     const int MT = std::min((M + 15) / 16, 4);  // row blocks of 16 per group
     const int n_mgroups = (M + 16 * MT - 1) / (16 * MT);
     const long wgs = (long)g.n_tiles * n_mgroups;
