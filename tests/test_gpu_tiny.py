@@ -231,6 +231,20 @@ def test_tiny_prefix_cache_hit_skips_the_shared_prefill(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("heads,kv_heads,rows,ctxs", [(2, 2, [5, 16, 20], [100, 0, 37]),
+                                                     (8, 2, [1, 5, 2], [300, 17, 0]),
+                                                     (8, 1, [3, 1], [64, 250])])
+def test_tiny_matrix_core_attention(dtype, heads, kv_heads, rows, ctxs):
+    """Head dim 128 with several rows per sequence or grouped heads: attention runs on the matrix
+    cores, 16 (row, head) states per workgroup; 20 rows need two row groups, contexts span pages
+    and key splits, and a sequence with no cached context attends only within its rows."""
+    _say(f"tiny MFMA attention {heads}/{kv_heads} rows={rows} ctxs={ctxs} dtype={dtype}")
+    dims = W.ModelDims(f"tiny-dh128-{heads}x{kv_heads}", heads * 128, heads, kv_heads, 128, 1024, 1000, 1, dtype)
+    sb, ref, so, pool, rows_ = run_case(dims, ctxs, rows, gains="random")
+    check_case(dims, sb, ref, so, pool, rows_, ctxs, rows)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_tiny_prompt_chunk_of_more_than_64_rows(dtype):
     """A 100-row prompt chunk from position 0 beside a decode row and a 5-row verify pass (M = 106):
     steps of more than 64 rows run their products, LM head included, on the LDS-tiled MFMA GEMM."""

@@ -1,0 +1,279 @@
+// Paged split-KV attention on the matrix cores, for workgroups whose query
+// states share each K/V page: the rows of a verify pass or prompt chunk of one
+// sequence, times the query heads of one grouped K/V head (gfx950).
+//
+// Same method and outputs as attn_split_kernel ([KV Cache] sections 05 and 07;
+// [Serving Efficiency] section 31.4): pages read through the block table, an
+// online softmax per query state over each split of the keys, the splits'
+// (max, sum, output) statistics merged afterwards. Up to 16 states
+// (R rows x HG heads, state s = row s / HG, head s % HG) form the rows of MFMA
+// tiles; one 16-key page per wave step:
+//   scores   S[16 states][16 keys] = Q K^T: four MFMA 16x16x32 over the head
+//            dimension, q fragments held in registers for the whole split, K
+//            loaded from the page straight into B-operand layout;
+//   softmax  per state in fp32 (log2 domain), row reductions by DPP over the 16
+//            lanes that hold one state's 16 keys;
+//   output   O[16 states][128] += P V: eight MFMA 16x16x16 per term. P is
+//            carried as two storage-type terms (hi + lo, about 16 significant
+//            bits) transposed through a wave-private LDS tile; V is staged in a
+//            wave-private LDS tile and read back key-wise for the B operand.
+// A lane's output rows are the same four states as its score rows, so the
+// softmax rescale needs no exchange. The waves' states are merged through LDS
+// at the end of the split, in wave order.
+#pragma once
+
+#include "attention.h"
+#include "common.h"
+
+namespace vs {
+
+// maximum over the 16 lanes of each DPP row, the same result in every lane of the row
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// O(16 x 16) += A(16 x 16) B(16 x 16), operands as four storage-type elements per lane (raw bits)
+template <int DT>
+__device__ __forceinline__ float4_t mma16(uint2 a, uint2 b, float4_t acc) {
+    if constexpr (DT == F16)
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a), __builtin_bit_cast(half4_t, b),
+                                                     acc, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
+                                                         __builtin_bit_cast(short4_t, b), acc, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ float4_t mma32(uint4 a, uint4 b, float4_t acc) {
+    if constexpr (DT == F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b),
+                                                      acc, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                       acc, 0, 0, 0);
+}
+
+constexpr int kAmWaves = 4;
+constexpr int kAmDh = 128;
+constexpr int kAmPLd = 16 + 4;     // P tile row stride (elements)
+constexpr int kAmVLd = kAmDh + 8;  // V tile row stride (elements)
+
+// two 8-bit floats (bytes 0, 1 of a word, or 2, 3 with HI) widened to two storage-type elements packed
+// in one word. Every e4m3 and e5m2 value is exact in fp16 and in bf16, so no rounding is involved:
+// an e5m2 byte is the high byte of the binary16 of its value; otherwise the packed conversion to
+// fp32 is exact and bf16 keeps the upper half of each fp32, fp16 converts it (exactly).
+template <int DT, int KVT, bool HI>
+__device__ __forceinline__ uint32_t widen2(uint32_t word) {
+    typedef float float2_t __attribute__((ext_vector_type(2)));
+    if constexpr (KVT == E5M2 && DT == F16) {
+        return __builtin_amdgcn_perm(0u, word, HI ? 0x030C020Cu : 0x010C000Cu);
+    } else {
+        float2_t f;
+        if constexpr (KVT == E4M3) f = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, HI);
+        else f = __builtin_amdgcn_cvt_pk_f32_bf8((int)word, HI);
+        if constexpr (DT == BF16) {
+            return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+        } else {
+            return (uint32_t)St<F16>::from_f(f.x) | ((uint32_t)St<F16>::from_f(f.y) << 16);
+        }
+    }
+}
+
+// eight 8-bit floats (two words) widened to eight storage-type elements
+template <int DT, int KVT>
+__device__ __forceinline__ uint4 widen8(uint2 w) {
+    return make_uint4(widen2<DT, KVT, false>(w.x), widen2<DT, KVT, true>(w.x), widen2<DT, KVT, false>(w.y),
+                      widen2<DT, KVT, true>(w.y));
+}
+
+// Two waves per SIMD (at most 256 registers, no scratch): with one page in flight per wave, a
+// decode step's few states leave the kernel bound by load latency, and the second resident
+// workgroup is what hides it.
+template <int DT, int HG, int KVT>
+__global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a) {
+    constexpr int DH = kAmDh;
+    constexpr int R = 16 / HG;  // rows per group
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, kq = lane >> 4;
+    const int s = blockIdx.x, h0 = blockIdx.y * HG;
+    const int b = blockIdx.z % a.B, rgb = blockIdx.z / a.B;
+    const int hk = h0 / (a.n_heads / a.n_kv_heads);
+    const int r0 = min(max(a.q_start[b], 0), a.M);
+    const int Rn = min(max(a.q_start[b + 1] - r0, 0), a.M - r0);
+    const int ctx = max(a.ctx_len[b], 0);
+    const int T = a.page_tokens;
+    const int p_begin = s * a.split_pages;
+    const int* bt = a.block_tables + (long)b * a.max_blocks;
+    const long kofs = (long)a.layer * a.layer_elems + (long)hk * T * DH;
+    const long vofs = kofs + (long)a.n_kv_heads * T * DH;
+    const int QLD = a.n_heads * DH;
+    const unsigned char* kv = reinterpret_cast<const unsigned char*>(a.kv_base);
+    constexpr int KB = St<KVT>::bytes;
+    const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q);
+
+    __shared__ __align__(16) uint16_t pt[kAmWaves][2][16 * kAmPLd];  // P hi / lo, [state][key]
+    __shared__ __align__(16) uint16_t vt[kAmWaves][16 * kAmVLd];     // V page, [key][dim]
+    __shared__ float wst[kAmWaves][16][DH + 2];                      // per-wave (m, l, o) of each state
+
+    for (int rg = rgb * R; rg < Rn; rg += a.rg_blocks * R) {
+        const int nr = min(R, Rn - rg);
+        const int n_pages = min((ctx + rg + nr + T - 1) / T, a.max_blocks);
+        const int p_end = min(p_begin + a.split_pages, n_pages);
+        // q fragments (A operand of the scores): state l16, dims 8 kq + 32 step
+        uint4 qf[4];
+        {
+            const int i = l16 / HG, j = l16 % HG;
+            const bool ok = i < nr;
+            const long qrow = (long)(r0 + rg + (ok ? i : 0)) * QLD + (long)(h0 + j) * DH + 8 * kq;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const uint4 v = *reinterpret_cast<const uint4*>(qb + qrow + 32 * st);
+                qf[st] = ok ? v : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+        // this lane's four states (score and output rows): 4 kq + r
+        int qpos[4];
+        bool sv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = (4 * kq + r) / HG;
+            sv[r] = i < nr;
+            qpos[r] = ctx + rg + i;
+        }
+        float m[4], l[4];
+        float4_t o[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            m[r] = -INFINITY;
+            l[r] = 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o[t] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+        // K (B operand of the scores) and V of one page: key slot l16, dims 8 kq + 32 step
+        auto load_page = [&](uint4(&kk)[4], uint4(&vv)[4], int p) {
+            const long pb = (long)min(max(bt[p], 0), a.num_pages - 1) * a.page_elems + (long)l16 * DH + 8 * kq;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                if constexpr (KB == 2) {
+                    kk[st] = load_stream16(kv + (pb + kofs + 32 * st) * 2);
+                    vv[st] = load_stream16(kv + (pb + vofs + 32 * st) * 2);
+                } else {  // an 8-bit cache: eight values per lane, widened (exactly) to the storage type
+                    typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+                    const u32x2_t k8 = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(kv + pb + kofs + 32 * st));
+                    const u32x2_t v8 = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(kv + pb + vofs + 32 * st));
+                    kk[st] = widen8<DT, KVT>(make_uint2(k8.x, k8.y));
+                    vv[st] = widen8<DT, KVT>(make_uint2(v8.x, v8.y));
+                }
+            }
+        };
+        uint16_t* my_p = &pt[wave][0][0];
+        uint16_t* my_v = &vt[wave][0];
+        auto reduce_page = [&](const uint4(&kk)[4], const uint4(&vv)[4], int p) {
+            // V to LDS, natural layout [key][dim]
+#pragma unroll
+            for (int st = 0; st < 4; ++st) *reinterpret_cast<uint4*>(my_v + l16 * kAmVLd + 8 * kq + 32 * st) = vv[st];
+            __builtin_amdgcn_wave_barrier();
+            float4_t sc = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) sc = mma32<DT>(qf[st], kk[st], sc);
+            const int kp = p * T + l16;
+            float pr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = (sv[r] && kp <= qpos[r]) ? sc[r] * a.scale_log2 : -INFINITY;
+                const float mn = fmaxf(m[r], row16_max(x));
+                const float alpha = mn == -INFINITY ? 1.f : exp2f(m[r] - mn);
+                const float e = mn == -INFINITY ? 0.f : exp2f(x - mn);
+                l[r] = l[r] * alpha + row16_sum(e);
+                m[r] = mn;
+                pr[r] = e;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) o[t][r] *= alpha;
+            }
+            // P as hi + lo storage-type terms, transposed: [state 4 kq + r][key l16]
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint16_t hi = St<DT>::from_f(pr[r]);
+                const uint16_t lo = St<DT>::from_f(pr[r] - St<DT>::to_f(hi));
+                my_p[(4 * kq + r) * kAmPLd + l16] = hi;
+                my_p[16 * kAmPLd + (4 * kq + r) * kAmPLd + l16] = lo;
+            }
+            __builtin_amdgcn_wave_barrier();  // the wave's LDS writes above come before its reads below
+            const uint2 ph = *reinterpret_cast<const uint2*>(my_p + l16 * kAmPLd + 4 * kq);
+            const uint2 pl = *reinterpret_cast<const uint2*>(my_p + 16 * kAmPLd + l16 * kAmPLd + 4 * kq);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                // B operand: V[keys 4 kq .. +3][dim 16 t + l16]
+                const int d = 16 * t + l16;
+                const uint32_t v0 = my_v[(4 * kq + 0) * kAmVLd + d], v1 = my_v[(4 * kq + 1) * kAmVLd + d];
+                const uint32_t v2 = my_v[(4 * kq + 2) * kAmVLd + d], v3 = my_v[(4 * kq + 3) * kAmVLd + d];
+                const uint2 vb = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+                o[t] = mma16<DT>(ph, vb, o[t]);
+                o[t] = mma16<DT>(pl, vb, o[t]);
+            }
+        };
+        const int p0 = p_begin + wave;
+        uint4 ka[4], va[4], kb2[4], vb2[4];
+        if (p0 < p_end) load_page(ka, va, p0);
+        for (int p = p0; p < p_end; p += 2 * kAmWaves) {
+            if (p + kAmWaves < p_end) load_page(kb2, vb2, p + kAmWaves);
+            reduce_page(ka, va, p);
+            if (p + kAmWaves >= p_end) break;
+            if (p + 2 * kAmWaves < p_end) load_page(ka, va, p + 2 * kAmWaves);
+            reduce_page(kb2, vb2, p + kAmWaves);
+        }
+        // this wave's states to LDS: lane holds o[state 4 kq + r][dim 16 t + l16]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int st = 4 * kq + r;
+            if (l16 == 0) {
+                wst[wave][st][0] = m[r];
+                wst[wave][st][1] = l[r];
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) wst[wave][st][2 + 16 * t + l16] = o[t][r];
+        }
+        __syncthreads();
+        // merge the waves in wave order; thread t takes (state, dim) pairs of the valid states
+        for (int idx = tid; idx < nr * HG * DH; idx += kAmWaves * 64) {
+            const int st = idx / DH, d = idx % DH;
+            const int row = r0 + rg + st / HG, h = h0 + st % HG;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < kAmWaves; ++w) mx = fmaxf(mx, wst[w][st][0]);
+            float ls = 0.f, os = 0.f;
+            if (mx != -INFINITY) {
+#pragma unroll
+                for (int w = 0; w < kAmWaves; ++w) {
+                    const float wm = wst[w][st][0];
+                    if (wm == -INFINITY) continue;
+                    const float f = exp2f(wm - mx);
+                    ls += f * wst[w][st][1];
+                    os += f * wst[w][st][2 + d];
+                }
+            }
+            if (a.n_splits == 1) {
+                store_round<DT>(a.out, (long)row * a.n_heads * DH + (long)h * DH + d, safe_div(os, ls));
+            } else {
+                float* dst = a.part + (((long)row * a.n_heads + h) * a.n_splits + s) * part_stride(DH);
+                if (d == 0) {
+                    dst[0] = mx;
+                    dst[1] = ls;
+                }
+                dst[kPartO + d] = os;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace vs

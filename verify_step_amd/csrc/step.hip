@@ -8,6 +8,7 @@
 
 #include "../../include/verify_step.h"
 #include "attention.h"
+#include "attention_mfma.h"
 #include "common.h"
 #include "error.h"
 #include "gemm.h"
@@ -81,13 +82,16 @@ constexpr size_t kGemvPhaseLds = 64 * 1024;
 // and the workgroups the key splits aim for (one per CU).
 int attn_waves(int states, int dt) { return states == 1 || (states == 2 && dt != VS_F32) ? 8 : 4; }
 constexpr long kAttnTargetWaves = 2048;  // eight-wave workgroups: 256 (one per CU)
-constexpr long kAttnTargetWgsFew = 512;  // four-wave workgroups (several rows per sequence): two per CU
+// four-wave workgroups (several rows per sequence, matrix-core attention): two per CU (for the
+// matrix-core kernel, measured: more splits only add the per-split start-up)
+constexpr long kAttnTargetWgsFew = 512;
 // Output units per workgroup of the output GEMV when it merges the key splits itself.
 constexpr int kGemvMergeUnits = 16;
 
 struct Plan {
     int B, M, M_log, D, H, Hkv, Dh, F, V, L, dt, esz;
     int n_splits, split_pages, rmax, attn_hg, attn_waves, rg_blocks;
+    bool attn_mfma;  // matrix-core attention: up to 16 (row, head) states per workgroup
     bool ksplit;  // residual products through the split-K tile GEMM
     int ks_slices;  // most slices of one of them (sizes the partial sums)
     bool gemv;      // the row-streaming path serves every product of the step
@@ -161,6 +165,20 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
         }
     }
     p->attn_waves = attn_waves(p->rmax * p->attn_hg, m->dtype);
+    {
+        // several rows per sequence or grouped heads (fp16 / bf16, head_dim 128): the states that share
+        // each page run as MFMA tiles of 16: HG heads of one K/V group (the largest power of two up to
+        // 16 dividing the group) x 16 / HG rows
+        const int group = m->n_heads / m->n_kv_heads;
+        p->attn_mfma = m->dtype != VS_F32 && m->head_dim == kAmDh && (d->max_rows >= 2 || group >= 2);
+        if (p->attn_mfma) {
+            int hg = 1;
+            while (hg < 16 && group % (2 * hg) == 0) hg *= 2;
+            p->attn_hg = hg;
+            p->rmax = 16 / hg;
+            p->attn_waves = kAmWaves;
+        }
+    }
     const int max_pages = (d->max_ctx + kPageTokens - 1) / kPageTokens;
     // row groups of a sequence go to separate workgroups (a prompt chunk's groups run in parallel)
     const int rg_needed = (d->max_rows + p->rmax - 1) / p->rmax;
@@ -328,9 +346,32 @@ void launch_attention_kv(const AttnArgs& a, int B, int M, int rmax, int hg, bool
 
 // The cache's storage type picks the K/V loads: the model's type, or (fp16 / bf16 models with
 // head_dim 128) an 8-bit float.
+// Matrix-core attention: grid (splits, head groups of HG, sequences x row-group blocks).
+template <int DT, int KVT>
+void launch_attention_mfma(const AttnArgs& a, int B, int hg, hipStream_t s) {
+    const dim3 grid(a.n_splits, a.n_heads / hg, B * a.rg_blocks), block(kAmWaves * 64);
+    switch (hg) {
+        case 1: launch1(VS_KERNEL_ATTN, attn_mfma_kernel<DT, 1, KVT>, grid, block, 0, s, a); break;
+        case 2: launch1(VS_KERNEL_ATTN, attn_mfma_kernel<DT, 2, KVT>, grid, block, 0, s, a); break;
+        case 4: launch1(VS_KERNEL_ATTN, attn_mfma_kernel<DT, 4, KVT>, grid, block, 0, s, a); break;
+        case 8: launch1(VS_KERNEL_ATTN, attn_mfma_kernel<DT, 8, KVT>, grid, block, 0, s, a); break;
+        default: launch1(VS_KERNEL_ATTN, attn_mfma_kernel<DT, 16, KVT>, grid, block, 0, s, a); break;
+    }
+}
+
 template <int DT, int DH>
-void launch_attention(const AttnArgs& a, int B, int M, int rmax, int hg, int kv_dt, bool merge_kernel,
+void launch_attention(const AttnArgs& a, int B, int M, int rmax, int hg, int kv_dt, bool merge_kernel, bool mfma,
                       hipStream_t s) {
+    if constexpr (DT != F32 && DH == kAmDh) {
+        if (mfma) {
+            if (kv_dt == E4M3) launch_attention_mfma<DT, E4M3>(a, B, hg, s);
+            else if (kv_dt == E5M2) launch_attention_mfma<DT, E5M2>(a, B, hg, s);
+            else launch_attention_mfma<DT, DT>(a, B, hg, s);
+            if (merge_kernel && a.n_splits > 1)
+                launch1(VS_KERNEL_MERGE, attn_merge_kernel<DT, DH>, dim3(M, a.n_heads), dim3(DH), 0, s, a);
+            return;
+        }
+    }
     if constexpr (DT != F32 && DH == 128) {
         if (kv_dt == E4M3) return launch_attention_kv<DT, DH, E4M3>(a, B, M, rmax, hg, merge_kernel, s);
         if (kv_dt == E5M2) return launch_attention_kv<DT, DH, E5M2>(a, B, M, rmax, hg, merge_kernel, s);
@@ -459,8 +500,10 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
         }
 
         a.layer = l;
-        if (p.Dh == 128) launch_attention<DT, 128>(a, p.B, p.M, p.rmax, p.attn_hg, pg->dtype, !p.merge_in_o, s);
-        else launch_attention<DT, 64>(a, p.B, p.M, p.rmax, p.attn_hg, pg->dtype, !p.merge_in_o, s);
+        if (p.Dh == 128)
+            launch_attention<DT, 128>(a, p.B, p.M, p.rmax, p.attn_hg, pg->dtype, !p.merge_in_o, p.attn_mfma, s);
+        else
+            launch_attention<DT, 64>(a, p.B, p.M, p.rmax, p.attn_hg, pg->dtype, !p.merge_in_o, p.attn_mfma, s);
 
         // x += W_o attn
         if (p.gemv) {
