@@ -12,7 +12,8 @@
 // wave-private LDS slab (read back as MFMA A fragments), two 128-element blocks
 // ahead of the multiply. Workgroups along the reduction write fp32 partial sums
 // [slice][row][feature]; resid_reduce_kernel adds them to x in slice order, so
-// the result does not depend on timing.
+// the result does not depend on timing (resid_norm_kernel does the same and also
+// writes the RMSNorm of the new x that the next product reads).
 #pragma once
 
 #include "common.h"
@@ -177,6 +178,61 @@ __global__ void __launch_bounds__(256) resid_reduce_kernel(float* __restrict__ x
             for (int sl = 1; sl < n_slices; ++sl) s += src[sl * plane + r];
             x[(long)m * x_ld + n + r] += s;
         }
+    }
+}
+
+// The residual add above fused with the RMSNorm that reads its result (in the pre-norm block of
+// [KV Cache] section 03 every residual add is followed by the next sublayer's RMSNorm): for one
+// row m per workgroup, x[m] += sum over slices of part[slice][m] (slices in order, as resid_reduce_kernel),
+// then y[m] = round(x[m] / sqrt(mean(x[m]^2) + eps) * gain). A step's few rows leave few
+// workgroups, so every thread keeps its four features' partial sums of all slices in flight at
+// once; the mean of squares is summed in a fixed order (per thread, then per wave, then over the
+// waves in order). D must be a multiple of 4.
+template <int DT>
+__global__ void __launch_bounds__(1024) resid_norm_kernel(float* __restrict__ x, const float* __restrict__ part,
+                                                          int n_slices, int M, int D, const void* gain, float eps,
+                                                          void* y) {
+    const int m = blockIdx.x, tid = threadIdx.x;
+    const long plane = (long)M * D;
+    float* xr = x + (long)m * D;
+    float ss = 0.f;
+    for (int k = tid * 4; k < D; k += 1024 * 4) {
+        const float* src = part + (long)m * D + k;
+        // twelve slices' loads at a time, all issued before the first add (the slice index is clamped
+        // instead of branched around, so none of them waits for another)
+        float4_t s = (float4_t){0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < n_slices; s0 += 12) {
+            float4_t v[12];
+#pragma unroll
+            for (int j = 0; j < 12; ++j)
+                v[j] = *reinterpret_cast<const float4_t*>(src + min(s0 + j, n_slices - 1) * plane);
+#pragma unroll
+            for (int j = 0; j < 12; ++j)
+                if (s0 + j < n_slices) s = s0 + j == 0 ? v[j] : s + v[j];
+        }
+        float4_t v = *reinterpret_cast<const float4_t*>(xr + k);
+        v[0] += s[0];
+        v[1] += s[1];
+        v[2] += s[2];
+        v[3] += s[3];
+        *reinterpret_cast<float4_t*>(xr + k) = v;
+        ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    }
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) ss += shfl_xor(ss, mask);
+    __shared__ float wsum[16];
+    if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) tot += wsum[w];
+    const float inv = 1.0f / sqrtf(tot / (float)D + eps);
+    for (int k = tid * 4; k < D; k += 1024 * 4) {
+        const float4_t v = *reinterpret_cast<const float4_t*>(xr + k);  // this thread's own writes above
+        float gv[4];
+        load_widen<DT, 4>(reinterpret_cast<const char*>(gain) + (long)k * St<DT>::bytes, gv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_round<DT>(y, (long)m * D + k + e, v[e] * inv * gv[e]);
     }
 }
 

@@ -241,10 +241,12 @@ void launch_gemm_mt(int kind, const GemmArgs& g, int NW, int n_mgroups, hipStrea
 }
 
 // x += W a for 5..64 rows: the split-K tile GEMM writes per-slice partial sums, then they are added
-// to x in slice order.
+// to x in slice order. With a gain, the same kernel that adds them also writes RMSNorm(x) * gain to
+// y (x rows of exactly N features).
 template <int DT>
 void launch_resid_ksplit(int kind, const void* w, int N, int K, const void* act, int act_ld, int M, float* x,
-                         int x_ld, float* part, hipStream_t s) {
+                         int x_ld, float* part, hipStream_t s, const void* gain = nullptr, float eps = 0.f,
+                         void* y = nullptr) {
     if constexpr (DT == F32) {
         return;  // fp32 models keep the tile GEMM (the plan never selects this for them)
     } else {
@@ -256,9 +258,13 @@ void launch_resid_ksplit(int kind, const void* w, int N, int K, const void* act,
         case 3: launch1(kind, gemm_ksplit_kernel<DT, 3, true>, grid, block, 0, s, a); break;
         default: launch1(kind, gemm_ksplit_kernel<DT, 4, true>, grid, block, 0, s, a); break;
     }
-    const long groups = (long)M * ((N + 3) / 4);
-    hipLaunchKernelGGL(resid_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, x, x_ld, part,
-                       a.n_slices, M, N);
+    if (gain) {
+        hipLaunchKernelGGL((resid_norm_kernel<DT>), dim3(M), dim3(1024), 0, s, x, part, a.n_slices, M, N, gain, eps, y);
+    } else {
+        const long groups = (long)M * ((N + 3) / 4);
+        hipLaunchKernelGGL(resid_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, x, x_ld,
+                           part, a.n_slices, M, N);
+    }
     }
 }
 
@@ -466,6 +472,9 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     a.part = part;
     a.out = attn;
 
+    // the split-K residual products hand the next RMSNorm's output over in xn (fused into their
+    // partial-sum reduction): the norm ahead of the next product is then already done
+    bool xn_ready = false;
     for (int l = 0; l < p.L; ++l) {
         const vs_layer_weights& lw = w->layers[l];
         // RMSNorm(x) -> q, k, v; rotary; K/V into the pages
@@ -481,8 +490,10 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             q.n_units = (p.H + 2 * p.Hkv) * p.Dh / 2;
             launch_gemv<DT, X_NORM, EPI_QKV>(VS_KERNEL_QKV, q, s);
         } else {
-            hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
-                               lw.attn_norm, p.D, eps, xn);
+            if (!xn_ready)
+                hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
+                                   lw.attn_norm, p.D, eps, xn);
+            xn_ready = false;
             GemmArgs q = gm;
             q.w0 = lw.wq;
             q.w1 = lw.wk;
@@ -533,9 +544,11 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             o.n_tiles = (p.D + 15) / 16;
             o.x = x;
             o.x_ld = p.D;
-            if (p.ksplit)
-                launch_resid_ksplit<DT>(VS_KERNEL_OPROJ, lw.wo, p.D, p.H * p.Dh, attn, p.H * p.Dh, p.M, x, p.D, ksp, s);
-            else
+            if (p.ksplit) {
+                launch_resid_ksplit<DT>(VS_KERNEL_OPROJ, lw.wo, p.D, p.H * p.Dh, attn, p.H * p.Dh, p.M, x, p.D, ksp, s,
+                                        lw.ffn_norm, eps, xn);
+                xn_ready = true;
+            } else
                 launch_gemm<DT, EPI_RESID>(VS_KERNEL_OPROJ, o, s);
         }
 
@@ -551,8 +564,10 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             gu.n_units = p.F;
             launch_gemv<DT, X_NORM, EPI_SWIGLU>(VS_KERNEL_GATEUP, gu, s);
         } else {
-            hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
-                               lw.ffn_norm, p.D, eps, xn);
+            if (!xn_ready)
+                hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
+                                   lw.ffn_norm, p.D, eps, xn);
+            xn_ready = false;
             GemmArgs gu = gm;
             gu.w0 = lw.wg;
             gu.w1 = lw.wu;
@@ -588,9 +603,13 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             dn.n_tiles = (p.D + 15) / 16;
             dn.x = x;
             dn.x_ld = p.D;
-            if (p.ksplit)
+            if (p.ksplit && l + 1 < p.L) {
+                launch_resid_ksplit<DT>(VS_KERNEL_DOWN, lw.wd, p.D, p.F, hmid, p.F, p.M, x, p.D, ksp, s,
+                                        w->layers[l + 1].attn_norm, eps, xn);
+                xn_ready = true;
+            } else if (p.ksplit) {
                 launch_resid_ksplit<DT>(VS_KERNEL_DOWN, lw.wd, p.D, p.F, hmid, p.F, p.M, x, p.D, ksp, s);
-            else
+            } else
                 launch_gemm<DT, EPI_RESID>(VS_KERNEL_DOWN, dn, s);
         }
     }
