@@ -168,28 +168,41 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
                 m[st] = mn;
             }
         };
+        // Every load in the ring is unconditional (a page past the split re-reads the split's last
+        // page, and is never reduced): with a branch around a load the compiler can only wait for
+        // all outstanding loads, the pages in flight included.
         const int p0 = p_begin + wave;
-        if constexpr (NS >= 4) {  // many states: a ring of two pages leaves registers for them
-            if (p0 < p_end) load_page(ka, va, p0);
-            for (int p = p0; p < p_end; p += 2 * NW) {
-                if (p + NW < p_end) load_page(kb, vb, p + NW);
-                reduce_page(ka, va, p);
-                if (p + NW >= p_end) break;
-                if (p + 2 * NW < p_end) load_page(ka, va, p + 2 * NW);
-                reduce_page(kb, vb, p + NW);
-            }
-        } else {
-            if (p0 < p_end) load_page(ka, va, p0);
-            if (p0 + NW < p_end) load_page(kb, vb, p0 + NW);
-            for (int p = p0; p < p_end; p += 3 * NW) {
-                if (p + 2 * NW < p_end) load_page(kc, vc, p + 2 * NW);
-                reduce_page(ka, va, p);
-                if (p + NW >= p_end) break;
-                if (p + 3 * NW < p_end) load_page(ka, va, p + 3 * NW);
-                reduce_page(kb, vb, p + NW);
-                if (p + 2 * NW >= p_end) break;
-                if (p + 4 * NW < p_end) load_page(kb, vb, p + 4 * NW);
-                reduce_page(kc, vc, p + 2 * NW);
+        const int plast = p_end - 1;
+        if (p0 < p_end) {
+            if constexpr (NS >= 4) {  // many states: a ring of two pages leaves registers for them
+                load_page(ka, va, p0);
+                for (int p = p0;; p += 2 * NW) {
+                    load_page(kb, vb, min(p + NW, plast));
+                    __builtin_amdgcn_sched_barrier(0);  // the next page's loads stay ahead of this reduction
+                    reduce_page(ka, va, p);
+                    if (p + NW >= p_end) break;
+                    load_page(ka, va, min(p + 2 * NW, plast));
+                    __builtin_amdgcn_sched_barrier(0);
+                    reduce_page(kb, vb, p + NW);
+                    if (p + 2 * NW >= p_end) break;
+                }
+            } else {
+                load_page(ka, va, p0);
+                load_page(kb, vb, min(p0 + NW, plast));
+                for (int p = p0;; p += 3 * NW) {
+                    load_page(kc, vc, min(p + 2 * NW, plast));
+                    __builtin_amdgcn_sched_barrier(0);
+                    reduce_page(ka, va, p);
+                    if (p + NW >= p_end) break;
+                    load_page(ka, va, min(p + 3 * NW, plast));
+                    __builtin_amdgcn_sched_barrier(0);
+                    reduce_page(kb, vb, p + NW);
+                    if (p + 2 * NW >= p_end) break;
+                    load_page(kb, vb, min(p + 4 * NW, plast));
+                    __builtin_amdgcn_sched_barrier(0);
+                    reduce_page(kc, vc, p + 2 * NW);
+                    if (p + 3 * NW >= p_end) break;
+                }
             }
         }
         // this wave's state: merge the four key slots' states (rescaled to their common maximum),

@@ -221,15 +221,24 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
                 o[t] = mma16<DT>(pl, vb, o[t]);
             }
         };
+        // a ring of two pages per wave. Every load in the loop is unconditional (a page past the
+        // split re-reads the split's last page, and is never reduced): with a branch around a load
+        // the compiler can only wait for all outstanding loads, the one in flight included.
         const int p0 = p_begin + wave;
-        uint4 ka[4], va[4], kb2[4], vb2[4];
-        if (p0 < p_end) load_page(ka, va, p0);
-        for (int p = p0; p < p_end; p += 2 * kAmWaves) {
-            if (p + kAmWaves < p_end) load_page(kb2, vb2, p + kAmWaves);
-            reduce_page(ka, va, p);
-            if (p + kAmWaves >= p_end) break;
-            if (p + 2 * kAmWaves < p_end) load_page(ka, va, p + 2 * kAmWaves);
-            reduce_page(kb2, vb2, p + kAmWaves);
+        if (p0 < p_end) {
+            const int plast = p_end - 1;
+            uint4 ka[4], va[4], kb2[4], vb2[4];
+            load_page(ka, va, p0);
+            for (int p = p0;; p += 2 * kAmWaves) {
+                load_page(kb2, vb2, min(p + kAmWaves, plast));
+                __builtin_amdgcn_sched_barrier(0);  // the next page's loads stay ahead of this reduction
+                reduce_page(ka, va, p);
+                if (p + kAmWaves >= p_end) break;
+                load_page(ka, va, min(p + 2 * kAmWaves, plast));
+                __builtin_amdgcn_sched_barrier(0);
+                reduce_page(kb2, vb2, p + kAmWaves);
+                if (p + 2 * kAmWaves >= p_end) break;
+            }
         }
         // this wave's states to LDS: lane holds o[state 4 kq + r][dim 16 t + l16]
 #pragma unroll
