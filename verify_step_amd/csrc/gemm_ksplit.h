@@ -3,14 +3,16 @@
 //
 // x[m][n] += sum_k X[m][k] * W[n][k] ([KV Cache] section 02: every row passing
 // through a weight matrix shares one read of it). A workgroup of 8 waves owns
-// 128 output features (16 per wave) and one slice of at most 512 reduction
-// elements. It stages its slice of all the step's rows (X) in LDS once, with
-// coalesced loads, and every wave reads its MFMA B fragments from there: the
-// activation bytes fetched from L2 are 1/8 of what a 16-feature tile per
+// one slice of at most 512 reduction elements and a run of consecutive blocks
+// of 128 output features (16 per wave per block). It stages its slice of all
+// the step's rows (X) in LDS once, with coalesced loads, and every wave reads
+// its MFMA B fragments from there for every block of the run: the activation
+// bytes fetched from L2 are 1/8 (or less) of what a 16-feature tile per
 // workgroup would fetch, where they cost as much as the weight stream itself.
 // Each wave streams its 16 weight rows four rows x 256 bytes per load through a
 // wave-private LDS slab (read back as MFMA A fragments), two 128-element blocks
-// ahead of the multiply. Workgroups along the reduction write fp32 partial sums
+// ahead of the multiply; the stream runs on from one feature block to the next,
+// so a run of blocks pays the workgroup's start (X staging, first loads) once. Workgroups along the reduction write fp32 partial sums
 // [slice][row][feature]; resid_reduce_kernel adds them to x in slice order, so
 // the result does not depend on timing (resid_norm_kernel does the same and also
 // writes the RMSNorm of the new x that the next product reads).
@@ -27,6 +29,11 @@ constexpr int kKsXPad = 8;    // LDS row padding (elements): a fragment's 16 row
 // 4096-feature products, shorter ones add partial sums)
 __host__ __device__ constexpr int ks_slice(int) { return 512; }
 
+// LDS of one workgroup (X slice + eight weight slabs), for the workgroups a CU can hold
+__host__ __device__ constexpr int ks_lds_bytes(int MT) {
+    return MT * 16 * (ks_slice(MT) + kKsXPad) * 2 + 8 * 16 * (256 + 16);
+}
+
 struct KsplitArgs {
     const void* w;  // [N][K] storage type
     int N, K;       // K a multiple of 32
@@ -34,6 +41,7 @@ struct KsplitArgs {
     int act_ld, M;    // M <= 16 * MT
     int n_slices;     // workgroups along K (gridDim.y); every slice holds at most ks_slice(MT) elements
     float* part;      // [n_slices][M][N] fp32
+    int fb_per_wg;    // 128-feature blocks per workgroup (gridDim.x = ceil(ceil(N / 128) / fb_per_wg))
 };
 
 template <int DT, int MT, bool STREAM>
@@ -41,41 +49,43 @@ __global__ void __launch_bounds__(512) gemm_ksplit_kernel(KsplitArgs g) {
     constexpr int ROWB = 256 + 16;  // slab row stride in bytes
     constexpr int SLAB = 16 * ROWB;
     constexpr int XLD = ks_slice(MT) + kKsXPad;  // X row stride in LDS, elements
+    static_assert(MT * 16 * XLD * 2 + 8 * SLAB == ks_lds_bytes(MT), "LDS size");
     __shared__ __align__(16) uint16_t xs[MT * 16 * XLD];
     __shared__ __align__(16) unsigned char slabs[8 * SLAB];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n0 = blockIdx.x * kKsRows + wave * 16;
+    const int fb0 = blockIdx.x * g.fb_per_wg;  // this workgroup's feature blocks fb0 .. fb0 + nfb - 1
+    const int nfb = min(g.fb_per_wg, (g.N + kKsRows - 1) / kKsRows - fb0);
     const int sl = blockIdx.y;
     const int KC = g.K / 32;
     const int c0 = (int)(((long)sl * KC) / g.n_slices), c1 = (int)(((long)(sl + 1) * KC) / g.n_slices);
     const int nsteps = c1 - c0;  // 32-element steps of this slice (<= ks_slice(MT) / 32)
     const long kbase = (long)c0 * 32;
 
-    // ---- weights: 16 rows of this wave, blocks of 128 elements (4 steps), R4 layout
+    // ---- weights: 16 rows of this wave per feature block, blocks of 128 elements (4 steps), R4 layout.
+    // The wave's stream is the sequence q = (feature block i, K block b) = (q / nb, q % nb).
+    const int nb = (nsteps + 3) / 4;  // K blocks per feature block
+    const int total = nfb * nb;
     const int rr = lane >> 4, cc = lane & 15;
-    long rowoff[4];
-    bool rowv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = n0 + 4 * j + rr;
-        rowv[j] = row < g.N;
-        rowoff[j] = (long)(rowv[j] ? row : 0) * g.K + kbase + 8 * cc;
-    }
     const uint16_t* W = reinterpret_cast<const uint16_t*>(g.w);
     struct WBlock {
         uint4 v[4];
         uint32_t keep[4];
     };
-    // out-of-slice steps read their row's first chunk and are zeroed on the way into the slab
-    auto load_block = [&](WBlock& wb, int b) {
-        const bool kin = 4 * b + (cc >> 2) < nsteps;
-        const long ko = kin ? (long)b * 128 : -(long)(8 * cc) - kbase;
+    // steps past the slice or the stream read their row's first chunk (rows past N: row 0) and are
+    // zeroed on the way into the slab
+    auto load_block = [&](WBlock& wb, int q) {
+        const int i = min(q / nb, nfb - 1), b = q - (q / nb) * nb;
+        const bool kin = q < total && 4 * b + (cc >> 2) < nsteps;
+        const long ko = kin ? (long)b * 128 : 0;
+        const int n0 = (fb0 + i) * kKsRows + wave * 16;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint16_t* src = W + rowoff[j] + ko;
+            const int row = n0 + 4 * j + rr;
+            const bool rv = row < g.N;
+            const uint16_t* src = W + (long)(rv ? row : 0) * g.K + (kin ? kbase + 8 * cc + ko : 0);
             wb.v[j] = STREAM ? load_stream16(src) : *reinterpret_cast<const uint4*>(src);
-            wb.keep[j] = (kin && rowv[j]) ? 0xFFFFFFFFu : 0u;
+            wb.keep[j] = (kin && rv) ? 0xFFFFFFFFu : 0u;
         }
     };
     WBlock w0, w1, w2;
@@ -98,6 +108,26 @@ __global__ void __launch_bounds__(512) gemm_ksplit_kernel(KsplitArgs g) {
     float4_t acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    // partial sums of feature block i, then a fresh accumulator: lane holds
+    // C[feature n0 + 4 kq + r][row 16 mt + l16], r = 0..3
+    auto flush = [&](int i) {
+        const int n = (fb0 + i) * kKsRows + wave * 16 + 4 * (lane >> 4);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = mt * 16 + (lane & 15);
+            if (m < g.M) {
+                float* dst = g.part + ((long)sl * g.M + m) * g.N + n;
+                if (n + 3 < g.N) {
+                    *reinterpret_cast<float4_t*>(dst) = acc[mt];
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < g.N) dst[r] = acc[mt][r];
+                }
+            }
+            acc[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        }
+    };
     unsigned char* my = slabs + wave * SLAB;
     const int l16 = lane & 15, kq = lane >> 4;
     auto multiply = [&](const WBlock& wb, int b) {
@@ -121,36 +151,25 @@ __global__ void __launch_bounds__(512) gemm_ksplit_kernel(KsplitArgs g) {
             }
         }
     };
+    // multiply stream element q; after a feature block's last K block, write its partial sums
+    auto step = [&](const WBlock& wb, int q) {
+        const int i = q / nb, b = q - i * nb;
+        multiply(wb, b);
+        if (b == nb - 1) flush(i);
+    };
     // three blocks in the ring: while one is multiplied, the next two are in flight
-    const int nb = (nsteps + 3) / 4;
-    for (int b = 0; b < nb; b += 3) {
-        load_block(w2, b + 2);
+    for (int q = 0; q < total; q += 3) {
+        load_block(w2, q + 2);
         __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of this multiply
-        multiply(w0, b);
-        if (b + 1 >= nb) break;
-        load_block(w0, b + 3);
+        step(w0, q);
+        if (q + 1 >= total) break;
+        load_block(w0, q + 3);
         __builtin_amdgcn_sched_barrier(0);
-        multiply(w1, b + 1);
-        if (b + 2 >= nb) break;
-        load_block(w1, b + 4);
+        step(w1, q + 1);
+        if (q + 2 >= total) break;
+        load_block(w1, q + 4);
         __builtin_amdgcn_sched_barrier(0);
-        multiply(w2, b + 2);
-    }
-
-    // ---- partial sums: lane holds C[feature n0 + 4 kq + r][row 16 mt + l16], r = 0..3
-    const int n = n0 + 4 * kq;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + l16;
-        if (m >= g.M) continue;
-        float* dst = g.part + ((long)sl * g.M + m) * g.N + n;
-        if (n + 3 < g.N) {
-            *reinterpret_cast<float4_t*>(dst) = acc[mt];
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (n + r < g.N) dst[r] = acc[mt][r];
-        }
+        step(w2, q + 2);
     }
 }
 

@@ -85,6 +85,9 @@ constexpr long kAttnTargetWaves = 2048;  // eight-wave workgroups: 256 (one per 
 // four-wave workgroups (several rows per sequence, matrix-core attention): two per CU (for the
 // matrix-core kernel, measured: more splits only add the per-split start-up)
 constexpr long kAttnTargetWgsFew = 512;
+// The chip: 256 CUs of 160 KB LDS (MI355X).
+constexpr int kNumCUs = 256;
+constexpr int kLdsPerCu = 160 * 1024;
 // Output units per workgroup of the output GEMV when it merges the key splits itself.
 constexpr int kGemvMergeUnits = 16;
 
@@ -250,8 +253,14 @@ void launch_resid_ksplit(int kind, const void* w, int N, int K, const void* act,
     if constexpr (DT == F32) {
         return;  // fp32 models keep the tile GEMM (the plan never selects this for them)
     } else {
-    const KsplitArgs a{w, N, K, act, act_ld, M, ks_slices(K, (M + 15) / 16), part};
-    const dim3 grid((N + kKsRows - 1) / kKsRows, a.n_slices), block(512);
+    // each workgroup takes a run of feature blocks, so that the grid is about one round of the
+    // workgroups the CUs hold (the start of a workgroup, X staging and the first loads, is paid
+    // once per run)
+    const int MT = (M + 15) / 16, nblk = (N + kKsRows - 1) / kKsRows, slices = ks_slices(K, MT);
+    const long resident = (long)kNumCUs * std::max(1, (int)(kLdsPerCu / ks_lds_bytes(MT)));
+    const int fb = (int)std::max<long>(1, ((long)nblk * slices + resident - 1) / resident);
+    const KsplitArgs a{w, N, K, act, act_ld, M, slices, part, fb};
+    const dim3 grid((nblk + fb - 1) / fb, a.n_slices), block(512);
     switch ((M + 15) / 16) {
         case 1: launch1(kind, gemm_ksplit_kernel<DT, 1, true>, grid, block, 0, s, a); break;
         case 2: launch1(kind, gemm_ksplit_kernel<DT, 2, true>, grid, block, 0, s, a); break;
