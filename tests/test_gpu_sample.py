@@ -170,6 +170,14 @@ def test_verify_sample_matches_oracle_full_vocab(B, K, std):
     _check_case(case, f"V=32000 B={B} K={K} std={std}", min_exact=0.85 if std >= 4 else 0.0)
 
 
+def test_verify_sample_vocabulary_past_the_vector_path():
+    """A 152064-token vocabulary (more than 16 x 8192): chunks of 32 tokens take the scalar path;
+    and a vocabulary that is not a multiple of four (151939) takes unaligned scalar loads."""
+    for V in (152064, 151939):
+        case = Case(V, B=6, V=V, K_lo=0, K_hi=3, std=4.0, corr=0.6)
+        _check_case(case, f"V={V}", min_exact=0.6)
+
+
 def test_verify_sample_edge_cases():
     # no draft rows at all: every token drawn from p_0
     case = Case(1, B=5, V=300, K_lo=0, K_hi=0)
