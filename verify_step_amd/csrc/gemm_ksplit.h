@@ -1,5 +1,7 @@
-// Split-K tile GEMM for the residual products (attention output and MLP down
-// projections) of steps with 17..64 rows (gfx950).
+// Split-K tile GEMM for the weight products of steps with 17..64 rows (gfx950),
+// with the reductions that finish them: the residual products (attention output,
+// MLP down) add their sums to x, the q/k/v and gate/up products run their
+// epilogues on the summed values.
 //
 // x[m][n] += sum_k X[m][k] * W[n][k] ([KV Cache] section 02: every row passing
 // through a weight matrix shares one read of it). A workgroup of 8 waves owns
@@ -35,7 +37,13 @@ __host__ __device__ constexpr int ks_lds_bytes(int MT) {
 }
 
 struct KsplitArgs {
-    const void* w;  // [N][K] storage type
+    // W [N][K] in the storage type, up to three segments stacked along N: rows [0, n0) of w0,
+    // then [n0, n0 + n1) of w1, then the rest of w2 (one matrix: n0 = N, w1 = w2 = w0). n0 and
+    // n1 are multiples of 128, so that no block of 128 features spans two segments.
+    const void* w0;
+    const void* w1;
+    const void* w2;
+    int n0, n1;
     int N, K;       // K a multiple of 32
     const void* act;  // [M][act_ld] storage type
     int act_ld, M;    // M <= 16 * MT
@@ -44,8 +52,48 @@ struct KsplitArgs {
     int fb_per_wg;    // 128-feature blocks per workgroup (gridDim.x = ceil(ceil(N / 128) / fb_per_wg))
 };
 
+// One 128-element block of a wave's 16 weight rows, R4 layout (lane: row 4 j + lane / 16 of the 16,
+// bytes 16 (lane % 16) .. +15), with the masks applied on the way into the slab.
+struct KsBlock {
+    uint4 v[4];
+    uint32_t keep[4];
+};
+
+// Loads element q = (feature block i, K block b) = (q / nb, q % nb) of a wave's stream. Steps past
+// the slice or the stream read their row's first chunk (rows past N: row 0) and are masked.
+// f0: first feature of the workgroup's run; r0: this lane's first row inside a block (wave * 16 +
+// lane / 16).
+template <bool STREAM>
+__device__ __forceinline__ void ks_load_block(KsBlock& wb, int q, int nb, int nfb, int total, int nsteps, int f0,
+                                              int r0, int cc, long kbase, const uint16_t* W0, const uint16_t* W1,
+                                              const uint16_t* W2, int n0s, int n01, int N, int K) {
+    const int i = min(q / nb, nfb - 1), b = q - (q / nb) * nb;
+    const bool kin = q < total && 4 * b + (cc >> 2) < nsteps;
+    const long ko = kin ? kbase + 8 * cc + (long)b * 128 : 0;
+    // the block's segment (wave-uniform): its base and its first row inside it
+    const int b0 = f0 + i * kKsRows;
+    const bool in0 = b0 < n0s, in1 = b0 < n01;
+    const uint16_t* seg = in0 ? W0 : in1 ? W1 : W2;
+    const int sb = in0 ? b0 : in1 ? b0 - n0s : b0 - n01;
+    // a global-memory pointer, said explicitly: after the choice among three pointers the compiler
+    // no longer infers it, and would issue generic loads
+    typedef const __attribute__((address_space(1))) u32x4_t* gptr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = r0 + 4 * j;  // row inside the block
+        const bool rv = b0 + r < N;
+        const gptr src = (gptr)(seg + (long)(rv ? sb + r : 0) * K + ko);
+        wb.v[j] = __builtin_bit_cast(uint4, STREAM ? __builtin_nontemporal_load(src) : *src);
+        wb.keep[j] = (kin && rv) ? 0xFFFFFFFFu : 0u;
+    }
+}
+
 template <int DT, int MT, bool STREAM>
 __global__ void __launch_bounds__(512) gemm_ksplit_kernel(KsplitArgs g) {
+    // the fields the lambdas below use, as plain values (a lambda holding a reference to the whole
+    // argument block keeps the block in scratch memory)
+    const int N = g.N, K = g.K, M = g.M, n0s = g.n0, n01 = g.n0 + g.n1;
+    float* const part = g.part;
     constexpr int ROWB = 256 + 16;  // slab row stride in bytes
     constexpr int SLAB = 16 * ROWB;
     constexpr int XLD = ks_slice(MT) + kKsXPad;  // X row stride in LDS, elements
@@ -55,9 +103,9 @@ __global__ void __launch_bounds__(512) gemm_ksplit_kernel(KsplitArgs g) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int fb0 = blockIdx.x * g.fb_per_wg;  // this workgroup's feature blocks fb0 .. fb0 + nfb - 1
-    const int nfb = min(g.fb_per_wg, (g.N + kKsRows - 1) / kKsRows - fb0);
+    const int nfb = min(g.fb_per_wg, (N + kKsRows - 1) / kKsRows - fb0);
     const int sl = blockIdx.y;
-    const int KC = g.K / 32;
+    const int KC = K / 32;
     const int c0 = (int)(((long)sl * KC) / g.n_slices), c1 = (int)(((long)(sl + 1) * KC) / g.n_slices);
     const int nsteps = c1 - c0;  // 32-element steps of this slice (<= ks_slice(MT) / 32)
     const long kbase = (long)c0 * 32;
@@ -67,28 +115,16 @@ __global__ void __launch_bounds__(512) gemm_ksplit_kernel(KsplitArgs g) {
     const int nb = (nsteps + 3) / 4;  // K blocks per feature block
     const int total = nfb * nb;
     const int rr = lane >> 4, cc = lane & 15;
-    const uint16_t* W = reinterpret_cast<const uint16_t*>(g.w);
-    struct WBlock {
-        uint4 v[4];
-        uint32_t keep[4];
+    const uint16_t* W0 = reinterpret_cast<const uint16_t*>(g.w0);
+    const uint16_t* W1 = reinterpret_cast<const uint16_t*>(g.w1);
+    const uint16_t* W2 = reinterpret_cast<const uint16_t*>(g.w2);
+    // (a free function: inside a lambda, the choice among the captured pointers becomes a load
+    // from the closure at a run-time offset, which keeps the closure in scratch memory)
+    auto load_block = [&](KsBlock& wb, int q) {
+        ks_load_block<STREAM>(wb, q, nb, nfb, total, nsteps, fb0 * kKsRows, wave * 16 + rr, cc, kbase, W0, W1, W2,
+                              n0s, n01, N, K);
     };
-    // steps past the slice or the stream read their row's first chunk (rows past N: row 0) and are
-    // zeroed on the way into the slab
-    auto load_block = [&](WBlock& wb, int q) {
-        const int i = min(q / nb, nfb - 1), b = q - (q / nb) * nb;
-        const bool kin = q < total && 4 * b + (cc >> 2) < nsteps;
-        const long ko = kin ? (long)b * 128 : 0;
-        const int n0 = (fb0 + i) * kKsRows + wave * 16;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = n0 + 4 * j + rr;
-            const bool rv = row < g.N;
-            const uint16_t* src = W + (long)(rv ? row : 0) * g.K + (kin ? kbase + 8 * cc + ko : 0);
-            wb.v[j] = STREAM ? load_stream16(src) : *reinterpret_cast<const uint4*>(src);
-            wb.keep[j] = (kin && rv) ? 0xFFFFFFFFu : 0u;
-        }
-    };
-    WBlock w0, w1, w2;
+    KsBlock w0, w1, w2;
     load_block(w0, 0);
     load_block(w1, 1);
 
@@ -98,7 +134,7 @@ __global__ void __launch_bounds__(512) gemm_ksplit_kernel(KsplitArgs g) {
         const uint16_t* A = reinterpret_cast<const uint16_t*>(g.act);
         for (int c = threadIdx.x; c < MT * 16 * cpr; c += 512) {
             const int r = c / cpr, q = c - r * cpr;
-            const int m = r < g.M ? r : 0;
+            const int m = r < M ? r : 0;
             const uint4 v = *reinterpret_cast<const uint4*>(A + (long)m * g.act_ld + kbase + 8 * q);
             *reinterpret_cast<uint4*>(xs + r * XLD + 8 * q) = v;
         }
@@ -110,19 +146,19 @@ __global__ void __launch_bounds__(512) gemm_ksplit_kernel(KsplitArgs g) {
     for (int mt = 0; mt < MT; ++mt) acc[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
     // partial sums of feature block i, then a fresh accumulator: lane holds
     // C[feature n0 + 4 kq + r][row 16 mt + l16], r = 0..3
-    auto flush = [&](int i) {
+    auto flush = [=, &acc](int i) {
         const int n = (fb0 + i) * kKsRows + wave * 16 + 4 * (lane >> 4);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int m = mt * 16 + (lane & 15);
-            if (m < g.M) {
-                float* dst = g.part + ((long)sl * g.M + m) * g.N + n;
-                if (n + 3 < g.N) {
+            if (m < M) {
+                float* dst = part + ((long)sl * M + m) * N + n;
+                if (n + 3 < N) {
                     *reinterpret_cast<float4_t*>(dst) = acc[mt];
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (n + r < g.N) dst[r] = acc[mt][r];
+                        if (n + r < N) dst[r] = acc[mt][r];
                 }
             }
             acc[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
@@ -130,7 +166,7 @@ __global__ void __launch_bounds__(512) gemm_ksplit_kernel(KsplitArgs g) {
     };
     unsigned char* my = slabs + wave * SLAB;
     const int l16 = lane & 15, kq = lane >> 4;
-    auto multiply = [&](const WBlock& wb, int b) {
+    auto multiply = [=, &acc](const KsBlock& wb, int b) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint4 v = wb.v[j];
@@ -152,7 +188,7 @@ __global__ void __launch_bounds__(512) gemm_ksplit_kernel(KsplitArgs g) {
         }
     };
     // multiply stream element q; after a feature block's last K block, write its partial sums
-    auto step = [&](const WBlock& wb, int q) {
+    auto step = [=, &acc](const KsBlock& wb, int q) {
         const int i = q / nb, b = q - i * nb;
         multiply(wb, b);
         if (b == nb - 1) flush(i);
@@ -171,6 +207,83 @@ __global__ void __launch_bounds__(512) gemm_ksplit_kernel(KsplitArgs g) {
         __builtin_amdgcn_sched_barrier(0);
         step(w2, q + 2);
     }
+}
+
+// sum over slices of part[slice][j] (plane apart), in slice order; the loads of eight slices at a
+// time are issued before the first add (the index is clamped, not branched around)
+__device__ __forceinline__ float slice_sum(const float* p, long plane, int n_slices) {
+    float s = 0.f;
+    for (int s0 = 0; s0 < n_slices; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = p[min(s0 + j, n_slices - 1) * plane];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (s0 + j < n_slices) s = s0 + j == 0 ? v[j] : s + v[j];
+    }
+    return s;
+}
+
+// q, k, v of the step's rows from the split-K partial sums of the stacked [Wq; Wk; Wv] product
+// (N = (n_heads + 2 n_kv_heads) head_dim): the epilogue of the skinny tile GEMM on summed values
+// ([KV Cache] section 03: rotary on q and k, q to q_out, k and v into the row's page slot). One
+// thread per (row, head of the stack, rotary pair i, i + head_dim / 2).
+template <int DT>
+__global__ void __launch_bounds__(256) qkv_reduce_kernel(GemmArgs g, const float* __restrict__ part, int n_slices,
+                                                         int N) {
+    const int half = g.head_dim / 2;
+    const int units = (g.n_heads + 2 * g.n_kv_heads) * half;
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)g.M * units) return;
+    const int m = (int)(idx / units), u = (int)(idx - (long)m * units);
+    const int hh = u / half, i = u - hh * half;  // head of the stack, pair index
+    const int seg = hh < g.n_heads ? 0 : hh < g.n_heads + g.n_kv_heads ? 1 : 2;
+    const int head = seg == 0 ? hh : seg == 1 ? hh - g.n_heads : hh - g.n_heads - g.n_kv_heads;
+    const long plane = (long)g.M * N;
+    const float* src = part + (long)m * N + (long)hh * g.head_dim + i;
+    const float a = slice_sum(src, plane, n_slices);
+    const float b = slice_sum(src + half, plane, n_slices);
+    float ra = a, rb = b;
+    if (seg < 2) {
+        const float c = g.rope_cs[((long)m * half + i) * 2 + 0];
+        const float sn = g.rope_cs[((long)m * half + i) * 2 + 1];
+        ra = a * c - b * sn;
+        rb = b * c + a * sn;
+    }
+    if (seg == 0) {
+        const long o = (long)m * (g.n_heads * g.head_dim) + (long)head * g.head_dim + i;
+        store_round<DT>(g.q_out, o, ra);
+        store_round<DT>(g.q_out, o + half, rb);
+    } else {
+        const int pos = g.row_pos[m];
+        const int sq = g.row_seq[m];
+        if (pos < 0 || pos / g.page_tokens >= g.max_blocks) return;
+        const int page = g.block_tables[(long)sq * g.max_blocks + pos / g.page_tokens];
+        if (page < 0 || page >= g.num_pages) return;
+        const int slot = pos % g.page_tokens;
+        const long o = (long)page * g.page_elems + (long)g.layer * g.layer_elems +
+                       ((long)(seg - 1) * g.n_kv_heads + head) * g.page_tokens * g.head_dim +
+                       (long)slot * g.head_dim + i;
+        store_kv<DT>(g.kv_base, o, ra, g.kv_dt);
+        store_kv<DT>(g.kv_base, o + half, rb, g.kv_dt);
+    }
+}
+
+// h = silu(gate) * up from the split-K partial sums of the stacked [W_gate; W_up] product
+// (N = 2F): the SwiGLU epilogue of the skinny tile GEMM on summed values. One thread per
+// (row, feature).
+template <int DT>
+__global__ void __launch_bounds__(256) swiglu_reduce_kernel(const float* __restrict__ part, int n_slices, int M,
+                                                            int F, void* h_out, int h_ld) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)M * F) return;
+    const int m = (int)(idx / F), f = (int)(idx - (long)m * F);
+    const long plane = (long)M * 2 * F;
+    const float* src = part + (long)m * 2 * F + f;
+    const float a = slice_sum(src, plane, n_slices);
+    const float b = slice_sum(src + F, plane, n_slices);
+    const float s = a / (1.0f + expf(-a));
+    store_round<DT>(h_out, (long)m * h_ld + f, s * b);
 }
 
 // x[m][n] += sum over slices of part[slice][m][n], slices in order; four features per thread.

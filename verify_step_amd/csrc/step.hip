@@ -96,6 +96,7 @@ struct Plan {
     int n_splits, split_pages, rmax, attn_hg, attn_waves, rg_blocks;
     bool attn_mfma;  // matrix-core attention: up to 16 (row, head) states per workgroup
     bool ksplit;  // residual products through the split-K tile GEMM
+    bool ksplit_qkv, ksplit_gu;  // the q/k/v and gate/up products too (their epilogues after the sums)
     int ks_slices;  // most slices of one of them (sizes the partial sums)
     bool gemv;      // the row-streaming path serves every product of the step
     bool merge_in_o; // the output product's prologue merges the key splits (no merge kernel)
@@ -202,6 +203,12 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->ksplit = !p->gemv && p->dt != VS_F32 && d->M > 16 && d->M <= 64;
     const int ks_mt = (std::max(d->M, 1) + 15) / 16;
     p->ks_slices = std::max(ks_slices(p->H * p->Dh, ks_mt), ks_slices(p->F, ks_mt));
+    // (the stacked products' segments must start on 128-feature blocks)
+    p->ksplit_qkv = p->ksplit && (p->H * p->Dh) % kKsRows == 0 && (p->Hkv * p->Dh) % kKsRows == 0;
+    p->ksplit_gu = p->ksplit && p->F % kKsRows == 0;
+    const long n_qkv = (long)(p->H + 2 * p->Hkv) * p->Dh, n_gu = 2L * p->F;
+    const long ks_floats = std::max<long>((long)p->ks_slices * p->D,
+                                          (long)ks_slices(p->D, ks_mt) * std::max(n_qkv, n_gu));
     const size_t M = (size_t)std::max(d->M, 1), ML = (size_t)std::max(d->M_log, 1);
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -220,7 +227,7 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->off_part = take(M * p->H * p->n_splits * part_stride(p->Dh) * 4);
     p->off_xf = take(ML * p->D * p->esz);
     p->off_lmpart = take(ML * p->n_lm_parts * sizeof(ArgPart));
-    p->off_ksp = take(p->ksplit ? (size_t)p->ks_slices * M * p->D * 4 : 4);
+    p->off_ksp = take(p->ksplit ? (size_t)ks_floats * M * 4 : 4);
     p->total = o;
     return vs_ok();
 }
@@ -246,12 +253,13 @@ void launch_gemm_mt(int kind, const GemmArgs& g, int NW, int n_mgroups, hipStrea
 // x += W a for 5..64 rows: the split-K tile GEMM writes per-slice partial sums, then they are added
 // to x in slice order. With a gain, the same kernel that adds them also writes RMSNorm(x) * gain to
 // y (x rows of exactly N features).
+// Partial sums part[slice][M][N] of W a for 5..64 rows through the split-K tile GEMM, W up to
+// three stacked segments (w0: rows [0, n0), w1: [n0, n0 + n1), w2: the rest); returns the slices.
 template <int DT>
-void launch_resid_ksplit(int kind, const void* w, int N, int K, const void* act, int act_ld, int M, float* x,
-                         int x_ld, float* part, hipStream_t s, const void* gain = nullptr, float eps = 0.f,
-                         void* y = nullptr) {
+int launch_ksplit(int kind, const void* w0, const void* w1, const void* w2, int n0, int n1, int N, int K,
+                  const void* act, int act_ld, int M, float* part, hipStream_t s) {
     if constexpr (DT == F32) {
-        return;  // fp32 models keep the tile GEMM (the plan never selects this for them)
+        return 0;  // fp32 models keep the tile GEMM (the plan never selects this for them)
     } else {
     // each workgroup takes a run of feature blocks, so that the grid is about one round of the
     // workgroups the CUs hold (the start of a workgroup, X staging and the first loads, is paid
@@ -259,20 +267,32 @@ void launch_resid_ksplit(int kind, const void* w, int N, int K, const void* act,
     const int MT = (M + 15) / 16, nblk = (N + kKsRows - 1) / kKsRows, slices = ks_slices(K, MT);
     const long resident = (long)kNumCUs * std::max(1, (int)(kLdsPerCu / ks_lds_bytes(MT)));
     const int fb = (int)std::max<long>(1, ((long)nblk * slices + resident - 1) / resident);
-    const KsplitArgs a{w, N, K, act, act_ld, M, slices, part, fb};
+    const KsplitArgs a{w0, w1, w2, n0, n1, N, K, act, act_ld, M, slices, part, fb};
     const dim3 grid((nblk + fb - 1) / fb, a.n_slices), block(512);
-    switch ((M + 15) / 16) {
+    switch (MT) {
         case 1: launch1(kind, gemm_ksplit_kernel<DT, 1, true>, grid, block, 0, s, a); break;
         case 2: launch1(kind, gemm_ksplit_kernel<DT, 2, true>, grid, block, 0, s, a); break;
         case 3: launch1(kind, gemm_ksplit_kernel<DT, 3, true>, grid, block, 0, s, a); break;
         default: launch1(kind, gemm_ksplit_kernel<DT, 4, true>, grid, block, 0, s, a); break;
     }
+    return slices;
+    }
+}
+
+template <int DT>
+void launch_resid_ksplit(int kind, const void* w, int N, int K, const void* act, int act_ld, int M, float* x,
+                         int x_ld, float* part, hipStream_t s, const void* gain = nullptr, float eps = 0.f,
+                         void* y = nullptr) {
+    if constexpr (DT == F32) {
+        return;  // fp32 models keep the tile GEMM (the plan never selects this for them)
+    } else {
+    const int slices = launch_ksplit<DT>(kind, w, w, w, N, 0, N, K, act, act_ld, M, part, s);
     if (gain) {
-        hipLaunchKernelGGL((resid_norm_kernel<DT>), dim3(M), dim3(1024), 0, s, x, part, a.n_slices, M, N, gain, eps, y);
+        hipLaunchKernelGGL((resid_norm_kernel<DT>), dim3(M), dim3(1024), 0, s, x, part, slices, M, N, gain, eps, y);
     } else {
         const long groups = (long)M * ((N + 3) / 4);
         hipLaunchKernelGGL(resid_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, x, x_ld,
-                           part, a.n_slices, M, N);
+                           part, slices, M, N);
     }
     }
 }
@@ -516,7 +536,16 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             q.n_tiles = (p.H + 2 * p.Hkv) * p.Dh / 32;
             q.q_out = qb;
             q.layer = l;
-            launch_gemm<DT, EPI_QKV>(VS_KERNEL_QKV, q, s);
+            if (p.ksplit_qkv) {
+                const int N = q.n0 + q.n1 + q.n2;
+                const int slices = launch_ksplit<DT>(VS_KERNEL_QKV, lw.wq, lw.wk, lw.wv, q.n0, q.n1, N, p.D, xn, p.D,
+                                                     p.M, ksp, s);
+                const long threads = (long)p.M * (p.H + 2 * p.Hkv) * (p.Dh / 2);
+                hipLaunchKernelGGL((qkv_reduce_kernel<DT>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                                   q, ksp, slices, N);
+            } else {
+                launch_gemm<DT, EPI_QKV>(VS_KERNEL_QKV, q, s);
+            }
         }
 
         a.layer = l;
@@ -588,7 +617,15 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             gu.n_tiles = (p.F + 15) / 16;
             gu.h_out = hmid;
             gu.h_ld = p.F;
-            launch_gemm<DT, EPI_SWIGLU>(VS_KERNEL_GATEUP, gu, s);
+            if (p.ksplit_gu) {
+                const int slices = launch_ksplit<DT>(VS_KERNEL_GATEUP, lw.wg, lw.wu, lw.wu, p.F, p.F, 2 * p.F, p.D, xn,
+                                                     p.D, p.M, ksp, s);
+                const long threads = (long)p.M * p.F;
+                hipLaunchKernelGGL((swiglu_reduce_kernel<DT>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                                   s, ksp, slices, p.M, p.F, hmid, p.F);
+            } else {
+                launch_gemm<DT, EPI_SWIGLU>(VS_KERNEL_GATEUP, gu, s);
+            }
         }
 
         // x += W_d h
