@@ -106,56 +106,52 @@ __global__ void __launch_bounds__(256) argmax_accept_kernel(const ArgPart* parts
     const int r1 = min(max(q_start[b + 1], r0), M);
     __shared__ float sv1[4], sv2[4];
     __shared__ int si1[4];
-    for (int r = r0; r < r1 && argmax; ++r) {
-        // logit row index of r: binary search in the ascending logit_rows
-        int j = -1;
-        if (M_log > 0) {
-            int lo = 0, hi = M_log - 1;
-            while (lo <= hi) {
-                const int mid = (lo + hi) >> 1;
-                const int v = logit_rows[mid];
-                if (v == r) {
-                    j = mid;
-                    break;
-                }
-                if (v < r) lo = mid + 1;
-                else hi = mid - 1;
+    if (argmax) {
+        // rows without logits first (all threads), then the sequence's logit rows: one lower-bound
+        // search in the ascending logit_rows finds the first, the rest follow it in order (a search
+        // per row would be a chain of dependent loads for every row of a long prompt chunk)
+        for (int r = r0 + threadIdx.x; r < r1; r += blockDim.x) {
+            argmax[r] = -1;
+            if (gap) gap[r] = NAN;
+        }
+        int lo = 0, hi = M_log;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (logit_rows[mid] < r0) lo = mid + 1;
+            else hi = mid;
+        }
+        __syncthreads();  // the defaults above land before the values below
+        for (int j = lo; j < M_log; ++j) {
+            const int r = logit_rows[j];
+            if (r >= r1) break;
+            float v1 = -INFINITY, v2 = -INFINITY;
+            int i1 = 0x7FFFFFFF;
+            for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) {
+                const ArgPart p = parts[(long)j * n_tiles + t];
+                argpart_combine(v1, i1, v2, p.v1, p.i1, p.v2);
             }
-        }
-        if (j < 0) {
-            if (threadIdx.x == 0) {
-                if (argmax) argmax[r] = -1;
-                if (gap) gap[r] = NAN;
-            }
-            continue;
-        }
-        float v1 = -INFINITY, v2 = -INFINITY;
-        int i1 = 0x7FFFFFFF;
-        for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) {
-            const ArgPart p = parts[(long)j * n_tiles + t];
-            argpart_combine(v1, i1, v2, p.v1, p.i1, p.v2);
-        }
 #pragma unroll
-        for (int mask = 32; mask >= 1; mask >>= 1) {
-            const float o1 = shfl_xor(v1, mask);
-            const int oi = shfl_xor(i1, mask);
-            const float o2 = shfl_xor(v2, mask);
-            argpart_combine(v1, i1, v2, o1, oi, o2);
+            for (int mask = 32; mask >= 1; mask >>= 1) {
+                const float o1 = shfl_xor(v1, mask);
+                const int oi = shfl_xor(i1, mask);
+                const float o2 = shfl_xor(v2, mask);
+                argpart_combine(v1, i1, v2, o1, oi, o2);
+            }
+            if ((threadIdx.x & 63) == 0) {
+                sv1[threadIdx.x >> 6] = v1;
+                si1[threadIdx.x >> 6] = i1;
+                sv2[threadIdx.x >> 6] = v2;
+            }
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                float a1 = sv1[0], a2 = sv2[0];
+                int ai = si1[0];
+                for (int w = 1; w < 4; ++w) argpart_combine(a1, ai, a2, sv1[w], si1[w], sv2[w]);
+                argmax[r] = ai;
+                if (gap) gap[r] = a1 - a2;
+            }
+            __syncthreads();
         }
-        if ((threadIdx.x & 63) == 0) {
-            sv1[threadIdx.x >> 6] = v1;
-            si1[threadIdx.x >> 6] = i1;
-            sv2[threadIdx.x >> 6] = v2;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            float a1 = sv1[0], a2 = sv2[0];
-            int ai = si1[0];
-            for (int w = 1; w < 4; ++w) argpart_combine(a1, ai, a2, sv1[w], si1[w], sv2[w]);
-            argmax[r] = ai;
-            if (gap) gap[r] = a1 - a2;
-        }
-        __syncthreads();
     }
     if (accept_len && threadIdx.x == 0) {
         // drafts d_1..d_K are the row tokens; g_0 is given, g_j = argmax of row j-1
