@@ -198,13 +198,17 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->gemv = d->M <= kGemvMaxRows && (size_t)std::max(d->M, 1) * p->D * p->esz <= kGemvMaxLds;
     p->merge_in_o = p->gemv && p->n_splits > 1 && p->n_splits <= kMergeMaxSplits;
     p->n_lm_parts = p->gemv ? (p->V + gemv_units_per_wg(p->V) - 1) / gemv_units_per_wg(p->V) : (p->V + 15) / 16;
-    // 17..64 rows in fp16 / bf16: the output and down products split K over workgroups (up to 16 rows
-    // the 16-feature tiles read no more activation bytes than weight bytes)
+    // 17..64 rows in fp16 / bf16: the weight products split K over workgroups, the X slice staged
+    // once per workgroup in LDS (up to 16 rows the 16-feature tiles read no more activation bytes
+    // than weight bytes)
     p->ksplit = !p->gemv && p->dt != VS_F32 && d->M > 16 && d->M <= 64;
     const int ks_mt = (std::max(d->M, 1) + 15) / 16;
     p->ks_slices = std::max(ks_slices(p->H * p->Dh, ks_mt), ks_slices(p->F, ks_mt));
-    // (the stacked products' segments must start on 128-feature blocks)
-    p->ksplit_qkv = p->ksplit && (p->H * p->Dh) % kKsRows == 0 && (p->Hkv * p->Dh) % kKsRows == 0;
+    // (the stacked products' segments must start on 128-feature blocks). The q/k/v product takes
+    // it from 5 rows on (measured at 8 rows: 25 against 29 us per layer at the 7B shape; the other
+    // products are faster as 16-feature tiles there)
+    p->ksplit_qkv = !p->gemv && p->dt != VS_F32 && d->M <= 64 && (p->H * p->Dh) % kKsRows == 0 &&
+                    (p->Hkv * p->Dh) % kKsRows == 0;
     p->ksplit_gu = p->ksplit && p->F % kKsRows == 0;
     const long n_qkv = (long)(p->H + 2 * p->Hkv) * p->Dh, n_gu = 2L * p->F;
     const long ks_floats = std::max<long>((long)p->ks_slices * p->D,
@@ -227,7 +231,7 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->off_part = take(M * p->H * p->n_splits * part_stride(p->Dh) * 4);
     p->off_xf = take(ML * p->D * p->esz);
     p->off_lmpart = take(ML * p->n_lm_parts * sizeof(ArgPart));
-    p->off_ksp = take(p->ksplit ? (size_t)ks_floats * M * 4 : 4);
+    p->off_ksp = take(p->ksplit || p->ksplit_qkv ? (size_t)ks_floats * M * 4 : 4);
     p->total = o;
     return vs_ok();
 }
