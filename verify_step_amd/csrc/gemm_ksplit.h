@@ -27,9 +27,10 @@ namespace vs {
 
 constexpr int kKsRows = 128;  // output features per workgroup (8 waves x 16)
 constexpr int kKsXPad = 8;    // LDS row padding (elements): a fragment's 16 rows fall on different banks
-// most reduction elements per workgroup (measured: longer slices leave too few workgroups for the
-// 4096-feature products, shorter ones add partial sums)
-__host__ __device__ constexpr int ks_slice(int) { return 512; }
+// most reduction elements per workgroup: 1024 for 33..48 rows (the X slice then fills most of the
+// LDS of the one workgroup a CU holds at that size anyway), 512 otherwise (with 17..32 rows two
+// workgroups fit a CU, with 49..64 rows a longer slice does not fit)
+__host__ __device__ constexpr int ks_slice(int MT) { return MT == 3 ? 1024 : 512; }
 
 // LDS of one workgroup (X slice + eight weight slabs), for the workgroups a CU can hold
 __host__ __device__ constexpr int ks_lds_bytes(int MT) {
@@ -47,7 +48,8 @@ struct KsplitArgs {
     int N, K;       // K a multiple of 32
     const void* act;  // [M][act_ld] storage type
     int act_ld, M;    // M <= 16 * MT
-    int n_slices;     // workgroups along K (gridDim.y); every slice holds at most ks_slice(MT) elements
+    int n_slices;     // workgroups along K (gridDim.y); slices are whole 128-element blocks, at most
+                      // ks_slice(MT) elements each: n_slices >= ceil(ceil(K / 128) / (ks_slice(MT) / 128))
     float* part;      // [n_slices][M][N] fp32
     int fb_per_wg;    // 128-feature blocks per workgroup (gridDim.x = ceil(ceil(N / 128) / fb_per_wg))
 };
@@ -105,8 +107,11 @@ __global__ void __launch_bounds__(512) gemm_ksplit_kernel(KsplitArgs g) {
     const int fb0 = blockIdx.x * g.fb_per_wg;  // this workgroup's feature blocks fb0 .. fb0 + nfb - 1
     const int nfb = min(g.fb_per_wg, (N + kKsRows - 1) / kKsRows - fb0);
     const int sl = blockIdx.y;
-    const int KC = K / 32;
-    const int c0 = (int)(((long)sl * KC) / g.n_slices), c1 = (int)(((long)(sl + 1) * KC) / g.n_slices);
+    // slices on whole 128-element blocks (a block cut by a slice boundary would be loaded whole and
+    // partly masked); only the last block of K may be short
+    const int KC = K / 32, KB = (KC + 3) / 4;
+    const int c0 = min(4 * (int)(((long)sl * KB) / g.n_slices), KC);
+    const int c1 = min(4 * (int)(((long)(sl + 1) * KB) / g.n_slices), KC);
     const int nsteps = c1 - c0;  // 32-element steps of this slice (<= ks_slice(MT) / 32)
     const long kbase = (long)c0 * 32;
 

@@ -65,8 +65,42 @@ void launch1(int kind, void (*kern)(T), dim3 grid, dim3 block, size_t lds, hipSt
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// slices of a split-K residual product with MT row blocks: every slice at most ks_slice(MT) elements
-int ks_slices(int K, int MT) { return (K / 32 + ks_slice(MT) / 32 - 1) / (ks_slice(MT) / 32); }
+// The chip: 256 CUs of 160 KB LDS (MI355X).
+constexpr int kNumCUs = 256;
+constexpr int kLdsPerCu = 160 * 1024;
+
+// Slices along K and 128-feature blocks per workgroup of a split-K product (N features, K, M rows).
+// Every slice holds at most ks_slice(MT) elements; a workgroup takes a run of fb blocks of one slice,
+// so that the grid is about one round of the workgroups the CUs hold (the start of a workgroup,
+// X staging and the first loads, is paid once per run). With 33..48 rows a slice may hold 1024
+// elements: the fewest slices whose grid still fills 85 % of one round are taken, since every
+// slice is one more fp32 partial sum per output that is written and read again.
+struct KsShape {
+    int slices, fb;
+};
+KsShape ks_shape(int N, int K, int M) {
+    // slices are whole 128-element blocks of K (KB of them), at most mb blocks each
+    const int MT = (M + 15) / 16, nblk = (N + kKsRows - 1) / kKsRows, KB = (K / 32 + 3) / 4,
+              mb = ks_slice(MT) / 128;
+    const long resident = (long)kNumCUs * std::max(1, (int)(kLdsPerCu / ks_lds_bytes(MT)));
+    auto fb_of = [&](int s) { return (int)std::max<long>(1, ((long)nblk * s + resident - 1) / resident); };
+    int s = (KB + mb - 1) / mb;
+    if (MT == 3) {
+        int best = s;
+        double best_eff = 0.0;
+        for (int t = s; t <= KB; ++t) {
+            const long wgs = (long)((nblk + fb_of(t) - 1) / fb_of(t)) * t;
+            const double eff = (double)wgs / ((double)((wgs + resident - 1) / resident) * resident);
+            if (eff > best_eff + 1e-9) {
+                best_eff = eff;
+                best = t;
+            }
+            if (eff >= 0.85) break;
+        }
+        s = best;
+    }
+    return {s, fb_of(s)};
+}
 
 int kv_elem_bytes(int dtype) { return dtype == VS_F32 ? 4 : (dtype == VS_FP8_E4M3 || dtype == VS_FP8_E5M2) ? 1 : 2; }
 
@@ -85,9 +119,6 @@ constexpr long kAttnTargetWaves = 2048;  // eight-wave workgroups: 256 (one per 
 // four-wave workgroups (several rows per sequence, matrix-core attention): two per CU (for the
 // matrix-core kernel, measured: more splits only add the per-split start-up)
 constexpr long kAttnTargetWgsFew = 512;
-// The chip: 256 CUs of 160 KB LDS (MI355X).
-constexpr int kNumCUs = 256;
-constexpr int kLdsPerCu = 160 * 1024;
 // Output units per workgroup of the output GEMV when it merges the key splits itself.
 constexpr int kGemvMergeUnits = 16;
 
@@ -202,8 +233,7 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     // once per workgroup in LDS (up to 16 rows the 16-feature tiles read no more activation bytes
     // than weight bytes)
     p->ksplit = !p->gemv && p->dt != VS_F32 && d->M > 16 && d->M <= 64;
-    const int ks_mt = (std::max(d->M, 1) + 15) / 16;
-    p->ks_slices = std::max(ks_slices(p->H * p->Dh, ks_mt), ks_slices(p->F, ks_mt));
+    p->ks_slices = std::max(ks_shape(p->D, p->H * p->Dh, d->M).slices, ks_shape(p->D, p->F, d->M).slices);
     // (the stacked products' segments must start on 128-feature blocks). The q/k/v product takes
     // it from 5 rows on (measured at 8 rows: 25 against 29 us per layer at the 7B shape; the other
     // products are faster as 16-feature tiles there)
@@ -212,7 +242,8 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->ksplit_gu = p->ksplit && p->F % kKsRows == 0;
     const long n_qkv = (long)(p->H + 2 * p->Hkv) * p->Dh, n_gu = 2L * p->F;
     const long ks_floats = std::max<long>((long)p->ks_slices * p->D,
-                                          (long)ks_slices(p->D, ks_mt) * std::max(n_qkv, n_gu));
+                                          std::max((long)ks_shape(n_qkv, p->D, d->M).slices * n_qkv,
+                                                   (long)ks_shape(n_gu, p->D, d->M).slices * n_gu));
     const size_t M = (size_t)std::max(d->M, 1), ML = (size_t)std::max(d->M_log, 1);
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -265,12 +296,9 @@ int launch_ksplit(int kind, const void* w0, const void* w1, const void* w2, int 
     if constexpr (DT == F32) {
         return 0;  // fp32 models keep the tile GEMM (the plan never selects this for them)
     } else {
-    // each workgroup takes a run of feature blocks, so that the grid is about one round of the
-    // workgroups the CUs hold (the start of a workgroup, X staging and the first loads, is paid
-    // once per run)
-    const int MT = (M + 15) / 16, nblk = (N + kKsRows - 1) / kKsRows, slices = ks_slices(K, MT);
-    const long resident = (long)kNumCUs * std::max(1, (int)(kLdsPerCu / ks_lds_bytes(MT)));
-    const int fb = (int)std::max<long>(1, ((long)nblk * slices + resident - 1) / resident);
+    const int MT = (M + 15) / 16, nblk = (N + kKsRows - 1) / kKsRows;
+    const KsShape sh = ks_shape(N, K, M);
+    const int slices = sh.slices, fb = sh.fb;
     const KsplitArgs a{w0, w1, w2, n0, n1, N, K, act, act_ld, M, slices, part, fb};
     const dim3 grid((nblk + fb - 1) / fb, a.n_slices), block(512);
     switch (MT) {
