@@ -27,10 +27,10 @@ namespace vs {
 
 constexpr int kKsRows = 128;  // output features per workgroup (8 waves x 16)
 constexpr int kKsXPad = 8;    // LDS row padding (elements): a fragment's 16 rows fall on different banks
-// most reduction elements per workgroup: 1024 for 33..48 rows (the X slice then fills most of the
-// LDS of the one workgroup a CU holds at that size anyway), 512 otherwise (with 17..32 rows two
-// workgroups fit a CU, with 49..64 rows a longer slice does not fit)
-__host__ __device__ constexpr int ks_slice(int MT) { return MT == 3 ? 1024 : 512; }
+// most reduction elements per workgroup: 1024 for 33..48 rows and 768 for 49..64 (the X slice then
+// fills most of the LDS of the one workgroup a CU holds at those sizes anyway), 512 otherwise (with
+// up to 32 rows two or more workgroups fit a CU)
+__host__ __device__ constexpr int ks_slice(int MT) { return MT == 3 ? 1024 : MT == 4 ? 768 : 512; }
 
 // LDS of one workgroup (X slice + eight weight slabs), for the workgroups a CU can hold
 __host__ __device__ constexpr int ks_lds_bytes(int MT) {

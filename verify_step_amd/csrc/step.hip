@@ -70,32 +70,36 @@ constexpr int kNumCUs = 256;
 constexpr int kLdsPerCu = 160 * 1024;
 
 // Slices along K and 128-feature blocks per workgroup of a split-K product (N features, K, M rows).
-// Every slice holds at most ks_slice(MT) elements; a workgroup takes a run of fb blocks of one slice,
-// so that the grid is about one round of the workgroups the CUs hold (the start of a workgroup,
-// X staging and the first loads, is paid once per run). With 33..48 rows a slice may hold 1024
-// elements: the fewest slices whose grid still fills 85 % of one round are taken, since every
-// slice is one more fp32 partial sum per output that is written and read again.
+// Slices are whole 128-element blocks of K, at most ks_slice(MT) elements each; a workgroup takes a
+// run of fb feature blocks of one slice, so that the grid is about one round of the workgroups the
+// CUs hold (the start of a workgroup, X staging and the first loads, is paid once per run). From 33
+// rows on, slices may be longer than 512 elements, and the slice count minimises an estimate of the
+// time: rounds x the longest workgroup's blocks (fb x blocks per slice), times 1 + the fp32 partial
+// sums' bytes (written and read again) over the weight bytes, 4 s M / K; ties go to fewer slices.
+// (The estimate reproduces the measured best choice for the 7B and 8B-GQA products at 40 and 64
+// rows.)
 struct KsShape {
     int slices, fb;
 };
 KsShape ks_shape(int N, int K, int M) {
-    // slices are whole 128-element blocks of K (KB of them), at most mb blocks each
     const int MT = (M + 15) / 16, nblk = (N + kKsRows - 1) / kKsRows, KB = (K / 32 + 3) / 4,
               mb = ks_slice(MT) / 128;
     const long resident = (long)kNumCUs * std::max(1, (int)(kLdsPerCu / ks_lds_bytes(MT)));
     auto fb_of = [&](int s) { return (int)std::max<long>(1, ((long)nblk * s + resident - 1) / resident); };
     int s = (KB + mb - 1) / mb;
-    if (MT == 3) {
+    if (MT >= 3) {
         int best = s;
-        double best_eff = 0.0;
+        double best_cost = 0.0;
         for (int t = s; t <= KB; ++t) {
-            const long wgs = (long)((nblk + fb_of(t) - 1) / fb_of(t)) * t;
-            const double eff = (double)wgs / ((double)((wgs + resident - 1) / resident) * resident);
-            if (eff > best_eff + 1e-9) {
-                best_eff = eff;
+            const int fb = fb_of(t);
+            const long wgs = (long)((nblk + fb - 1) / fb) * t;
+            const long rounds = (wgs + resident - 1) / resident;
+            const double cost =
+                (double)rounds * fb * ((KB + t - 1) / t) * (1.0 + 4.0 * t * std::max(M, 1) / (double)K);
+            if (t == s || cost < best_cost - 1e-9) {
+                best_cost = cost;
                 best = t;
             }
-            if (eff >= 0.85) break;
         }
         s = best;
     }
