@@ -120,9 +120,12 @@ constexpr size_t kGemvPhaseLds = 64 * 1024;
 // and the workgroups the key splits aim for (one per CU).
 int attn_waves(int states, int dt) { return states == 1 || (states == 2 && dt != VS_F32) ? 8 : 4; }
 constexpr long kAttnTargetWaves = 2048;  // eight-wave workgroups: 256 (one per CU)
-// four-wave workgroups (several rows per sequence, matrix-core attention): two per CU (for the
-// matrix-core kernel, measured: more splits only add the per-split start-up)
+// four-wave workgroups (several rows per sequence): two per CU
 constexpr long kAttnTargetWgsFew = 512;
+// matrix-core attention: one per CU (measured: each further split adds its start-up and, past one
+// split, the merge kernel; at 8 x 5 verify rows one split per sequence and head ran 5.44 -> 5.21 ms
+// per 7B step)
+constexpr long kAttnTargetWgsMfma = 256;
 // Output units per workgroup of the output GEMV when it merges the key splits itself.
 constexpr int kGemvMergeUnits = 16;
 
@@ -223,7 +226,9 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     const int rg_needed = (d->max_rows + p->rmax - 1) / p->rmax;
     p->rg_blocks = (int)std::max<long>(1, std::min<long>(rg_needed, 65535L / d->B));
     const long pairs = (long)d->B * (m->n_heads / p->attn_hg) * p->rg_blocks;  // workgroups per split
-    const long wgs_target = p->attn_waves == 8 ? kAttnTargetWaves / 8 : kAttnTargetWgsFew;
+    const long wgs_target = p->attn_mfma          ? kAttnTargetWgsMfma
+                            : p->attn_waves == 8 ? kAttnTargetWaves / 8
+                                                 : kAttnTargetWgsFew;
     const int ns = (int)std::min<long>(std::max(1, max_pages / (2 * p->attn_waves)),
                                        std::max<long>(1, (wgs_target + pairs - 1) / pairs));
     p->split_pages = (max_pages + ns - 1) / ns;
