@@ -332,11 +332,11 @@ __global__ void __launch_bounds__(1024) resid_norm_kernel(float* __restrict__ x,
     const int m = blockIdx.x, tid = threadIdx.x;
     const long plane = (long)M * D;
     float* xr = x + (long)m * D;
-    float ss = 0.f;
-    for (int k = tid * 4; k < D; k += 1024 * 4) {
+    // the sum over slices of four features' partials; twelve slices' loads at a time, all issued
+    // before the first add (the slice index is clamped instead of branched around, so none of them
+    // waits for another)
+    auto slice_sum4 = [&](int k) {
         const float* src = part + (long)m * D + k;
-        // twelve slices' loads at a time, all issued before the first add (the slice index is clamped
-        // instead of branched around, so none of them waits for another)
         float4_t s = (float4_t){0.f, 0.f, 0.f, 0.f};
         for (int s0 = 0; s0 < n_slices; s0 += 12) {
             float4_t v[12];
@@ -347,6 +347,47 @@ __global__ void __launch_bounds__(1024) resid_norm_kernel(float* __restrict__ x,
             for (int j = 0; j < 12; ++j)
                 if (s0 + j < n_slices) s = s0 + j == 0 ? v[j] : s + v[j];
         }
+        return s;
+    };
+    __shared__ float wsum[16];
+    auto row_inv = [&](float ss) {
+#pragma unroll
+        for (int mask = 32; mask >= 1; mask >>= 1) ss += shfl_xor(ss, mask);
+        if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) tot += wsum[w];
+        return 1.0f / sqrtf(tot / (float)D + eps);
+    };
+    if (D <= 4 * 1024) {
+        // one group of four features per thread: the residual, the gain and the partials are all
+        // requested at once, and the new residual stays in registers across the row's reduction
+        const int k = tid * 4;
+        float4_t v = (float4_t){0.f, 0.f, 0.f, 0.f};
+        float gv[4] = {0.f, 0.f, 0.f, 0.f};
+        float ss = 0.f;
+        if (k < D) {
+            load_widen<DT, 4>(reinterpret_cast<const char*>(gain) + (long)k * St<DT>::bytes, gv);
+            v = *reinterpret_cast<const float4_t*>(xr + k);
+            const float4_t s = slice_sum4(k);
+            v[0] += s[0];
+            v[1] += s[1];
+            v[2] += s[2];
+            v[3] += s[3];
+            *reinterpret_cast<float4_t*>(xr + k) = v;
+            ss = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+        }
+        const float inv = row_inv(ss);
+        if (k < D) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) store_round<DT>(y, (long)m * D + k + e, v[e] * inv * gv[e]);
+        }
+        return;
+    }
+    float ss = 0.f;
+    for (int k = tid * 4; k < D; k += 1024 * 4) {
+        const float4_t s = slice_sum4(k);
         float4_t v = *reinterpret_cast<const float4_t*>(xr + k);
         v[0] += s[0];
         v[1] += s[1];
@@ -355,15 +396,7 @@ __global__ void __launch_bounds__(1024) resid_norm_kernel(float* __restrict__ x,
         *reinterpret_cast<float4_t*>(xr + k) = v;
         ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) ss += shfl_xor(ss, mask);
-    __shared__ float wsum[16];
-    if ((tid & 63) == 0) wsum[tid >> 6] = ss;
-    __syncthreads();
-    float tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < 16; ++w) tot += wsum[w];
-    const float inv = 1.0f / sqrtf(tot / (float)D + eps);
+    const float inv = row_inv(ss);
     for (int k = tid * 4; k < D; k += 1024 * 4) {
         const float4_t v = *reinterpret_cast<const float4_t*>(xr + k);  // this thread's own writes above
         float gv[4];
