@@ -343,10 +343,12 @@ void launch_gemm(int kind, const GemmArgs& g, hipStream_t s) {
     const int M = g.M;
     if (M <= 0) return;
     if constexpr (DT != F32) {
-        // more than 64 rows (a prompt chunk): LDS-tiled MFMA GEMM, two feature tiles x 128 rows per workgroup
+        // more than 64 rows (a prompt chunk): LDS-tiled MFMA GEMM, eight paired (or two single) feature
+        // tiles x 128 rows per workgroup
         if (M > 64 && g.K % kBigK == 0) {
-            const dim3 grid((M + kBigRows - 1) / kBigRows, (g.n_tiles + 1) / 2);
-            launch1(kind, gemm_big_kernel<DT, EPI>, grid, dim3(256), 0, s, g);
+            constexpr int T = big_tiles(EPI);
+            const dim3 grid((M + kBigRows - 1) / kBigRows, (g.n_tiles + T - 1) / T);
+            launch1(kind, gemm_big_kernel<DT, EPI>, grid, dim3(T * big_rgroups(EPI) * 64), 0, s, g);
             return;
         }
     }
