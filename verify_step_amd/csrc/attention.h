@@ -53,6 +53,8 @@ struct AttnArgs {
     float scale_log2;  // log2(e) / sqrt(DH)
     float* part;       // [M][n_heads][n_splits][part_stride(DH)]: m (log2 domain), l, -, -, o[DH]
     void* out;         // [M][n_heads*DH] storage type
+    int rows_lo, rows_hi;  // a workgroup serves only sequences of rows_lo..rows_hi rows (a step that mixes
+                           // one-row and longer sequences runs each kind through its own kernel)
 };
 
 // One split's statistics: m, l, two unused floats (so o starts 16-byte aligned), o[dh].
@@ -78,6 +80,7 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
 
     const int r0 = min(max(a.q_start[b], 0), a.M);
     const int R = min(max(a.q_start[b + 1] - r0, 0), a.M - r0);
+    if (R < a.rows_lo || R > a.rows_hi) return;  // another kernel's sequence
     const int ctx = max(a.ctx_len[b], 0);
     const int T = a.page_tokens;
     const int p_begin = s * a.split_pages;

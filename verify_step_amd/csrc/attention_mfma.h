@@ -108,6 +108,7 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
     const int hk = h0 / (a.n_heads / a.n_kv_heads);
     const int r0 = min(max(a.q_start[b], 0), a.M);
     const int Rn = min(max(a.q_start[b + 1] - r0, 0), a.M - r0);
+    if (Rn < a.rows_lo || Rn > a.rows_hi) return;  // another kernel's sequence
     const int ctx = max(a.ctx_len[b], 0);
     const int T = a.page_tokens;
     const int p_begin = s * a.split_pages;

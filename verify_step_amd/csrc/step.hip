@@ -133,6 +133,8 @@ struct Plan {
     int B, M, M_log, D, H, Hkv, Dh, F, V, L, dt, esz;
     int n_splits, split_pages, rmax, attn_hg, attn_waves, rg_blocks;
     bool attn_mfma;  // matrix-core attention: up to 16 (row, head) states per workgroup
+    bool attn_mixed;  // matrix-core attention for sequences of 2+ rows, the VALU kernel for one-row ones
+    int attn_hg1;     // head group of the VALU kernel's one-row sequences
     bool ksplit;  // residual products through the split-K tile GEMM
     bool ksplit_qkv, ksplit_gu;  // the q/k/v and gate/up products too (their epilogues after the sums)
     int ks_slices;  // most slices of one of them (sizes the partial sums)
@@ -213,6 +215,11 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
         // 16 dividing the group) x 16 / HG rows
         const int group = m->n_heads / m->n_kv_heads;
         p->attn_mfma = m->dtype != VS_F32 && m->head_dim == kAmDh && (d->max_rows >= 2 || group >= 2);
+        // rows differ between sequences (a prompt chunk among decode rows): the one-row sequences,
+        // which would fill one of the 16 states, go to the VALU kernel, whose one-state workgroups
+        // stream K/V faster
+        p->attn_mixed = p->attn_mfma && d->max_rows >= 2 && (long)d->M < (long)d->B * d->max_rows;
+        p->attn_hg1 = group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
         if (p->attn_mfma) {
             int hg = 1;
             while (hg < 16 && group % (2 * hg) == 0) hg *= 2;
@@ -439,12 +446,22 @@ void launch_attention_mfma(const AttnArgs& a, int B, int hg, hipStream_t s) {
 
 template <int DT, int DH>
 void launch_attention(const AttnArgs& a, int B, int M, int rmax, int hg, int kv_dt, bool merge_kernel, bool mfma,
-                      hipStream_t s) {
+                      hipStream_t s, bool mixed = false, int hg1 = 1) {
     if constexpr (DT != F32 && DH == kAmDh) {
         if (mfma) {
-            if (kv_dt == E4M3) launch_attention_mfma<DT, E4M3>(a, B, hg, s);
-            else if (kv_dt == E5M2) launch_attention_mfma<DT, E5M2>(a, B, hg, s);
-            else launch_attention_mfma<DT, DT>(a, B, hg, s);
+            AttnArgs am = a;
+            if (mixed) am.rows_lo = 2;
+            if (kv_dt == E4M3) launch_attention_mfma<DT, E4M3>(am, B, hg, s);
+            else if (kv_dt == E5M2) launch_attention_mfma<DT, E5M2>(am, B, hg, s);
+            else launch_attention_mfma<DT, DT>(am, B, hg, s);
+            if (mixed) {  // the one-row sequences: one-row groups of the VALU kernel, same splits
+                AttnArgs av = a;
+                av.rows_hi = 1;
+                av.rg_blocks = 1;
+                if (kv_dt == E4M3) launch_attention_kv<DT, DH, E4M3>(av, B, M, 1, hg1, false, s);
+                else if (kv_dt == E5M2) launch_attention_kv<DT, DH, E5M2>(av, B, M, 1, hg1, false, s);
+                else launch_attention_kv<DT, DH, DT>(av, B, M, 1, hg1, false, s);
+            }
             if (merge_kernel && a.n_splits > 1)
                 launch1(VS_KERNEL_MERGE, attn_merge_kernel<DT, DH>, dim3(M, a.n_heads), dim3(DH), 0, s, a);
             return;
@@ -523,6 +540,8 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     gm.M = p.M;
 
     AttnArgs a = {};
+    a.rows_lo = 0;
+    a.rows_hi = 0x7fffffff;  // every sequence (the mixed launch narrows it)
     a.q = qb;
     a.kv_base = kv_pool_base(d->pool);
     a.page_elems = (long)(kv_page_bytes(pg) / kv_elem_bytes(pg->dtype));
@@ -593,7 +612,8 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
 
         a.layer = l;
         if (p.Dh == 128)
-            launch_attention<DT, 128>(a, p.B, p.M, p.rmax, p.attn_hg, pg->dtype, !p.merge_in_o, p.attn_mfma, s);
+            launch_attention<DT, 128>(a, p.B, p.M, p.rmax, p.attn_hg, pg->dtype, !p.merge_in_o, p.attn_mfma, s,
+                                      p.attn_mixed, p.attn_hg1);
         else
             launch_attention<DT, 64>(a, p.B, p.M, p.rmax, p.attn_hg, pg->dtype, !p.merge_in_o, p.attn_mfma, s);
 
