@@ -291,6 +291,58 @@ __global__ void __launch_bounds__(256) swiglu_reduce_kernel(const float* __restr
     store_round<DT>(h_out, (long)m * h_ld + f, s * b);
 }
 
+// Logits of the step's logit rows from the split-K partial sums of the LM head (N = vocab), and the
+// argmax partials of every 16-feature tile, as the skinny tile GEMM's logits epilogue writes them
+// (largest value, its lowest index on ties, second largest). One thread per (row, tile): the tile's
+// 16 logits summed over the slices in order, written (when logits is not null) and folded in
+// column order.
+__global__ void __launch_bounds__(256) logits_reduce_kernel(const float* __restrict__ part, int n_slices, int M,
+                                                           int V, float* logits, ArgPart* parts, int n_tiles) {
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)M * n_tiles) return;
+    const int m = (int)(idx / n_tiles), t = (int)(idx - (long)m * n_tiles);
+    const long plane = (long)M * V;
+    const float* src = part + (long)m * V + 16 * t;
+    float acc[16];
+    if (16 * t + 16 <= V && (V & 3) == 0) {
+        // a whole tile in 16-byte loads, four slices' worth in flight at a time, added in slice order
+        for (int s0 = 0; s0 < n_slices; s0 += 4) {
+            float4_t a[4][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    a[j][q] = *reinterpret_cast<const float4_t*>(src + min(s0 + j, n_slices - 1) * plane + 4 * q);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (s0 + j < n_slices) acc[4 * q + e] = s0 + j == 0 ? a[j][q][e] : acc[4 * q + e] + a[j][q][e];
+        }
+    } else {  // the vocabulary's last, partial tile (or rows not 16-byte aligned): column by column
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] = 16 * t + j < V ? slice_sum(src + j, plane, n_slices) : 0.f;
+    }
+    float v1 = -INFINITY, v2 = -INFINITY;
+    int i1 = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int col = 16 * t + j;
+        if (col < V) {
+            if (logits) logits[(long)m * V + col] = acc[j];
+            argpart_combine(v1, i1, v2, acc[j], col, -INFINITY);
+        }
+    }
+    ArgPart p;
+    p.v1 = v1;
+    p.i1 = i1;
+    p.v2 = v2;
+    p.pad = 0;
+    parts[(long)m * n_tiles + t] = p;
+}
+
 // x[m][n] += sum over slices of part[slice][m][n], slices in order; four features per thread.
 __global__ void __launch_bounds__(256) resid_reduce_kernel(float* __restrict__ x, int x_ld,
                                                            const float* __restrict__ part, int n_slices, int M,

@@ -137,6 +137,7 @@ struct Plan {
     int attn_hg1;     // head group of the VALU kernel's one-row sequences
     bool ksplit;  // residual products through the split-K tile GEMM
     bool ksplit_qkv, ksplit_gu;  // the q/k/v and gate/up products too (their epilogues after the sums)
+    bool ksplit_lm;              // the LM head too (logits and argmax partials after the sums)
     int ks_slices;  // most slices of one of them (sizes the partial sums)
     bool gemv;      // the row-streaming path serves every product of the step
     bool merge_in_o; // the output product's prologue merges the key splits (no merge kernel)
@@ -256,10 +257,15 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->ksplit_qkv = !p->gemv && p->dt != VS_F32 && d->M <= 64 && (p->H * p->Dh) % kKsRows == 0 &&
                     (p->Hkv * p->Dh) % kKsRows == 0;
     p->ksplit_gu = p->ksplit && p->F % kKsRows == 0;
+    p->ksplit_lm = p->ksplit && d->M_log > 0;
     const long n_qkv = (long)(p->H + 2 * p->Hkv) * p->Dh, n_gu = 2L * p->F;
-    const long ks_floats = std::max<long>((long)p->ks_slices * p->D,
-                                          std::max((long)ks_shape(n_qkv, p->D, d->M).slices * n_qkv,
-                                                   (long)ks_shape(n_gu, p->D, d->M).slices * n_gu));
+    long ks_floats = std::max<long>((long)p->ks_slices * p->D,
+                                    std::max((long)ks_shape(n_qkv, p->D, d->M).slices * n_qkv,
+                                             (long)ks_shape(n_gu, p->D, d->M).slices * n_gu));
+    // (the LM head's partial sums cover only the logit rows: per-row size scaled to M below)
+    if (p->ksplit_lm)
+        ks_floats = std::max<long>(ks_floats, ((long)ks_shape(p->V, p->D, d->M_log).slices * p->V * d->M_log +
+                                               std::max(d->M, 1) - 1) / std::max(d->M, 1));
     const size_t M = (size_t)std::max(d->M, 1), ML = (size_t)std::max(d->M_log, 1);
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -751,7 +757,15 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             lm.logits = out->logits;
             lm.vocab = p.V;
             lm.parts = lmpart;
-            launch_gemm<DT, EPI_LOGITS>(VS_KERNEL_LMHEAD, lm, s);
+            if (p.ksplit_lm) {
+                const int slices = launch_ksplit<DT>(VS_KERNEL_LMHEAD, w->lm_head, w->lm_head, w->lm_head, p.V, 0, p.V,
+                                                     p.D, xf, p.D, p.M_log, ksp, s);
+                const long threads = (long)p.M_log * p.n_lm_parts;
+                hipLaunchKernelGGL(logits_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, ksp,
+                                   slices, p.M_log, p.V, out->logits, lmpart, p.n_lm_parts);
+            } else {
+                launch_gemm<DT, EPI_LOGITS>(VS_KERNEL_LMHEAD, lm, s);
+            }
         }
     }
     if (out->argmax || d->ctx_advance) {
