@@ -63,28 +63,53 @@ __global__ void __launch_bounds__(256) prep_embed_kernel(PrepArgs p) {
 }
 
 // y[r] = round(x[src] / sqrt(mean(x[src]^2) + eps) * gain), src = map ? map[r] : r
-// (a mapped row is clamped into [0, n_src)); one 256-thread workgroup per row,
-// fixed-order reduction. Used ahead of the MFMA path; the GEMV path normalises
-// inside its own prologue.
+// (a mapped row is clamped into [0, n_src)); one 1024-thread workgroup per row,
+// fixed-order reduction (per thread, per wave, then over the 16 waves in
+// order). Rows up to 4096 wide take one group of four features per thread, with
+// x and the gain requested together and kept in registers across the reduction.
+// Used ahead of the MFMA path; the GEMV path normalises inside its own prologue.
 template <int DT>
-__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* x, const int* map, int n_src, const void* gain,
-                                                      int D, float eps, void* y) {
+__global__ void __launch_bounds__(1024) rmsnorm_kernel(const float* x, const int* map, int n_src, const void* gain,
+                                                       int D, float eps, void* y) {
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
     const int src = map ? min(max(map[r], 0), n_src - 1) : r;
     const float* xr = x + (long)src * D;
+    __shared__ float wsum[16];
+    auto row_inv = [&](float ss) {
+#pragma unroll
+        for (int mask = 32; mask >= 1; mask >>= 1) ss += shfl_xor(ss, mask);
+        if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) tot += wsum[w];
+        return 1.0f / sqrtf(tot / (float)D + eps);
+    };
+    if (D <= 4 * 1024) {
+        const int k = tid * 4;
+        float4_t v = (float4_t){0.f, 0.f, 0.f, 0.f};
+        float gv[4] = {0.f, 0.f, 0.f, 0.f};
+        float ss = 0.f;
+        if (k < D) {
+            load_widen<DT, 4>(reinterpret_cast<const char*>(gain) + (long)k * St<DT>::bytes, gv);
+            v = *reinterpret_cast<const float4_t*>(xr + k);
+            ss = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+        }
+        const float inv = row_inv(ss);
+        if (k < D) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) store_round<DT>(y, (long)r * D + k + e, v[e] * inv * gv[e]);
+        }
+        return;
+    }
     float ss = 0.f;
-    for (int k = tid * 4; k < D; k += 256 * 4) {
+    for (int k = tid * 4; k < D; k += 1024 * 4) {
         const float4_t v = *reinterpret_cast<const float4_t*>(xr + k);
         ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     }
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) ss += shfl_xor(ss, mask);
-    __shared__ float wsum[4];
-    if ((tid & 63) == 0) wsum[tid >> 6] = ss;
-    __syncthreads();
-    const float inv = 1.0f / sqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)D + eps);
-    for (int k = tid * 4; k < D; k += 256 * 4) {
+    const float inv = row_inv(ss);
+    for (int k = tid * 4; k < D; k += 1024 * 4) {
         const float4_t v = *reinterpret_cast<const float4_t*>(xr + k);
         float gv[4];
         load_widen<DT, 4>(reinterpret_cast<const char*>(gain) + (long)k * St<DT>::bytes, gv);

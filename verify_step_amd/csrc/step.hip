@@ -588,7 +588,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             launch_gemv<DT, X_NORM, EPI_QKV>(VS_KERNEL_QKV, q, s);
         } else {
             if (!xn_ready)
-                hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
+                hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(1024), 0, s, x, (const int*)nullptr, p.M,
                                    lw.attn_norm, p.D, eps, xn);
             xn_ready = false;
             GemmArgs q = gm;
@@ -672,7 +672,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             launch_gemv<DT, X_NORM, EPI_SWIGLU>(VS_KERNEL_GATEUP, gu, s);
         } else {
             if (!xn_ready)
-                hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(256), 0, s, x, (const int*)nullptr, p.M,
+                hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M), dim3(1024), 0, s, x, (const int*)nullptr, p.M,
                                    lw.ffn_norm, p.D, eps, xn);
             xn_ready = false;
             GemmArgs gu = gm;
@@ -744,7 +744,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             lm.n_units = p.V;
             launch_gemv<DT, X_NORM, EPI_LOGITS>(VS_KERNEL_LMHEAD, lm, s);
         } else {
-            hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M_log), dim3(256), 0, s, x, d->logit_rows, p.M,
+            hipLaunchKernelGGL((rmsnorm_kernel<DT>), dim3(p.M_log), dim3(1024), 0, s, x, d->logit_rows, p.M,
                                w->final_norm, p.D, eps, xf);
             GemmArgs lm = gm;
             lm.w0 = w->lm_head;
