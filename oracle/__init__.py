@@ -12,7 +12,7 @@ blocking, fusion or reordering beyond each operation's definition. Every
 function cites the page and section it follows.
 
 Modules:
-  layers  -- RMSNorm, rotary embedding, standard and online-softmax
+  layers  -- RMSNorm, rotary embedding, standard and key-blockwise
              attention, tile-statistics merge, SiLU / SwiGLU, argmax + gap
   model   -- one decode / verify step over contiguous caches; byte counts
   accept  -- greedy acceptance, expected tokens per pass, rejection-sampling
@@ -24,7 +24,7 @@ pin that does not restate its own formula (printed page values, closed forms,
 library routines, invariants, brute force on tiny inputs).
 """
 from .accept import accept_greedy, expected_tokens_per_pass, rejection_output_dist  # noqa: F401
-from .layers import (argmax_lowest, attention_online, attention_standard, combine_partials,  # noqa: F401
+from .layers import (argmax_lowest, attention_blockwise, attention_standard, combine_partials,  # noqa: F401
                      linear, rmsnorm, rope, round_to, silu, swiglu)
 from .model import SeqState, StepResult, decode_step, kv_bytes_per_token, param_count  # noqa: F401
 from .model import streamed_weight_bytes  # noqa: F401

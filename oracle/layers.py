@@ -144,41 +144,55 @@ def attention_standard(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: 
     return (p / p.sum(dim=-1, keepdim=True)) @ v
 
 
-def attention_online(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int, mask: torch.Tensor | None = None,
-                     scale: float | None = None) -> torch.Tensor:
-    """The same function computed block by block over the keys.
+def key_block_stats(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: torch.Tensor | None, scale: float):
+    """Softmax statistics of one block of keys, relative to the block's own maximum.
 
-    [KV Cache] section 07: walk K and V in blocks; for each block form its
-    scores, raise the running maximum m to m', rescale the running sum l and
-    output O by exp(m - m'), add exp(S - m') and its product with V_j, and
-    divide O by l at the end. Works in the dtype of q (the pages run it in fp32
-    and in fp64 to show both agree to rounding).
+    For every query row: m = the largest scaled score in the block, l = the sum of
+    exp(s - m) over the block, o = the sum of exp(s - m) v over the block. A row
+    whose keys in the block are all masked has m = -inf and l = o = 0. Computes in
+    the dtype of its inputs. These are the per-block sufficient statistics that
+    [Serving Efficiency] section 31.4 (Example 31.2) merges instead of normalised
+    tile outputs.
     """
-    dt = q.dtype
+    s = (q @ k.transpose(-1, -2)) * scale
+    if keep is not None:
+        s = s.masked_fill(~keep, float("-inf"))
+    m = s.amax(dim=-1)
+    live = torch.isfinite(m)
+    e = torch.exp(s - torch.where(live, m, torch.zeros_like(m)).unsqueeze(-1))
+    e = torch.where(live.unsqueeze(-1), e, torch.zeros_like(e))
+    return m, e.sum(dim=-1), e @ v
+
+
+def attention_blockwise(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int,
+                        mask: torch.Tensor | None = None, scale: float | None = None) -> torch.Tensor:
+    """softmax(q k^T * scale) v computed from blocks of keys, never holding a whole score row.
+
+    [KV Cache] section 07: the online-softmax recurrence keeps a running maximum m and
+    a running sum l, shrinking the old sum by exp(m_old - m_new) whenever the maximum
+    grows, and FlashAttention applies the same factor to the accumulated output before
+    adding a block's part. Applied to whole blocks, the recurrence is the merge of
+    per-block statistics: every block's (m_b, l_b, o_b) is brought to the common
+    maximum by exp(m_b - max m) and the sums are added (combine_partials), then the
+    output is divided by the total sum. Works in the dtype of q (the pages run it in
+    fp32 and fp64 to show that both agree to rounding).
+
+    q: [..., n_q, d]; k, v: [..., n_k, d]; mask: bool [n_q, n_k], True = keep.
+    """
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
-    n_q, n_k = q.shape[-2], k.shape[-2]
-    m = torch.full(q.shape[:-1] + (1,), float("-inf"), dtype=dt)
-    l = torch.zeros(q.shape[:-1] + (1,), dtype=dt)
-    o = torch.zeros(q.shape[:-1] + (v.shape[-1],), dtype=dt)
-    for j in range(0, n_k, block):
-        kj, vj = k[..., j:j + block, :], v[..., j:j + block, :]
-        s = (q @ kj.transpose(-1, -2)) * scale
-        if mask is not None:
-            s = s.masked_fill(~mask[:, j:j + block], float("-inf"))
-        m_new = torch.maximum(m, s.amax(dim=-1, keepdim=True))
-        # a row whose keys in this block and before are all masked keeps m = -inf;
-        # exp(-inf - -inf) would be NaN, so those rows contribute nothing yet
-        safe = torch.where(torch.isinf(m_new), torch.zeros_like(m_new), m_new)
-        p = torch.exp(s - safe)
-        alpha = torch.exp(m - safe)
-        l = l * alpha + p.sum(dim=-1, keepdim=True)
-        o = o * alpha + p @ vj
-        m = m_new
-    return o / l
+    n_k = k.shape[-2]
+    stats = [key_block_stats(q, k[..., j0:j0 + block, :], v[..., j0:j0 + block, :],
+                             None if mask is None else mask[:, j0:j0 + block], scale)
+             for j0 in range(0, n_k, block)]
+    maxes = torch.stack([st[0] for st in stats])
+    sums = torch.stack([st[1] for st in stats])
+    outs = torch.stack([st[2] for st in stats])
+    return combine_partials(outs, sums, maxes, cdt=q.dtype)
 
 
-def combine_partials(nums: torch.Tensor, dens: torch.Tensor, maxes: torch.Tensor | None = None) -> torch.Tensor:
+def combine_partials(nums: torch.Tensor, dens: torch.Tensor, maxes: torch.Tensor | None = None,
+                     cdt: torch.dtype = F64) -> torch.Tensor:
     """Merge per-tile softmax statistics into one normalised output.
 
     [Serving Efficiency] section 31.4, Example 31.2: tiles are combined by
@@ -187,18 +201,21 @@ def combine_partials(nums: torch.Tensor, dens: torch.Tensor, maxes: torch.Tensor
     Flash-Decoding merge of [KV Cache] section 07: each split stores its
     log-sum-exp and the splits are merged with the online-softmax rescaling),
     tile t's numerator and denominator were computed relative to exp(-m_t) and
-    are first brought to the common scale exp(-max_t m_t).
+    are first brought to the common scale exp(-max_t m_t); a tile with
+    m_t = -inf (no key) carries weight 0.
 
-    nums: [T, ...d]; dens: [T]; maxes: [T] or None.
+    nums: [T, *S, d]; dens: [T, *S]; maxes: [T, *S] or None (S may be empty).
+    Computes in cdt (float64 by default) and returns that dtype.
     """
-    nums, dens = nums.to(F64), dens.to(F64)
+    nums, dens = nums.to(cdt), dens.to(cdt)
     if maxes is not None:
-        maxes = maxes.to(F64)
-        mstar = maxes.max()
-        w = torch.exp(maxes - mstar)
-        nums = nums * w.reshape((-1,) + (1,) * (nums.dim() - 1))
+        maxes = maxes.to(cdt)
+        mstar = maxes.amax(dim=0, keepdim=True)
+        w = torch.where(torch.isfinite(maxes), torch.exp(maxes - mstar), torch.zeros_like(maxes))
         dens = dens * w
-    return nums.sum(dim=0) / dens.sum(dim=0)
+        nums = nums * w.reshape(w.shape + (1,) * (nums.dim() - w.dim()))
+    den = dens.sum(dim=0)
+    return nums.sum(dim=0) / den.reshape(den.shape + (1,) * (nums.dim() - 1 - den.dim()))
 
 
 def silu(x: torch.Tensor, cdt: torch.dtype = F64) -> torch.Tensor:

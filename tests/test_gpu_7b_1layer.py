@@ -1,15 +1,19 @@
-"""Full-width, one-layer parity under the strict bounds: every row within 1e-2, greedy tokens exact.
+"""Full-width, one-layer parity: every row within the fixed 1e-2 bound, greedy tokens exact except at
+recorded near-ties.
 
 The 7B shape's widths (d_model 4096, 32 heads x 128, MLP 11008, vocab 32000),
 and the grouped-K/V widths of Llama 3.1 8B (32 query heads over 8 K/V heads of
-128, MLP 14336, vocab 128256; [KV Cache] sections 03 and 04), with a single layer, in
-fp16 and bf16: one layer keeps the rounding
-differences at the storage points from compounding, so the fixed bounds hold
-as stated -- logits and K/V rows within a maximum relative error of 1e-2, and
-every greedy token and accepted length exact except where the oracle's top-1
-minus top-2 logit gap is below 1e-3. Two launch shapes: 4 decode rows (the
-row-streaming GEMV path) and 8 sequences x 5 verify rows with fused
-acceptance (the MFMA tile path).
+128, MLP 14336, vocab 128256; [KV Cache] sections 03 and 04), with a single
+layer, in fp16 and bf16. One layer keeps the rounding differences at the
+storage points from compounding, so logits and K/V rows are held to the fixed
+maximum relative error of 1e-2 (no allowance from the oracle's fp32
+realisation). Greedy tokens and accepted lengths must be exact except on a
+row whose oracle top-1 minus top-2 logit gap is below that row's slack
+max(1e-3, 2 E_alt), where E_alt is the largest logit difference between the
+oracle's float64 and fp32 realisations of the row (taken from the oracle
+alone, never from the GPU). Four launch shapes: 4 decode rows (the
+row-streaming GEMV path), 8 sequences x 5 verify rows with fused acceptance,
+32 rows and 64 rows (the split-K tile path in each slice regime).
 """
 import dataclasses
 
@@ -20,7 +24,7 @@ import oracle
 import synth
 import verify_step_amd as vs
 from harness import GpuModel, GpuPool, SeqSpec, make_step
-from harness.compare import TOL, check_argmax, check_kv8, check_rows, first_divergence_is_near_tie, tie_slack
+from harness.compare import TOL, TieLog, check_kv8, check_rows, first_divergence_is_near_tie, tie_slack
 from synth import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -39,7 +43,7 @@ MODELS = {"7B": W.LLAMA7B, "8B-GQA": W.GQA8B}
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("B,K", [(4, 1), (8, 5), (32, 1), (16, 4)])
 def test_7b_width_one_layer_strict(shape, dtype, B, K):
-    """Full-width single layer against the oracle under the strict bounds: 4 rows (GEMV path), 40
+    """Full-width single layer against the oracle under the fixed bounds: 4 rows (GEMV path), 40
     (split-K, 1024-element slices), 32 (split-K, two workgroups per CU) and 64 (768-element slices)."""
     _run(shape, dtype, None, B, K)
 
@@ -75,24 +79,23 @@ def _run(shape, dtype, kv8, B, K):
         full[:, :, :ctxs[b]] = kv
         states.append(oracle.SeqState(full, ctxs[b], list(toks)))
         specs.append(SeqSpec(ctxs[b], list(toks)))
+    states32 = [oracle.SeqState(st.kv.clone(), st.ctx, list(st.tokens)) for st in states]  # fp32 realisation
     g0 = [int(t) for t in synth.uniform_int(synth.key(SEED_TOK, 7, B), 0, B, 0, dims.vocab)] if K > 1 else None
     sb = make_step(model, pool, specs, rows, max_blocks=max_blocks, g0=g0)
     vs.decode_step(sb.desc, sb.block_tables, model.w, sb.out, sb.ws, sb.ws_bytes,
                    torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     ref = oracle.decode_step(dims, w_cpu, states)
+    alt = oracle.decode_step(dims, w_cpu, states32, compute="f32")
     tol = TOL[dtype]
     M = B * K
     worst = check_rows([sb.logits[r].cpu() for r in range(M)], ref.logits, tol, "logits")
     am = sb.argmax[:M].cpu().tolist()
-    # a differing token only where the oracle's top-2 gap is under the row's slack max(1e-3, 2 E), E
-    # the row's largest logit difference (at bf16, 32 rows over a 128256-token vocabulary meet gaps of
-    # a few 1e-3 that the oracle's own fp32 realisation resolves the other way as well)
-    slack = [tie_slack(sb.logits[r].cpu(), ref.logits[r]) for r in range(M)]
-    n_tie = 0
+    # a differing token only where the oracle's top-2 gap is under the row's slack max(1e-3, 2 E_alt)
+    slack = [tie_slack(alt.logits[r], ref.logits[r]) for r in range(M)]
+    ties = TieLog()
     for r in range(M):
-        n_tie += not check_argmax(am[r], ref.argmax[r], ref.logits[r], ref.gap[r], f"row {r}",
-                                  gpu_logits=sb.logits[r].cpu())
+        ties.check(am[r], ref.argmax[r], ref.logits[r], ref.gap[r], f"row {r}", alt.logits[r])
     for b in range(B):
         if kv8:
             check_kv8(pool.read(rows[b], ctxs[b], ctxs[b] + K), states[b].kv[:, :, ctxs[b]:ctxs[b] + K], f"seq {b} K/V")
@@ -109,6 +112,7 @@ def _run(shape, dtype, kv8, B, K):
             if (acc[b], bon[b]) != want:
                 assert first_divergence_is_near_tie(am[rs], ref.argmax[rs], ref.gap[rs], slack[rs])
     e_abs = max(float((sb.logits[r].cpu().double() - ref.logits[r]).abs().max()) for r in range(M))
-    _say(f"{shape} width 1 layer {dtype} cache {kv8 or dtype} B={B} K={K}: worst logits {worst:.2e} relative, {e_abs:.2e} absolute, "
-         f"{n_tie} near-tie rows")
+    e_alt = max(float((alt.logits[r] - ref.logits[r]).abs().max()) for r in range(M))
+    _say(f"{shape} width 1 layer {dtype} cache {kv8 or dtype} B={B} K={K}: worst logits {worst:.2e} relative, "
+         f"{e_abs:.2e} absolute (fp32 oracle {e_alt:.2e}); {ties.report()}")
     pool.close()

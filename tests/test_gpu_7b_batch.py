@@ -23,7 +23,7 @@ import oracle
 import synth
 import verify_step_amd as vs
 from harness import GpuModel, GpuPool, SeqSpec, make_step
-from harness.compare import TOL, check_argmax, check_rows
+from harness.compare import TOL, TieLog, check_rows
 from synth import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -91,16 +91,18 @@ def _run_and_check(dims, w_cpu, model, pool, seqs, what):
     alt = oracle.decode_step(dims, w_cpu, [seqs[i].state32 for i in samp], compute="f32")
     tol = TOL[dims.dtype]
     am = sb.argmax[:len(seqs)].cpu().tolist()
+    ties = TieLog()
     for j, i in enumerate(samp):
         s = seqs[i]
         check_rows([sb.logits[i].cpu()], [ref.logits[j]], tol, f"{what} seq {i} logits", [alt.logits[j]])
-        check_argmax(am[i], ref.argmax[j], ref.logits[j], ref.gap[j], f"{what} seq {i}", sb.logits[i])
+        ties.check(am[i], ref.argmax[j], ref.logits[j], ref.gap[j], f"{what} seq {i}", alt.logits[j])
         got = pool.read(s.row, s.ctx, s.ctx + 1).double()
         want = s.state.kv[:, :, s.ctx:s.ctx + 1].double()
         want32 = s.state32.kv[:, :, s.ctx:s.ctx + 1].double()
         for l in range(dims.n_layers):
             check_rows([got[l, t, 0] for t in range(2)], [want[l, t, 0] for t in range(2)], tol,
                        f"{what} seq {i} layer {l} K/V", [want32[l, t, 0] for t in range(2)])
+    _say(f"{what}: {ties.report()}")
     return am
 
 

@@ -20,7 +20,7 @@ import oracle
 import synth
 import verify_step_amd as vs
 from harness import GpuModel, GpuPool, SeqSpec, make_step, model_desc
-from harness.compare import TOL, check_argmax, check_rows
+from harness.compare import TOL, TieLog, check_rows
 from synth import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -36,12 +36,12 @@ def _say(msg):
     print(f"[gpu-case] {msg}", flush=True)
 
 
-def check_step(dims, sb, ref, alt, what):
+def check_step(dims, sb, ref, alt, what, ties):
     tol = TOL[dims.dtype]
     am = int(sb.argmax[0])
     gap = float(sb.gap[0])
     check_rows([sb.logits[0].cpu()], [ref.logits[0]], tol, f"{what} logits", [alt.logits[0]])
-    exact = check_argmax(am, ref.argmax[0], ref.logits[0], ref.gap[0], what, sb.logits[0])
+    exact = ties.check(am, ref.argmax[0], ref.logits[0], ref.gap[0], what, alt.logits[0])
     if exact:
         assert abs(gap - ref.gap[0]) <= tol * float(ref.logits[0].abs().max()), (gap, ref.gap[0])
     return am
@@ -94,6 +94,7 @@ def test_7b_decode_b1_graph_replays_match_oracle():
         state["row"], state["len"] = r, cur
 
     graph = None
+    ties = TieLog()
     for step in range(3):
         pos = CTX0 + step
         _say(f"7B fp16 decode B=1 step {step} at position {pos} ({'graph replay' if step else 'eager'})")
@@ -113,7 +114,7 @@ def test_7b_decode_b1_graph_replays_match_oracle():
             torch.cuda.synchronize()
         ref = oracle.decode_step(dims, w_cpu, [st])
         alt = oracle.decode_step(dims, w_cpu, [st32], compute="f32")
-        am = check_step(dims, sb, ref, alt, f"step {step}")
+        am = check_step(dims, sb, ref, alt, f"step {step}", ties)
         got = pool.read(state["row"], pos, pos + 1).double()
         want = st.kv[:, :, pos:pos + 1].double()
         want32 = st32.kv[:, :, pos:pos + 1].double()
@@ -127,4 +128,5 @@ def test_7b_decode_b1_graph_replays_match_oracle():
         if step > 0:
             bookkeeping()
     assert torch.equal(pool.read(state["row"], 0, CTX0), kv0), "the step must not touch cached positions"
+    _say(f"7B fp16 decode B=1: {ties.report()}")
     pool.close()

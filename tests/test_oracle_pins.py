@@ -55,7 +55,7 @@ def test_example_31_2_through_attention_with_running_maxima():
     q = torch.ones(1, 1, dtype=torch.float64)
     k = torch.log(w).reshape(4, 1)
     assert float(L.attention_standard(q, k, v, scale=1.0)) == pytest.approx(g["output"], abs=1e-15)
-    assert float(L.attention_online(q, k, v, block=2, scale=1.0)) == pytest.approx(g["output"], abs=1e-15)
+    assert float(L.attention_blockwise(q, k, v, block=2, scale=1.0)) == pytest.approx(g["output"], abs=1e-15)
     # per-tile (max, num, den) relative to the tile's own max, merged with rescaling
     nums, dens, maxes = [], [], []
     for a, b in g["tiles"]:
@@ -79,7 +79,7 @@ def test_online_and_standard_agree_to_fp32_rounding_as_printed():
     mask = torch.ones(n, n, dtype=torch.bool).tril()
     ref64 = L.attention_standard(q.double(), k.double(), v.double(), mask)
     std = L.attention_standard(q, k, v, mask)
-    onl = L.attention_online(q, k, v, g["block"], mask)
+    onl = L.attention_blockwise(q, k, v, g["block"], mask)
     sdpa = F.scaled_dot_product_attention(q, k, v, is_causal=True)
     errs = {
         "standard_fp32": float((std.double() - ref64).abs().max()),
@@ -91,7 +91,7 @@ def test_online_and_standard_agree_to_fp32_rounding_as_printed():
         assert printed / 10 < errs[name] < printed * 10, (name, errs[name])
     assert torch.allclose(onl, std, atol=g["printed_allclose_atol"])
     # in float64 the two orders agree to float64 rounding
-    onl64 = L.attention_online(q.double(), k.double(), v.double(), g["block"], mask)
+    onl64 = L.attention_blockwise(q.double(), k.double(), v.double(), g["block"], mask)
     assert float((onl64 - ref64).abs().max()) < 1e-13
 
 
@@ -235,7 +235,7 @@ def _emitted(drafts, g0, row_argmax):
     return n, list(drafts[:n]) + [bonus]
 
 
-@pytest.mark.parametrize("K", [1, 2, 3, 4])
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 5])
 def test_greedy_acceptance_brute_force(K):
     """Exhaustive check over drafts, g0 and row argmaxes in {0,1,2}.
 

@@ -8,7 +8,8 @@ so the test keeps a bijection between them, fixed when pages are handed out,
 and compares reference counts, free counts, table lengths and every
 accept / reject decision. The pool here sits on a host buffer that no call
 touches: forks happen only at page boundaries, where an append never needs a
-device copy (copy-on-write is exercised on the GPU).
+device copy. The library's copy-on-write runs on the GPU (tests/test_gpu_tiny.py);
+the oracle's copy-on-write rule is worked by hand in the last test below.
 """
 import ctypes
 import os
@@ -200,3 +201,58 @@ def test_alloc_is_all_or_nothing(L):
     assert sorted(a + b) == list(range(8))
     assert vs.kv_refcount(P.h, 8) == -1 and vs.kv_refcount(P.h, -1) == -1
     P.close()
+
+
+def test_pool_model_copy_on_write_of_a_shared_partial_block():
+    """The oracle's copy-on-write rule, worked by hand ([KV Cache] section 05, "Block sharing and
+    copy-on-write"; [Serving Efficiency] section 31.3): a sequence about to write into a partly filled
+    last block that another sequence also references first copies it to a fresh page and writes there;
+    a full block is never written again, so it stays shared; a new block is taken only when the last
+    one is full. Pages are handed out lowest id first, so every id and count below is fixed."""
+    m = oracle.PoolModel(8, T)
+    a = m.alloc(2)  # A holds 20 tokens: page 0 full, page 1 with 4 of 16 slots
+    assert a == [0, 1]
+    assert m.share(a)  # B forks A after 20 tokens
+    assert [m.refcount(p) for p in range(8)] == [2, 2, 0, 0, 0, 0, 0, 0]
+
+    # B appends 3 tokens (positions 20..22): its last block is shared and partly filled
+    tb, copies = m.append(a, 20, 3)
+    assert tb == [0, 2] and copies == [(1, 2)]  # page 1's slots go to page 2, B writes there
+    assert [m.refcount(p) for p in range(8)] == [2, 1, 1, 0, 0, 0, 0, 0]
+
+    # A's last block is now its own: no copy; positions 20..32 fill page 1 and open page 3
+    ta, copies = m.append(a, 20, 13)
+    assert ta == [0, 1, 3] and copies == []
+    assert [m.refcount(p) for p in range(8)] == [2, 1, 1, 1, 0, 0, 0, 0]
+
+    # C forks A at the page boundary (16 tokens): the shared block is full, so appending takes a new
+    # page and copies nothing; the full block stays shared three ways
+    assert m.share([0])
+    tc, copies = m.append([0], 16, 5)
+    assert tc == [0, 4] and copies == []
+    assert [m.refcount(p) for p in range(8)] == [3, 1, 1, 1, 1, 0, 0, 0]
+
+    # appending nothing to a shared partial block copies nothing
+    assert m.share([0, 2])  # D forks B after 23 tokens (page 2 holds 7)
+    assert m.append([0, 2], 23, 0) == ([0, 2], [])
+    assert [m.refcount(p) for p in range(8)] == [4, 1, 2, 1, 1, 0, 0, 0]
+
+    # with no free page the copy cannot be made: the append fails and changes nothing
+    assert m.alloc(3) == [5, 6, 7] and m.num_free() == 0
+    before = [m.refcount(p) for p in range(8)]
+    assert m.append([0, 2], 23, 1) is None
+    assert [m.refcount(p) for p in range(8)] == before
+
+    # one page freed: the copy goes there, and B alone holds page 2 again
+    assert m.free([7])
+    td, copies = m.append([0, 2], 23, 1)
+    assert td == [0, 7] and copies == [(2, 7)]
+    assert [m.refcount(p) for p in range(8)] == [4, 1, 1, 1, 1, 1, 1, 1]
+
+    # a copy plus further pages in one append: E forks C after 21 tokens and appends 30 (positions
+    # 21..50 need ceil(51 / 16) = 4 pages: the copy of page 4 and two new ones, three free pages)
+    assert m.free([3, 5, 6])
+    assert m.share([0, 4])
+    te, copies = m.append([0, 4], 21, 30)
+    assert te == [0, 3, 5, 6] and copies == [(4, 3)]
+    assert [m.refcount(p) for p in range(8)] == [5, 1, 1, 1, 1, 1, 1, 1]

@@ -14,7 +14,6 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libverify_step.so")
 SOURCES = ["step.hip", "pool.cpp"]
-HEADERS = ["common.h", "gemm.h", "attention.h", "misc.h", "error.h"]
 
 
 def hipcc() -> str:
@@ -52,14 +51,6 @@ def build(verbose: bool = False) -> str:
         print("\n".join(msgs))
     os.replace(tmp, LIB)
     return LIB
-
-
-def sources_newer_than_lib() -> bool:
-    if not os.path.exists(LIB):
-        return True
-    t = os.path.getmtime(LIB)
-    paths = [os.path.join(CSRC, s) for s in SOURCES + HEADERS] + [os.path.join(ROOT, "include", "verify_step.h")]
-    return any(os.path.getmtime(p) > t for p in paths if os.path.exists(p))
 
 
 if __name__ == "__main__":
