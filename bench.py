@@ -107,7 +107,7 @@ def main():
     dev = torch.device("cuda:0")
     dims = W.LLAMA7B  # fp16
     K, Wm = args.steps, args.warmup
-    total_len = CTX0 + Wm + K + min(K, ROOFLINE_STEPS) + 1  # every position a step of this run writes
+    total_len = CTX0 + Wm + K + len(TIMED_KINDS) * min(K, ROOFLINE_STEPS) + 1  # every position this run writes
 
     # ---- weights (generated on the host, one tensor at a time) ----
     t0 = time.time()
@@ -204,24 +204,21 @@ def main():
     ms_step = ms_total / K
     log(f"timed {K} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / K:.3f} ms/step)")
 
-    # ---- dominant kernel: gate/up GEMV, each launch timed by its own dispatch events ----
-    # (a graph hides its nodes from events, so this window runs the same step eagerly)
+    # ---- per-kernel times from dispatch events: every launch of each kernel kind in n_rf eager steps
+    # after the timed window (a graph hides its nodes from events) ----
     n_rf = min(K, ROOFLINE_STEPS)
-    n_tk = dims.n_layers * n_rf
-    ev = HipEvents(n_tk)
-    vs.vs_time_kernel(vs.VS_KERNEL["gateup"], ev.start, ev.stop, n_tk)
-    for _ in range(n_rf):
+
+    def eager():
         device_step()
         host_bookkeeping()
-    torch.cuda.synchronize()
-    n_done = vs.vs_timed_launches()
-    vs.vs_time_kernel(0, None, None, 0)
-    durs = [ev.elapsed_ms(i) for i in range(n_done)]
-    ev.close()
-    gu_ms = sum(durs) / len(durs)
+
+    kt = kernel_times(vs, eager, n_rf, 4 * dims.n_layers)
+    gu_launches = kt["gateup"]["launch_us"]
+    gu_ms = sum(gu_launches) / len(gu_launches) / 1e3
     gu_bytes = 2 * dims.ffn * dims.d_model * dims.elem_bytes  # W_gate + W_up, read once per launch
     gu_gbps = gu_bytes / (gu_ms * 1e-3) / 1e9
     traffic = measured_traffic(GATEUP_TRAFFIC_PROFILE)
+    n_done = len(gu_launches)
 
     # ---- byte accounting for the whole step ----
     wbytes = streamed_weight_bytes(dims)
@@ -271,6 +268,8 @@ def main():
             "launches_timed": n_done,
             "timing": f"dispatch events of every gate/up launch in {n_rf} eager steps after the timed window",
         },
+        "weight_stream": weight_stream(dims, kt, n_rf),
+        "attention": attention_stream(kt, n_rf, avg_keys * kvpt + kvpt),
     }
 
     if args.copy_calibration:
@@ -393,6 +392,8 @@ def other_workload(args):
     kvpt = 2 * dims.n_layers * dims.n_kv_heads * dims.head_dim * dims.kv_elem_bytes
     kv_read = sum(s.ctx + len(s.tokens) for s in specs) * kvpt  # logical K/V bytes the attention reads
     step_bytes = streamed_weight_bytes(dims) + kv_read + M * kvpt
+    n_rf = min(args.steps, ROOFLINE_STEPS)
+    kt = kernel_times(vs, step, n_rf, 8 * dims.n_layers)
     result = {
         "workload": args.workload, "dtype": dt, "batch": B, "rows": M, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "rows_per_s": round(M * 1000.0 / ms, 1),
@@ -400,7 +401,11 @@ def other_workload(args):
         "step_frac_of_hbm_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "contexts": [min(ctxs), max(ctxs)], "prompt_chunk_rows": chunk, "model_shape": dims.name,
         "kv_cache": dims.kv_type,
+        "weight_stream": weight_stream(dims, kt, n_rf),
+        "attention": attention_stream(kt, n_rf, kv_read + M * kvpt),
     }
+    if args.copy_calibration:
+        copy_calibration()
     print(json.dumps(result), flush=True)
 
 
@@ -483,6 +488,55 @@ def sample_workload(args):
         "timing": "call: torch events around the timed calls; kernels: dispatch events of each launch",
     }
     print(json.dumps(result), flush=True)
+
+
+# kernel kinds timed per step: the weight products (a split-K product's slice reduction counts with it),
+# attention and the standalone split merge
+TIMED_KINDS = ["gateup", "qkv", "oproj", "down", "lmhead", "attn", "merge"]
+PRODUCT_KINDS = ["qkv", "oproj", "gateup", "down", "lmhead"]
+
+
+def kernel_times(vs, run_step, n_steps, per_step_cap):
+    """Dispatch-event durations of every launch of each kind in TIMED_KINDS over n_steps calls of
+    run_step (one pass of n_steps per kind)."""
+    import torch
+
+    out = {}
+    for kind in TIMED_KINDS:
+        cap = n_steps * per_step_cap
+        ev = HipEvents(cap)
+        vs.vs_time_kernel(vs.VS_KERNEL[kind], ev.start, ev.stop, cap)
+        for _ in range(n_steps):
+            run_step()
+        torch.cuda.synchronize()
+        n = vs.vs_timed_launches()
+        vs.vs_time_kernel(0, None, None, 0)
+        assert n < cap, f"{kind}: more launches than the event capacity"
+        out[kind] = {"launch_us": [ev.elapsed_ms(i) * 1e3 for i in range(n)]}
+        ev.close()
+    return out
+
+
+def weight_stream(dims, kt, n_steps):
+    """The weights every step streams once, over the summed time of the product kernels per step (and
+    the slice reductions of split-K products), against the HBM peak."""
+    per_kind = {k: sum(kt[k]["launch_us"]) / n_steps for k in PRODUCT_KINDS}
+    us = sum(per_kind.values())
+    wbytes = streamed_weight_bytes(dims)
+    gbps = wbytes / (us * 1e-6) / 1e9
+    return {"bytes_per_step": wbytes, "product_us_per_step": round(us, 2), "achieved": round(gbps, 1),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "us_per_step_by_kind": {k: round(v, 2) for k, v in per_kind.items()},
+            "timing": f"dispatch events of every product and slice-reduction launch in {n_steps} eager steps"}
+
+
+def attention_stream(kt, n_steps, kv_bytes):
+    """Logical K/V bytes per step (every cached key and value the step's rows attend to, plus the rows
+    written) over the attention and merge kernels' time per step."""
+    us = (sum(kt["attn"]["launch_us"]) + sum(kt["merge"]["launch_us"])) / n_steps
+    gbps = kv_bytes / (us * 1e-6) / 1e9
+    return {"kv_bytes_per_step": int(kv_bytes), "us_per_step": round(us, 2), "achieved": round(gbps, 1),
+            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
 def streamed_weight_bytes(dims):

@@ -312,7 +312,9 @@ vs_status verify_sample(int32_t B, int32_t M, int32_t V, const int32_t* q_start,
 
 /* ------------------------------------------------------------------ instrumentation */
 
-/* Kernel kinds of one step, for timing. */
+/* Kernel kinds of one step, for timing. Where a product runs as split-K
+ * partial sums, the kernel that adds the slices and runs the product's
+ * epilogue is timed with the product's kind. */
 #define VS_KERNEL_NONE 0
 #define VS_KERNEL_QKV 1       /* QKV product + rotary + K/V page write */
 #define VS_KERNEL_ATTN 2      /* paged split-KV attention */

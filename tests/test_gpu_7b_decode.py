@@ -16,6 +16,7 @@ the GPU's token (the oracle is fed the same token).
 import pytest
 import torch
 
+import bench
 import oracle
 import synth
 import verify_step_amd as vs
@@ -27,9 +28,9 @@ pytestmark = pytest.mark.gpu
 
 SEED_W, SEED_KV, SEED_TOK, SEED_PAGES = 2001, 2002, 2003, 2006
 CTX0 = 2048
-# positions the benchmark's default run reaches (2048 + 16 warm-up + 256 timed + 8 timing steps + 1); the
-# descriptor's max_ctx sets the key-split plan, so the test uses the benchmark's value
-CAPACITY = CTX0 + 16 + 256 + 8 + 1
+# positions the benchmark's default run reaches (2048 + 16 warm-up + 256 timed + the per-kernel timing
+# steps + 1); the descriptor's max_ctx sets the key-split plan, so the test uses the benchmark's value
+CAPACITY = CTX0 + 16 + 256 + len(bench.TIMED_KINDS) * bench.ROOFLINE_STEPS + 1
 
 
 def _say(msg):

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <string>
+#include <tuple>
 
 #include "../../include/verify_step.h"
 #include "attention.h"
@@ -61,6 +62,25 @@ void launch1(int kind, void (*kern)(T), dim3 grid, dim3 block, size_t lds, hipSt
     } else {
         (void)hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, lds, s);
     }
+}
+
+// The same for a kernel of several arguments (the split-K reductions, timed with their product's kind).
+template <typename... P, typename... A>
+void launchn(int kind, void (*kern)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s, A... args) {
+    std::tuple<P...> packed(static_cast<P>(args)...);
+    std::apply(
+        [&](auto&... e) {
+            void* argv[] = {static_cast<void*>(&e)...};
+            if (kind != VS_KERNEL_NONE && g_timer.kind == kind && g_timer.count < g_timer.capacity) {
+                const int i = g_timer.count++;
+                (void)hipExtLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, lds, s,
+                                         static_cast<hipEvent_t>(g_timer.start[i]),
+                                         static_cast<hipEvent_t>(g_timer.stop[i]), 0);
+            } else {
+                (void)hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, lds, s);
+            }
+        },
+        packed);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -342,10 +362,10 @@ void launch_resid_ksplit(int kind, const void* w, int N, int K, const void* act,
     } else {
     const int slices = launch_ksplit<DT>(kind, w, w, w, N, 0, N, K, act, act_ld, M, part, s);
     if (gain) {
-        hipLaunchKernelGGL((resid_norm_kernel<DT>), dim3(M), dim3(1024), 0, s, x, part, slices, M, N, gain, eps, y);
+        launchn(kind, resid_norm_kernel<DT>, dim3(M), dim3(1024), 0, s, x, part, slices, M, N, gain, eps, y);
     } else {
         const long groups = (long)M * ((N + 3) / 4);
-        hipLaunchKernelGGL(resid_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, x, x_ld,
+        launchn(kind, resid_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, x, x_ld,
                            part, slices, M, N);
     }
     }
@@ -609,7 +629,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
                 const int slices = launch_ksplit<DT>(VS_KERNEL_QKV, lw.wq, lw.wk, lw.wv, q.n0, q.n1, N, p.D, xn, p.D,
                                                      p.M, ksp, s);
                 const long threads = (long)p.M * (p.H + 2 * p.Hkv) * (p.Dh / 2);
-                hipLaunchKernelGGL((qkv_reduce_kernel<DT>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                launchn(VS_KERNEL_QKV, qkv_reduce_kernel<DT>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                                    q, ksp, slices, N);
             } else {
                 launch_gemm<DT, EPI_QKV>(VS_KERNEL_QKV, q, s);
@@ -690,7 +710,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
                 const int slices = launch_ksplit<DT>(VS_KERNEL_GATEUP, lw.wg, lw.wu, lw.wu, p.F, p.F, 2 * p.F, p.D, xn,
                                                      p.D, p.M, ksp, s);
                 const long threads = (long)p.M * p.F;
-                hipLaunchKernelGGL((swiglu_reduce_kernel<DT>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                launchn(VS_KERNEL_GATEUP, swiglu_reduce_kernel<DT>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                                    s, ksp, slices, p.M, p.F, hmid, p.F);
             } else {
                 launch_gemm<DT, EPI_SWIGLU>(VS_KERNEL_GATEUP, gu, s);
@@ -761,7 +781,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
                 const int slices = launch_ksplit<DT>(VS_KERNEL_LMHEAD, w->lm_head, w->lm_head, w->lm_head, p.V, 0, p.V,
                                                      p.D, xf, p.D, p.M_log, ksp, s);
                 const long threads = (long)p.M_log * p.n_lm_parts;
-                hipLaunchKernelGGL(logits_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, ksp,
+                launchn(VS_KERNEL_LMHEAD, logits_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, ksp,
                                    slices, p.M_log, p.V, out->logits, lmpart, p.n_lm_parts);
             } else {
                 launch_gemm<DT, EPI_LOGITS>(VS_KERNEL_LMHEAD, lm, s);
@@ -789,42 +809,58 @@ extern "C" vs_status decode_step_workspace_bytes(const vs_batch_desc* desc, cons
     return vs_ok();
 }
 
-extern "C" vs_status decode_step(const vs_batch_desc* desc, const int32_t* block_tables, const vs_weights* weights,
-                                 const vs_step_out* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+// Argument checks shared by decode_step and decode_step_noalloc; fills the plan.
+vs_status check_step(const vs_batch_desc* desc, const int32_t* block_tables, const vs_weights* weights,
+                     const vs_step_out* out, Plan* p) {
     if (!desc || !weights || !out) return vs_fail(VS_ERR_INVALID, "decode_step: null argument");
-    Plan p;
-    vs_status st = make_plan(desc, &weights->dims, &p);
+    vs_status st = make_plan(desc, &weights->dims, p);
     if (st != VS_OK) return st;
-    if (p.M == 0) return vs_ok();
+    if (p->M == 0) return vs_ok();
     if (!desc->pool || !desc->q_start || !desc->ctx_len || !desc->tokens || !block_tables)
         return vs_fail(VS_ERR_INVALID, "decode_step: pool, q_start, ctx_len, tokens and block_tables are required");
-    if (p.M_log > 0 && (!desc->logit_rows || !out->argmax))
+    if (p->M_log > 0 && (!desc->logit_rows || !out->argmax))
         return vs_fail(VS_ERR_INVALID, "decode_step: logit rows need logit_rows and out->argmax");
     const bool fused = out->accept_len || out->bonus || out->g0;
     if (fused && !(out->accept_len && out->bonus && out->g0 && out->argmax))
         return vs_fail(VS_ERR_INVALID, "decode_step: fused acceptance needs g0, accept_len, bonus and argmax");
     if (!weights->embed || !weights->final_norm || !weights->lm_head || !weights->layers)
         return vs_fail(VS_ERR_INVALID, "decode_step: missing weight pointer");
-    for (int l = 0; l < p.L; ++l) {
+    for (int l = 0; l < p->L; ++l) {
         const vs_layer_weights& lw = weights->layers[l];
         if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.wg || !lw.wu || !lw.wd)
             return vs_fail(VS_ERR_INVALID, "decode_step: missing weight pointer in layer " + std::to_string(l));
     }
     const vs_pool_desc* pg = vs_pool_geometry(desc->pool);
-    if (pg->page_tokens != kPageTokens || pg->n_layers != p.L || pg->n_kv_heads != p.Hkv || pg->head_dim != p.Dh)
+    if (pg->page_tokens != kPageTokens || pg->n_layers != p->L || pg->n_kv_heads != p->Hkv || pg->head_dim != p->Dh)
         return vs_fail(VS_ERR_SHAPE, "decode_step: pool geometry does not match the model");
     const bool kv8 = pg->dtype == VS_FP8_E4M3 || pg->dtype == VS_FP8_E5M2;
-    if (pg->dtype != p.dt && !(kv8 && p.dt != VS_F32 && p.Dh == 128))
+    if (pg->dtype != p->dt && !(kv8 && p->dt != VS_F32 && p->Dh == 128))
         return vs_fail(VS_ERR_SHAPE, "decode_step: the pool's dtype must be the model's, or an 8-bit float for an "
                                      "fp16 / bf16 model with head_dim 128");
-    if (!ws || ws_bytes < p.total)
-        return vs_fail(VS_ERR_SHAPE, "decode_step: workspace needs " + std::to_string(p.total) + " bytes");
-    char* w = static_cast<char*>(ws);
+    return vs_ok();
+}
+
+vs_status run_checked(const Plan& p, const vs_batch_desc* desc, const int32_t* block_tables,
+                      const vs_weights* weights, const vs_step_out* out, char* w, hipStream_t stream) {
     switch (p.dt) {
         case VS_F32: return run_step<F32>(p, desc, block_tables, weights, out, w, stream);
         case VS_F16: return run_step<F16>(p, desc, block_tables, weights, out, w, stream);
         default: return run_step<BF16>(p, desc, block_tables, weights, out, w, stream);
     }
+}
+
+}  // namespace
+
+extern "C" vs_status decode_step(const vs_batch_desc* desc, const int32_t* block_tables, const vs_weights* weights,
+                                 const vs_step_out* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    Plan p;
+    vs_status st = check_step(desc, block_tables, weights, out, &p);
+    if (st != VS_OK || p.M == 0) return st;
+    if (!ws || ws_bytes < p.total)
+        return vs_fail(VS_ERR_SHAPE, "decode_step: workspace needs " + std::to_string(p.total) + " bytes");
+    return run_checked(p, desc, block_tables, weights, out, static_cast<char*>(ws), stream);
 }
 
 extern "C" vs_status verify_accept(int32_t B, const int32_t* q_start, const int32_t* drafts, const int32_t* g0,
