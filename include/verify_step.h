@@ -263,6 +263,23 @@ vs_status decode_step_workspace_bytes(const vs_batch_desc* desc, const vs_model_
 vs_status decode_step(const vs_batch_desc* desc, const int32_t* block_tables, const vs_weights* weights,
                       const vs_step_out* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* decode_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same step and the same kernels, with the workspace taken from a scratch
+ * array the library holds in device memory, VS_NOALLOC_SCRATCH_BYTES per GPU,
+ * from the first call on that GPU until the process ends. The caller still
+ * owns every input and output. Allocates nothing: no hipMalloc, hipFree or
+ * allocating library routine. Returns VS_ERR_SHAPE, before enqueueing
+ * anything, when decode_step_workspace_bytes for this batch exceeds the array
+ * (every batch of up to 64 rows of the 7B shape fits; a large-vocabulary model
+ * at 64 rows does not). Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (two streams, two threads) race and give
+ * undefined results; calls serialised on one stream are safe. Nothing in the
+ * array needs to start at zero. The current device must be the stream's. */
+#define VS_NOALLOC_SCRATCH_BYTES (96u << 20)
+vs_status decode_step_noalloc(const vs_batch_desc* desc, const int32_t* block_tables, const vs_weights* weights,
+                              const vs_step_out* out, hipStream_t stream);
+
 /* Greedy acceptance of a verify pass ([Serving Efficiency] section 31.5;
  * [Spending the Idle] section 12.4; [KV Cache] section 08). For sequence b
  * with rows r0 = q_start[b] .. r0+K-1 holding drafts d_1..d_K (the row

@@ -107,3 +107,34 @@ def test_verify_accept_rejects_null(L):
     with pytest.raises(vs.VSError):
         vs.verify_accept(3, None, None, None, None, None, None, 0)
     vs.verify_accept(0, None, None, None, None, None, None, 0)  # nothing to do
+
+
+def test_noalloc_step_rejects_before_launching(L):
+    """decode_step_noalloc checks its arguments and its scratch limit on the host: a null argument is
+    VS_ERR_INVALID, and a batch whose workspace exceeds the library's scratch array is VS_ERR_SHAPE,
+    both before any device call."""
+    dims = vs.vs_model_desc(256, 4, 4, 64, 1024, 1000, 1, vs.VS_F32, 10000.0, 1e-5)
+    desc = vs.vs_batch_desc(4, 4, 4, 1, 65, 5, None, None, None, None, None)
+    with pytest.raises(vs.VSError) as e:
+        vs.decode_step_noalloc(desc, None, vs.vs_weights(dims, None, None, None, None), vs.vs_step_out(), 0)
+    assert e.value.status == vs.VS_ERR_INVALID
+    # 64 rows of a 32-layer model with a 128256-token vocabulary: the LM head's split-K partial sums
+    # alone need more than the scratch array holds
+    big = vs.vs_model_desc(4096, 32, 8, 128, 14336, 128256, 32, vs.VS_BF16, 10000.0, 1e-5)
+    pdesc = vs.vs_pool_desc(1, 16, 32, 8, 128, vs.VS_BF16)
+    nbytes = vs.kv_page_bytes(pdesc)
+    buf = ctypes.create_string_buffer(nbytes)
+    pool = vs.kv_pool_create(pdesc, ctypes.addressof(buf), nbytes)
+    try:
+        fake = 4096  # non-null stand-ins: nothing is dereferenced before the size check
+        layers = (vs.vs_layer_weights * 32)(*[vs.vs_layer_weights(*([fake] * 9)) for _ in range(32)])
+        w = vs.vs_weights(big, fake, fake, fake, ctypes.cast(layers, ctypes.POINTER(vs.vs_layer_weights)))
+        bdesc = vs.vs_batch_desc(64, 64, 64, 1, 4100, 257, pool, fake, fake, fake, fake, None)
+        need = vs.decode_step_workspace_bytes(bdesc, big)
+        assert need > vs.VS_NOALLOC_SCRATCH_BYTES
+        out = vs.vs_step_out(fake, fake, None, None, None, None)
+        with pytest.raises(vs.VSError) as e:
+            vs.decode_step_noalloc(bdesc, fake, w, out, 0)
+        assert e.value.status == vs.VS_ERR_SHAPE and "scratch" in str(e.value)
+    finally:
+        vs.kv_pool_destroy(pool)

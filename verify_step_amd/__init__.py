@@ -24,7 +24,7 @@ EXPORTS = [
     "vs_last_error", "kv_page_bytes", "kv_pool_create", "kv_pool_destroy", "kv_alloc", "kv_share", "kv_free",
     "kv_append", "kv_num_free", "kv_refcount", "kv_pool_base", "kv_prefix_root", "kv_prefix_chain",
     "kv_prefix_insert", "kv_prefix_lookup", "kv_prefix_evict", "kv_prefix_entries", "decode_step_workspace_bytes",
-    "decode_step",
+    "decode_step", "decode_step_noalloc",
     "verify_accept", "verify_sample_workspace_bytes", "verify_sample", "vs_time_kernel", "vs_timed_launches",
 ]
 
@@ -120,6 +120,9 @@ def lib() -> ctypes.CDLL:
         L.decode_step.restype = c_int32
         L.decode_step.argtypes = [POINTER(vs_batch_desc), c_void_p, POINTER(vs_weights), POINTER(vs_step_out),
                                   c_void_p, c_size_t, c_void_p]
+        L.decode_step_noalloc.restype = c_int32
+        L.decode_step_noalloc.argtypes = [POINTER(vs_batch_desc), c_void_p, POINTER(vs_weights),
+                                          POINTER(vs_step_out), c_void_p]
         L.verify_accept.restype = c_int32
         L.verify_accept.argtypes = [c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
         L.verify_sample_workspace_bytes.restype = c_int32
@@ -263,6 +266,15 @@ def decode_step(desc: vs_batch_desc, block_tables, weights: vs_weights, out: vs_
                 stream: int) -> None:
     _check(lib().decode_step(ctypes.byref(desc), c_void_p(_ptr(block_tables)), ctypes.byref(weights),
                              ctypes.byref(out), c_void_p(_ptr(ws)), ws_bytes, c_void_p(stream)))
+
+
+VS_NOALLOC_SCRATCH_BYTES = 96 << 20  # the library's per-GPU scratch array (include/verify_step.h)
+
+
+def decode_step_noalloc(desc: vs_batch_desc, block_tables, weights: vs_weights, out: vs_step_out,
+                        stream: int) -> None:
+    _check(lib().decode_step_noalloc(ctypes.byref(desc), c_void_p(_ptr(block_tables)), ctypes.byref(weights),
+                                     ctypes.byref(out), c_void_p(stream)))
 
 
 def verify_accept(B: int, q_start, drafts, g0, argmax, accept_len, bonus, stream: int) -> None:

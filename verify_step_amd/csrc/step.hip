@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <tuple>
 
@@ -860,6 +861,52 @@ extern "C" vs_status decode_step(const vs_batch_desc* desc, const int32_t* block
     if (st != VS_OK || p.M == 0) return st;
     if (!ws || ws_bytes < p.total)
         return vs_fail(VS_ERR_SHAPE, "decode_step: workspace needs " + std::to_string(p.total) + " bytes");
+    return run_checked(p, desc, block_tables, weights, out, static_cast<char*>(ws), stream);
+}
+
+// ---- the allocation-free variant: the workspace is a device array of the library itself -------
+//
+// One copy per GPU, alive until the process ends. In host code the array's name is only a host-side
+// stand-in; its device address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and that address is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[VS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+vs_status scratch_for_current_device(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return vs_fail(VS_ERR_HIP, std::string("decode_step_noalloc: hipGetDevice: ") + hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return vs_fail(VS_ERR_INVALID, "decode_step_noalloc: device index out of range");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return vs_fail(VS_ERR_HIP, std::string("decode_step_noalloc: hipGetSymbolAddress: ") + hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return vs_ok();
+}
+}  // namespace
+
+extern "C" vs_status decode_step_noalloc(const vs_batch_desc* desc, const int32_t* block_tables,
+                                         const vs_weights* weights, const vs_step_out* out, hipStream_t stream) {
+    Plan p;
+    vs_status st = check_step(desc, block_tables, weights, out, &p);
+    if (st != VS_OK || p.M == 0) return st;
+    if (p.total > (size_t)VS_NOALLOC_SCRATCH_BYTES)
+        return vs_fail(VS_ERR_SHAPE, "decode_step_noalloc: this batch needs " + std::to_string(p.total) +
+                                         " bytes of workspace, more than the library's " +
+                                         std::to_string((size_t)VS_NOALLOC_SCRATCH_BYTES) +
+                                         "-byte scratch array; use decode_step with a caller workspace");
+    void* ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st != VS_OK) return st;
     return run_checked(p, desc, block_tables, weights, out, static_cast<char*>(ws), stream);
 }
 
