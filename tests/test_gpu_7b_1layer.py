@@ -41,10 +41,11 @@ MODELS = {"7B": W.LLAMA7B, "8B-GQA": W.GQA8B}
 
 @pytest.mark.parametrize("shape", ["7B", "8B-GQA"])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("B,K", [(4, 1), (8, 5), (32, 1), (16, 4)])
+@pytest.mark.parametrize("B,K", [(4, 1), (12, 1), (8, 5), (32, 1), (16, 4)])
 def test_7b_width_one_layer_strict(shape, dtype, B, K):
-    """Full-width single layer against the oracle under the fixed bounds: 4 rows (GEMV path), 40
-    (split-K, 1024-element slices), 32 (split-K, two workgroups per CU) and 64 (768-element slices)."""
+    """Full-width single layer against the oracle under the fixed bounds: 4 rows (GEMV path); 12 rows
+    (strip GEMM for q/k/v and gate/up, 16-feature tiles for the rest); 40, 32 and 64 rows (strip GEMM
+    for q/k/v and gate/up at the 7B widths, split-K for the residual products and the LM head)."""
     _run(shape, dtype, None, B, K)
 
 

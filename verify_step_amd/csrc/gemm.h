@@ -62,6 +62,9 @@ struct GemmArgs {
     const int* row_seq;
     const int* row_pos;
     const float* rope_cs;  // [M][head_dim/2][2] (cos, sin)
+    // per row: element offset of its K/V slot inside its page, page * page_elems + slot * head_dim, or -1
+    // when the row has no valid page (computed once per step)
+    const long* row_kvoff;
     // residual add (EPI_RESID): x += C
     float* x;
     int x_ld;

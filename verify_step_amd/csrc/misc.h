@@ -19,6 +19,11 @@ struct PrepArgs {
     int* row_pos;
     float* rope_cs;  // [M][head_dim/2][2]
     float* x;        // [M][D] fp32 residual stream
+    // the row's K/V slot: page * page_elems + slot * head_dim (or -1 without a valid page)
+    long* row_kvoff;
+    const int* block_tables;
+    int max_blocks, num_pages, page_tokens;
+    long page_elems;
 };
 
 // One workgroup (256 threads) per row r: its sequence and position, the rotary
@@ -40,6 +45,13 @@ __global__ void __launch_bounds__(256) prep_embed_kernel(PrepArgs p) {
         p.row_seq[r] = lo;
         p.row_pos[r] = pos;
         s_pos = pos;
+        long off = -1;
+        if (pos >= 0 && pos / p.page_tokens < p.max_blocks) {
+            const int page = p.block_tables[(long)lo * p.max_blocks + pos / p.page_tokens];
+            if (page >= 0 && page < p.num_pages)
+                off = (long)page * p.page_elems + (long)(pos % p.page_tokens) * p.head_dim;
+        }
+        p.row_kvoff[r] = off;
     }
     __syncthreads();
     const int pos = s_pos;

@@ -7,6 +7,7 @@
 #include <mutex>
 #include <string>
 #include <tuple>
+#include <type_traits>
 
 #include "../../include/verify_step.h"
 #include "attention.h"
@@ -16,6 +17,7 @@
 #include "gemm.h"
 #include "gemm_big.h"
 #include "gemm_ksplit.h"
+#include "gemm_strip.h"
 #include "gemv.h"
 #include "misc.h"
 #include "sample.h"
@@ -159,11 +161,12 @@ struct Plan {
     bool ksplit;  // residual products through the split-K tile GEMM
     bool ksplit_qkv, ksplit_gu;  // the q/k/v and gate/up products too (their epilogues after the sums)
     bool ksplit_lm;              // the LM head too (logits and argmax partials after the sums)
+    bool strip_qkv, strip_gu;    // q/k/v, gate/up through the full-reduction strip GEMM (epilogue in-kernel)
     int ks_slices;  // most slices of one of them (sizes the partial sums)
     bool gemv;      // the row-streaming path serves every product of the step
     bool merge_in_o; // the output product's prologue merges the key splits (no merge kernel)
     int n_lm_parts; // argmax partials per logit row
-    size_t off_row_seq, off_row_pos, off_rope, off_x, off_xn, off_q, off_attn, off_h, off_part, off_xf, off_lmpart,
+    size_t off_row_seq, off_row_pos, off_kvoff, off_rope, off_x, off_xn, off_q, off_attn, off_h, off_part, off_xf, off_lmpart,
         off_ksp;
     size_t total;
 };
@@ -278,6 +281,20 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->ksplit_qkv = !p->gemv && p->dt != VS_F32 && d->M <= 64 && (p->H * p->Dh) % kKsRows == 0 &&
                     (p->Hkv * p->Dh) % kKsRows == 0;
     p->ksplit_gu = p->ksplit && p->F % kKsRows == 0;
+    // 8..64 rows: the q/k/v and gate/up products through the strip GEMM when its units (16 weight
+    // rows each) spread over the CUs in whole workgroups of U units with at most 15 % of them idle
+    // (at 7B widths: 3 q/k/v units on every CU, 6 gate/up units on 230 CUs). At least 8 rows: masked
+    // chunks read eight rows' offsets from the activations.
+    {
+        const int MT = (d->M + 15) / 16;
+        auto strip_ok = [&](long units, int U) {
+            const long wgs = (units + U - 1) / U;
+            return U <= strip_max_units(MT) && wgs <= kNumCUs && wgs * 100 >= 85L * kNumCUs;
+        };
+        const bool base = p->dt != VS_F32 && !p->gemv && d->M >= 8 && d->M <= 64 && p->D % 128 == 0;
+        p->strip_qkv = base && p->Dh % 16 == 0 && strip_ok((long)(p->H + 2 * p->Hkv) * p->Dh / 16, kStripUnitsQkv);
+        p->strip_gu = base && p->F % 8 == 0 && strip_ok(p->F / 8, kStripUnitsGu);
+    }
     p->ksplit_lm = p->ksplit && d->M_log > 0;
     const long n_qkv = (long)(p->H + 2 * p->Hkv) * p->Dh, n_gu = 2L * p->F;
     long ks_floats = std::max<long>((long)p->ks_slices * p->D,
@@ -296,6 +313,7 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     };
     p->off_row_seq = take(M * 4);
     p->off_row_pos = take(M * 4);
+    p->off_kvoff = take(M * 8);
     p->off_rope = take(M * (p->Dh / 2) * 2 * 4);
     p->off_x = take(M * p->D * 4);
     p->off_xn = take(M * p->D * p->esz);
@@ -351,6 +369,24 @@ int launch_ksplit(int kind, const void* w0, const void* w1, const void* w2, int 
         default: launch1(kind, gemm_ksplit_kernel<DT, 4, true>, grid, block, 0, s, a); break;
     }
     return slices;
+    }
+}
+
+// The strip GEMM (q/k/v or gate/up with its epilogue): one workgroup of eight waves per U units.
+template <int DT, int EPI, int U>
+void launch_strip(int kind, const GemmArgs& g, hipStream_t s) {
+    if constexpr (DT == F32) {
+        return;  // fp16 / bf16 only (the plan never selects this for fp32 models)
+    } else {
+        const dim3 grid((g.n_tiles + U - 1) / U), block(kStripWaves * 64);
+        switch ((g.M + 15) / 16) {
+            case 1: launch1(kind, gemm_strip_kernel<DT, 1, EPI, U>, grid, block, 0, s, g); break;
+            case 2: launch1(kind, gemm_strip_kernel<DT, 2, EPI, U>, grid, block, 0, s, g); break;
+            case 3: launch1(kind, gemm_strip_kernel<DT, 3, EPI, U>, grid, block, 0, s, g); break;
+            default:
+                if constexpr (U <= strip_max_units(4)) launch1(kind, gemm_strip_kernel<DT, 4, EPI, U>, grid, block, 0, s, g);
+                break;
+        }
     }
 }
 
@@ -504,7 +540,8 @@ void launch_attention(const AttnArgs& a, int B, int M, int rmax, int hg, int kv_
 // Common epilogue fields of both product paths.
 template <typename A>
 void fill_epilogue(A& g, const Plan& p, const vs_batch_desc* d, const int32_t* bt, const vs_pool_desc* pg,
-                   const int* row_seq, const int* row_pos, const float* rope_cs) {
+                   const int* row_seq, const int* row_pos, const float* rope_cs, const long* row_kvoff = nullptr) {
+    if constexpr (std::is_same<A, GemmArgs>::value) g.row_kvoff = row_kvoff;
     g.block_tables = bt;
     g.max_blocks = d->max_blocks;
     g.num_pages = pg->num_pages;
@@ -527,6 +564,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     const vs_pool_desc* pg = vs_pool_geometry(d->pool);
     int* row_seq = reinterpret_cast<int*>(ws + p.off_row_seq);
     int* row_pos = reinterpret_cast<int*>(ws + p.off_row_pos);
+    long* row_kvoff = reinterpret_cast<long*>(ws + p.off_kvoff);
     float* rope_cs = reinterpret_cast<float*>(ws + p.off_rope);
     float* x = reinterpret_cast<float*>(ws + p.off_x);
     void* xn = ws + p.off_xn;
@@ -554,6 +592,12 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     pa.row_pos = row_pos;
     pa.rope_cs = rope_cs;
     pa.x = x;
+    pa.row_kvoff = row_kvoff;
+    pa.block_tables = bt;
+    pa.max_blocks = d->max_blocks;
+    pa.num_pages = pg->num_pages;
+    pa.page_tokens = kPageTokens;
+    pa.page_elems = (long)(kv_page_bytes(pg) / kv_elem_bytes(pg->dtype));
     hipLaunchKernelGGL((prep_embed_kernel<DT>), dim3(p.M), dim3(256), 0, s, pa);
 
     GemvArgs gv = {};
@@ -563,7 +607,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     gv.xin_ld = p.D;
     gv.eps = eps;
     GemmArgs gm = {};
-    fill_epilogue(gm, p, d, bt, pg, row_seq, row_pos, rope_cs);
+    fill_epilogue(gm, p, d, bt, pg, row_seq, row_pos, rope_cs, row_kvoff);
     gm.M = p.M;
 
     AttnArgs a = {};
@@ -625,7 +669,10 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             q.n_tiles = (p.H + 2 * p.Hkv) * p.Dh / 32;
             q.q_out = qb;
             q.layer = l;
-            if (p.ksplit_qkv) {
+            if (p.strip_qkv) {
+                q.n_tiles = (p.H + 2 * p.Hkv) * p.Dh / 16;
+                launch_strip<DT, EPI_QKV, kStripUnitsQkv>(VS_KERNEL_QKV, q, s);
+            } else if (p.ksplit_qkv) {
                 const int N = q.n0 + q.n1 + q.n2;
                 const int slices = launch_ksplit<DT>(VS_KERNEL_QKV, lw.wq, lw.wk, lw.wv, q.n0, q.n1, N, p.D, xn, p.D,
                                                      p.M, ksp, s);
@@ -707,7 +754,10 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             gu.n_tiles = (p.F + 15) / 16;
             gu.h_out = hmid;
             gu.h_ld = p.F;
-            if (p.ksplit_gu) {
+            if (p.strip_gu) {
+                gu.n_tiles = p.F / 8;
+                launch_strip<DT, EPI_SWIGLU, kStripUnitsGu>(VS_KERNEL_GATEUP, gu, s);
+            } else if (p.ksplit_gu) {
                 const int slices = launch_ksplit<DT>(VS_KERNEL_GATEUP, lw.wg, lw.wu, lw.wu, p.F, p.F, 2 * p.F, p.D, xn,
                                                      p.D, p.M, ksp, s);
                 const long threads = (long)p.M * p.F;
