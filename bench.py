@@ -356,13 +356,19 @@ def other_workload(args):
     vs.kv_free(pool.handle, [ids[int(i)] for i in perm])
     rows, specs = [], []
     prefix_rows = {}
+    root = vs.kv_prefix_root(f"{dims.name};{dt};weights={1000 * wl + 1};theta=10000".encode())
     for b in range(B):
-        if ctx_rule == "prefix":  # 4 prefixes of 1024 tokens, each shared by 16 sequences
+        if ctx_rule == "prefix":  # 4 prefixes of 1024 tokens, each shared by 16 sequences through the index
             p = b // 16
-            if p not in prefix_rows:
+            ptok = W.token_ids(1000 * wl + 3, 500 + p, 1024, dims.vocab)
+            hashes = vs.kv_prefix_chain(root, ptok, 16)
+            if p not in prefix_rows:  # the prompt's prefill leaves its full blocks in the index
                 prefix_rows[p] = vs.kv_alloc(pool.handle, 64)
-            vs.kv_share(pool.handle, prefix_rows[p])
-            r = vs.kv_append(pool.handle, list(prefix_rows[p]), max_blocks, 1024, ctxs[b] - 1024 + K)
+                vs.kv_prefix_insert(pool.handle, root, hashes, ptok, prefix_rows[p])
+                vs.kv_free(pool.handle, prefix_rows[p])
+            hit = vs.kv_prefix_lookup(pool.handle, root, hashes, ptok)
+            assert hit == prefix_rows[p]
+            r = vs.kv_append(pool.handle, hit, max_blocks, 1024, ctxs[b] - 1024 + K)
         else:
             r = vs.kv_alloc(pool.handle, -(-ctxs[b] // 16))
             r = vs.kv_append(pool.handle, r, max_blocks, ctxs[b], K)

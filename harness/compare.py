@@ -6,7 +6,10 @@ Given the oracle's fp32 realisation of the same rows (``alt``), a row's bound
 is max(tol, 2 x the relative distance between the two oracle realisations):
 through a deep stack the rounding differences at the storage points compound,
 and no correct implementation can be held closer to the float64 oracle than a
-second correct one is. Both bounds depend on the oracle alone.
+second correct one is. For the rows one sequence wrote in one layer, the
+distance is taken as the largest over those rows (one depth of compounding, so
+one scale; a single row's distance is a noisy sample of it). Both bounds
+depend on the oracle alone.
 
 Integer decisions: the greedy token must match exactly, except on a row the
 oracle records as a near-tie; there the GPU may return any token whose oracle
@@ -38,13 +41,20 @@ def row_rel_err(gpu: torch.Tensor, ref: torch.Tensor) -> float:
     return float((gpu - ref).abs().max()) / (den if den > 0 else 1.0)
 
 
-def check_rows(gpu_rows, ref_rows, tol: float, what: str, alt_rows=None) -> float:
+def check_rows(gpu_rows, ref_rows, tol: float, what: str, alt_rows=None, alt_group: bool = False) -> float:
     """Every row within tol of the oracle's. With alt_rows (the oracle's fp32 realisation of the same
-    rows), a row's bound is max(tol, 2 x the distance between the two oracle realisations)."""
+    rows), a row's bound is max(tol, 2 x the distance between the two oracle realisations). With
+    alt_group, the rows are one sequence's rows of one layer (or its logit rows), which carry the same
+    depth of compounded rounding; the drift scale is then the largest of their fp32-oracle distances
+    rather than each row's own single sample of it."""
     worst = 0.0
+    alt_err = [row_rel_err(a, r) for a, r in zip(alt_rows, ref_rows)] if alt_rows is not None else None
     for i, (g, r) in enumerate(zip(gpu_rows, ref_rows)):
         e = row_rel_err(g, r)
-        bound = tol if alt_rows is None else max(tol, 2.0 * row_rel_err(alt_rows[i], r))
+        if alt_err is None:
+            bound = tol
+        else:
+            bound = max(tol, 2.0 * (max(alt_err) if alt_group else alt_err[i]))
         assert e <= bound, f"{what} row {i}: relative error {e:.3e} > {bound:.2e}"
         worst = max(worst, e)
     return worst

@@ -101,7 +101,7 @@ def _run_and_check(dims, w_cpu, model, pool, seqs, what):
         want32 = s.state32.kv[:, :, s.ctx:s.ctx + 1].double()
         for l in range(dims.n_layers):
             check_rows([got[l, t, 0] for t in range(2)], [want[l, t, 0] for t in range(2)], tol,
-                       f"{what} seq {i} layer {l} K/V", [want32[l, t, 0] for t in range(2)])
+                       f"{what} seq {i} layer {l} K/V", [want32[l, t, 0] for t in range(2)], alt_group=True)
     _say(f"{what}: {ties.report()}")
     return am
 

@@ -1,12 +1,14 @@
 """7B fp16 mixed step: 64 decode rows on shared prefixes plus a 512-row prompt chunk.
 
-The workload ([KV Cache] section 05 block sharing, section 06 chunked prefill;
-[Serving] "Chunked prefill"; [Serving Efficiency] section 31.3): 4 prompts of
-1024 tokens each sit in 64 pages shared by 16 sequences apiece (reference
-count 17: the 16 sequences plus the prefix's own holder); each sequence has a
-private suffix of 16..512 tokens and decodes one token; in the same step a new
-3000-token prompt runs its first 512-position chunk (positions 0..511, causal
-within the chunk, no logits). M = 576 rows go through the tile (MFMA) path.
+The workload ([KV Cache] section 05 block sharing and prefix caching, section 06
+chunked prefill; [Serving] "Chunked prefill"; [Serving Efficiency] section 31.3):
+4 prompts of 1024 tokens each sit in 64 pages that the prefix-cache index names
+by their chained block hashes; each of 16 sequences per prompt finds its prefix
+by a lookup in the index (reference count 17: the 16 sequences plus the index);
+each sequence has a private suffix of 16..512 tokens and decodes one token; in
+the same step a new 3000-token prompt runs its first 512-position chunk
+(positions 0..511, causal within the chunk, no logits). M = 576 rows go through
+the tile (MFMA) path.
 
 Checked against the oracle on one sampled decode sequence per prefix and on
 the whole chunk: logits, greedy tokens, and every K/V row written (the
@@ -50,13 +52,21 @@ def test_7b_shared_prefixes_and_prompt_chunk():
     perm = synth.permutation(synth.key(SEED_PAGES), n_pages)
     vs.kv_free(pool.handle, [ids[int(i)] for i in perm])
 
-    prefix_rows, prefix_kv = [], []
+    # each prompt's prefill leaves its 64 full blocks in the index, which then holds their only reference
+    root = vs.kv_prefix_root(f"7B;f16;weights={SEED_W};theta=10000;scope=test".encode())
+    prefix_rows, prefix_kv, prefix_tok, prefix_hash = [], [], [], []
     for p in range(N_PREFIX):
+        toks = W.token_ids(SEED_TOK, 500 + p, PREFIX, dims.vocab)
         r = vs.kv_alloc(pool.handle, PREFIX // 16)
         kv = W.kv_block(dims, SEED_KV, p, 0, PREFIX)
         pool.write(r, 0, kv)
+        h = vs.kv_prefix_chain(root, toks, 16)
+        assert vs.kv_prefix_insert(pool.handle, root, h, toks, r) == PREFIX // 16
+        vs.kv_free(pool.handle, r)
         prefix_rows.append(r)
         prefix_kv.append(kv)
+        prefix_tok.append(toks)
+        prefix_hash.append(h)
     sampled = {p * PER_PREFIX + int(synth.uniform_int(synth.key(SEED_CHURN, 2), p, 1, 0, PER_PREFIX)[0])
                for p in range(N_PREFIX)}
     _say(f"7B fp16 mixed: suffixes {min(suffix)}..{max(suffix)}, sampled decode sequences {sorted(sampled)}")
@@ -64,9 +74,11 @@ def test_7b_shared_prefixes_and_prompt_chunk():
     specs, rows, states, order = [], [], [], []
     for b in range(B_dec):
         p = b // PER_PREFIX
-        vs.kv_share(pool.handle, prefix_rows[p])
+        # the sequence's prompt starts with the shared 1024 tokens: the index hands over their pages
+        hit = vs.kv_prefix_lookup(pool.handle, root, vs.kv_prefix_chain(root, prefix_tok[p], 16), prefix_tok[p])
+        assert hit == prefix_rows[p], "every full block of the prefix is found"
         ctx = PREFIX + suffix[b]
-        r = vs.kv_append(pool.handle, list(prefix_rows[p]), max_blocks, PREFIX, suffix[b] + 1)
+        r = vs.kv_append(pool.handle, hit, max_blocks, PREFIX, suffix[b] + 1)
         assert r[:PREFIX // 16] == prefix_rows[p], "a page-aligned prefix stays shared"
         tok = W.token_ids(SEED_TOK, b, 1, dims.vocab)
         specs.append(SeqSpec(ctx, tok))
