@@ -73,6 +73,7 @@ struct GemvArgs {
     const int* row_seq;
     const int* row_pos;
     const float* rope_cs;
+    const long* row_kvoff;  // per row: page * page_elems + slot * head_dim of its K/V slot, or -1
     // residual (EPI_RESID)
     float* x;
     int x_ld;
@@ -234,12 +235,103 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs g) {
         }
     };
 
+    // ---- prologue inputs, requested before the first weight burst: loads retire in order, so anything
+    // requested after the burst would wait for it. X_NORM keeps each thread's share of the fp32 rows and
+    // of the gain in registers for both passes of the norm (rows up to PN * NW * 256 wide). (Fetching
+    // X_MERGE's split statistics or X_PLAIN's chunks early measured no faster.)
+    constexpr int PN = 2;  // float4 groups per row and thread
+    float4_t pre_x[XM == X_NORM ? MR : 1][PN];
+    uint32_t pre_g[XM == X_NORM ? PN : 1][St<DT>::bytes == 2 ? 2 : 4];
+    const bool pre_fast = XM == X_NORM && K <= PN * NW * 256;
+    if constexpr (XM == X_NORM) {
+        if (pre_fast) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                if (m >= g.M) break;
+                const int src = g.act_rows ? g.act_rows[m] : m;
+                const float* xr = g.xin + (long)src * g.xin_ld;
+#pragma unroll
+                for (int j = 0; j < PN; ++j) {
+                    const int k = tid * 4 + j * NW * 256;
+                    pre_x[m][j] = k < K ? *reinterpret_cast<const float4_t*>(xr + k) : (float4_t){0.f, 0.f, 0.f, 0.f};
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < PN; ++j) {
+                const int k = tid * 4 + j * NW * 256;
+                const uint32_t* gp = reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(g.gain) +
+                                                                       (long)(k < K ? k : 0) * St<DT>::bytes);
+#pragma unroll
+                for (int w = 0; w < (St<DT>::bytes == 2 ? 2 : 4); ++w) pre_g[j][w] = gp[w];
+            }
+        }
+    }
+    // the epilogue's own inputs (the residual, the rotary pair's cos / sin, the row's K/V slot), also
+    // requested now: thread t serves (unit t / M, row t % M) when there are few enough items
+    float ep_x = 0.f;
+    float2 ep_cs = make_float2(1.f, 0.f);
+    long ep_off = -1;
+    const bool ep_fast = n_local * g.M <= NW * 64;
+    if (ep_fast && tid < n_local * g.M) {
+        const int ul = tid / g.M, m = tid % g.M, u = u_begin + ul;
+        if constexpr (EPI == EPI_RESID) ep_x = g.x[(long)m * g.x_ld + u];
+        if constexpr (EPI == EPI_QKV) {
+            const UnitMap um = unit_map<EPI>(g, u);
+            ep_cs = *reinterpret_cast<const float2*>(g.rope_cs + ((long)m * (g.head_dim / 2) + um.i) * 2);
+            ep_off = g.row_kvoff[m];
+        }
+    }
+
     // the wave's first burst is in flight while X is staged
     uint4 buf[RU][CG];
     if (my_units > 0) issue(buf, unit_map<EPI>(g, u_begin + wave), 0);
 
     // ---- prologue: the batch rows into LDS ----
-    if constexpr (XM == X_NORM) {
+    if (XM == X_NORM && pre_fast) {
+        __shared__ float red_f[NW][MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            if (m >= g.M) break;
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < PN; ++j)
+                ss += pre_x[m][j][0] * pre_x[m][j][0] + pre_x[m][j][1] * pre_x[m][j][1] +
+                      pre_x[m][j][2] * pre_x[m][j][2] + pre_x[m][j][3] * pre_x[m][j][3];
+#pragma unroll
+            for (int mask = 32; mask >= 1; mask >>= 1) ss += shfl_xor(ss, mask);
+            if (lane == 0) red_f[wave][m] = ss;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            if (m >= g.M) break;
+            float part[NW];
+#pragma unroll
+            for (int w = 0; w < NW; ++w) part[w] = red_f[w][m];
+#pragma unroll
+            for (int span = 1; span < NW; span <<= 1)  // fixed pairwise tree
+#pragma unroll
+                for (int w = 0; w + span < NW; w += 2 * span) part[w] += part[w + span];
+            const float rinv = 1.0f / sqrtf(part[0] / (float)K + g.eps);
+            typename St<DT>::raw* xs = reinterpret_cast<typename St<DT>::raw*>(smem) + (long)m * K;
+#pragma unroll
+            for (int j = 0; j < PN; ++j) {
+                const int k = tid * 4 + j * NW * 256;
+                if (k >= K) continue;
+                float gv[4];
+                if constexpr (St<DT>::bytes == 2) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        gv[e] = St<DT>::to_f((typename St<DT>::raw)((pre_g[j][e / 2] >> (16 * (e % 2))) & 0xFFFFu));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) gv[e] = __uint_as_float(pre_g[j][e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xs[k + e] = St<DT>::from_f(pre_x[m][j][e] * rinv * gv[e]);
+            }
+        }
+    } else if constexpr (XM == X_NORM) {
         __shared__ float red[NW][MR];
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
@@ -448,9 +540,39 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs g) {
     __syncthreads();
 
     // ---- epilogues of the workgroup's units, all threads ----
-    for (int idx = tid; idx < n_local * g.M; idx += NW * 64) {
-        const int ul = idx / g.M, m = idx % g.M;
-        gemv_epilogue<DT, EPI>(g, u_begin + ul, m, res[ul][0][m], res[ul][RU - 1][m]);
+    if (ep_fast) {
+        if (tid < n_local * g.M) {
+            const int ul = tid / g.M, m = tid % g.M, u = u_begin + ul;
+            const float v0 = res[ul][0][m], v1 = res[ul][RU - 1][m];
+            if constexpr (EPI == EPI_RESID) {
+                g.x[(long)m * g.x_ld + u] = ep_x + v0;
+            } else if constexpr (EPI == EPI_QKV) {
+                const UnitMap um = unit_map<EPI>(g, u);
+                const int half = g.head_dim / 2;
+                float ra = v0, rb = v1;
+                if (um.seg < 2) {
+                    ra = v0 * ep_cs.x - v1 * ep_cs.y;
+                    rb = v1 * ep_cs.x + v0 * ep_cs.y;
+                }
+                if (um.seg == 0) {
+                    const long o = (long)m * (g.n_heads * g.head_dim) + um.head * g.head_dim + um.i;
+                    store_round<DT>(g.q_out, o, ra);
+                    store_round<DT>(g.q_out, o + half, rb);
+                } else if (ep_off >= 0) {
+                    const long o = ep_off + (long)g.layer * g.layer_elems +
+                                   ((long)(um.seg - 1) * g.n_kv_heads + um.head) * g.page_tokens * g.head_dim + um.i;
+                    store_kv<DT>(g.kv_base, o, ra, g.kv_dt);
+                    store_kv<DT>(g.kv_base, o + half, rb, g.kv_dt);
+                }
+            } else {
+                gemv_epilogue<DT, EPI>(g, u, m, v0, v1);
+            }
+        }
+    } else {
+        for (int idx = tid; idx < n_local * g.M; idx += NW * 64) {
+            const int ul = idx / g.M, m = idx % g.M;
+            gemv_epilogue<DT, EPI>(g, u_begin + ul, m, res[ul][0][m], res[ul][RU - 1][m]);
+        }
     }
     if constexpr (EPI == EPI_LOGITS) {
         // argmax partial of this workgroup's vocabulary range, per batch row (wave w takes rows w, w+4)

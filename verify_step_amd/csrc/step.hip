@@ -541,7 +541,7 @@ void launch_attention(const AttnArgs& a, int B, int M, int rmax, int hg, int kv_
 template <typename A>
 void fill_epilogue(A& g, const Plan& p, const vs_batch_desc* d, const int32_t* bt, const vs_pool_desc* pg,
                    const int* row_seq, const int* row_pos, const float* rope_cs, const long* row_kvoff = nullptr) {
-    if constexpr (std::is_same<A, GemmArgs>::value) g.row_kvoff = row_kvoff;
+    g.row_kvoff = row_kvoff;
     g.block_tables = bt;
     g.max_blocks = d->max_blocks;
     g.num_pages = pg->num_pages;
@@ -601,7 +601,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     hipLaunchKernelGGL((prep_embed_kernel<DT>), dim3(p.M), dim3(256), 0, s, pa);
 
     GemvArgs gv = {};
-    fill_epilogue(gv, p, d, bt, pg, row_seq, row_pos, rope_cs);
+    fill_epilogue(gv, p, d, bt, pg, row_seq, row_pos, rope_cs, row_kvoff);
     gv.M = p.M;
     gv.xin = x;
     gv.xin_ld = p.D;
