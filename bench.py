@@ -272,6 +272,7 @@ def main():
         "attention": attention_stream(kt, n_rf, avg_keys * kvpt + kvpt),
     }
 
+    result["stream_ceiling"] = stream_ceiling(vs)
     if args.copy_calibration:
         copy_calibration()
     if not args.no_cpu_baseline:
@@ -280,6 +281,31 @@ def main():
 
 
 COPY_BYTES = 256 << 20
+CEILING_BYTES = 4 << 30
+
+
+def stream_ceiling(vs):
+    """The device's streaming-read rate in the GEMV's load shape (vs_stream_read over 4 GiB, the best of
+    20 timed reads after 3 warm-up reads), the practical reference for the weight stream."""
+    import torch
+
+    buf = torch.ones(CEILING_BYTES // 2, dtype=torch.float16, device="cuda")
+    sink = torch.zeros(512, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        vs.vs_stream_read(buf, CEILING_BYTES, sink, stream)
+    best = float("inf")
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        vs.vs_stream_read(buf, CEILING_BYTES, sink, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del buf
+    gbps = CEILING_BYTES / (best * 1e-3) / 1e9
+    return {"achieved": round(gbps, 1), "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "bytes": CEILING_BYTES, "kernel": "vs_stream_read (1 KB wave loads, nontemporal)"}
 
 
 def copy_calibration():

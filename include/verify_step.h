@@ -235,7 +235,24 @@ typedef struct vs_batch_desc {
                                   sequence's row count to ctx_advance[b] after every other use of
                                   ctx_len; it may be ctx_len itself (a replayed decode loop then
                                   needs no host update of the context lengths). */
+    int32_t* error_flags;      /* device int32 or NULL: input validation. The device arrays are not
+                                  read on the host, so their contents cannot be checked before the
+                                  launch. Without this word, out-of-range values are clamped
+                                  silently (a token id into [0, vocab), a page id into
+                                  [0, num_pages)), so no access leaves its buffer but the result is
+                                  that of other inputs. With it, the step's first kernel also ORs in
+                                  VS_STEP_BAD_TOKEN for a token id outside [0, vocab),
+                                  VS_STEP_BAD_PAGE for a block-table entry outside [0, num_pages)
+                                  among the pages a row reads or writes, and VS_STEP_BAD_BATCH for a
+                                  decreasing q_start or a negative ctx_len; the step still completes
+                                  with the clamped values. The caller zeroes the word beforehand and
+                                  reads it after the stream reaches the step; any bit set means
+                                  the step's outputs are not valid (treat as VS_ERR_INVALID). */
 } vs_batch_desc;
+
+#define VS_STEP_BAD_TOKEN 1
+#define VS_STEP_BAD_PAGE 2
+#define VS_STEP_BAD_BATCH 4
 
 typedef struct vs_step_out {
     float* logits;     /* device [M_log][vocab] fp32, or NULL */
@@ -353,6 +370,14 @@ vs_status verify_sample(int32_t B, int32_t M, int32_t V, const int32_t* q_start,
  * Process-wide state; not for use while another thread runs decode_step. */
 vs_status vs_time_kernel(int32_t kind, void* const* start_events, void* const* stop_events, int32_t capacity);
 int32_t vs_timed_launches(void);
+
+/* Measurement aid: the streaming-read ceiling of the device. Reads `bytes` (a
+ * multiple of 8192) of device memory at `buf` once, in the GEMV's load shape
+ * (1 KB wave-wide nontemporal loads, rows of 8 KB spread over 512 workgroups
+ * of 8 waves), and computes nothing else; sink: device array of 512 uint32
+ * that is written only in a practically impossible case (it keeps the loads).
+ * Asynchronous on the stream. */
+vs_status vs_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -404,3 +404,35 @@ def test_tiny_many_key_splits_use_the_merge_kernel():
     ctxs, k = [3000], [1]
     sb, ref, so, pool, rows = run_case(dims, ctxs, k, pool_pages=200)
     check_case(dims, sb, ref, so, pool, rows, ctxs, k)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_tiny_validation_word_flags_bad_inputs(dtype):
+    """With desc->error_flags set, the step reports out-of-range inputs instead of only clamping them:
+    a token id outside [0, vocab), a block-table entry outside [0, num_pages) among the pages a row
+    reads, a negative context length. Valid inputs leave the word at zero; every step completes."""
+    _say(f"tiny validation word dtype={dtype}")
+    dims = W.TINY.with_dtype(dtype)
+    model = GpuModel(dims, weights_cpu=W.make_weights(dims, SEED_W))
+    pool = GpuPool(dims, 16)
+    rows = alloc_rows(pool, [20, 9])
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step(tokens, bt_patch=None, ctx=(19, 8)):
+        sb = make_step(model, pool, [SeqSpec(ctx[0], [tokens[0]]), SeqSpec(ctx[1], [tokens[1]])], rows, max_blocks=4)
+        if bt_patch is not None:
+            sb.block_tables[bt_patch[0], bt_patch[1]] = bt_patch[2]
+        flags.zero_()
+        sb.desc.error_flags = flags.data_ptr()
+        run_step(model, sb)
+        torch.cuda.synchronize()
+        assert all(0 <= a < dims.vocab for a in sb.argmax[:2].cpu().tolist())
+        return int(flags.item())
+
+    assert step([3, 4]) == 0
+    assert step([dims.vocab + 5, 4]) == vs.VS_STEP_BAD_TOKEN
+    assert step([3, -1]) == vs.VS_STEP_BAD_TOKEN
+    assert step([3, 4], bt_patch=(0, 1, pool.num_pages + 3)) == vs.VS_STEP_BAD_PAGE  # row 0 reads page 1
+    assert step([3, 4], bt_patch=(1, 2, pool.num_pages + 3)) == 0  # past row 1's pages: never read
+    assert step([dims.vocab, 4], bt_patch=(1, 0, -2)) == vs.VS_STEP_BAD_TOKEN | vs.VS_STEP_BAD_PAGE
+    pool.close()

@@ -25,8 +25,10 @@ EXPORTS = [
     "kv_append", "kv_num_free", "kv_refcount", "kv_pool_base", "kv_prefix_root", "kv_prefix_chain",
     "kv_prefix_insert", "kv_prefix_lookup", "kv_prefix_evict", "kv_prefix_entries", "decode_step_workspace_bytes",
     "decode_step", "decode_step_noalloc",
-    "verify_accept", "verify_sample_workspace_bytes", "verify_sample", "vs_time_kernel", "vs_timed_launches",
+    "verify_accept", "verify_sample_workspace_bytes", "verify_sample", "vs_time_kernel", "vs_timed_launches", "vs_stream_read",
 ]
+
+VS_STEP_BAD_TOKEN, VS_STEP_BAD_PAGE, VS_STEP_BAD_BATCH = 1, 2, 4
 
 VS_KERNEL = {"none": 0, "qkv": 1, "attn": 2, "merge": 3, "oproj": 4, "gateup": 5, "down": 6, "lmhead": 7,
              "smstats": 8, "sample": 9}
@@ -61,7 +63,8 @@ class vs_pool_desc(Structure):
 class vs_batch_desc(Structure):
     _fields_ = [("B", c_int32), ("M", c_int32), ("M_log", c_int32), ("max_rows", c_int32), ("max_ctx", c_int32),
                 ("max_blocks", c_int32), ("pool", c_void_p), ("q_start", c_void_p), ("ctx_len", c_void_p),
-                ("tokens", c_void_p), ("logit_rows", c_void_p), ("ctx_advance", c_void_p)]
+                ("tokens", c_void_p), ("logit_rows", c_void_p), ("ctx_advance", c_void_p),
+                ("error_flags", c_void_p)]
 
 
 class vs_step_out(Structure):
@@ -134,6 +137,8 @@ def lib() -> ctypes.CDLL:
         L.vs_time_kernel.argtypes = [c_int32, c_void_p, c_void_p, c_int32]
         L.vs_timed_launches.restype = c_int32
         L.vs_timed_launches.argtypes = []
+        L.vs_stream_read.restype = c_int32
+        L.vs_stream_read.argtypes = [c_void_p, c_size_t, c_void_p, c_void_p]
         _lib = L
     return _lib
 
@@ -306,3 +311,7 @@ def vs_time_kernel(kind: int, start_events, stop_events, capacity: int) -> None:
 
 def vs_timed_launches() -> int:
     return int(lib().vs_timed_launches())
+
+
+def vs_stream_read(buf, nbytes: int, sink, stream: int) -> None:
+    _check(lib().vs_stream_read(c_void_p(_ptr(buf)), nbytes, c_void_p(_ptr(sink)), c_void_p(stream)))

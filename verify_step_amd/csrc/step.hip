@@ -598,6 +598,7 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     pa.num_pages = pg->num_pages;
     pa.page_tokens = kPageTokens;
     pa.page_elems = (long)(kv_page_bytes(pg) / kv_elem_bytes(pg->dtype));
+    pa.error_flags = d->error_flags;
     hipLaunchKernelGGL((prep_embed_kernel<DT>), dim3(p.M), dim3(256), 0, s, pa);
 
     GemvArgs gv = {};
@@ -1033,3 +1034,13 @@ extern "C" vs_status vs_time_kernel(int32_t kind, void* const* start_events, voi
 }
 
 extern "C" int32_t vs_timed_launches(void) { return g_timer.count; }
+
+extern "C" vs_status vs_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+    if (!buf || !sink) return vs_fail(VS_ERR_INVALID, "vs_stream_read: null argument");
+    if (bytes == 0 || bytes % 8192 != 0) return vs_fail(VS_ERR_INVALID, "vs_stream_read: bytes must be a multiple of 8192");
+    hipLaunchKernelGGL(stream_read_kernel, dim3(512), dim3(512), 0, stream, static_cast<const char*>(buf),
+                       (long)(bytes / 8192), reinterpret_cast<unsigned*>(sink));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return vs_fail(VS_ERR_HIP, std::string("vs_stream_read launch: ") + hipGetErrorString(e));
+    return vs_ok();
+}
