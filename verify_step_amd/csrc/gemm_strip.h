@@ -1,5 +1,6 @@
 // Full-reduction strip GEMM for the q/k/v and gate/up products of steps with
-// 17..64 rows (gfx950), with their epilogues in the same kernel.
+// 8..64 rows, and for the residual products of 8..16 rows (gfx950), with their
+// epilogues in the same kernel.
 //
 // C[n][m] = sum_k W[n][k] X[m][k] ([KV Cache] section 02: every row passing
 // through a weight matrix shares one read of it). The output features are cut
@@ -269,6 +270,131 @@ __global__ void __launch_bounds__(kStripWaves * 64, 1) gemm_strip_kernel(GemmArg
                 store_kv<DT>(g.kv_base, o + half, rb, g.kv_dt);
             }
         }
+    }
+}
+
+// The residual products (attention output, MLP down) of 8..16-row steps: one unit of 16 output
+// features per workgroup (at 7B widths 4096 features make one unit per CU), the same wave split of the
+// reduction axis and slab. With a single unit the X block of a chunk serves only that chunk, so each
+// chunk carries its own X fragments and the ring of R chunks (weights and X) runs R - 1 chunks ahead.
+// The epilogue adds the 16 x M sums to the residual: x[m][16 u + r] += C[r][m].
+// Every CU reads all of X here (M K 2 bytes against its 32 K bytes of weights), so past 16 rows X
+// outweighs the weights: measured at 7B widths (fp16, with the RMSNorm launch that follows), 8 rows:
+// 11.6 / 22.0 us (O / down) against 13.4 / 26.8 us for split-K + fused norm; 32 rows: 17.7 / 33.9
+// against 15.4 / 32.6; 40 rows: 21.4 / 40.3 against 16.6 / 29.9.
+template <int DT, int MT>
+__global__ void __launch_bounds__(kStripWaves * 64, 1) gemm_strip_resid_kernel(GemmArgs g) {
+    typedef const __attribute__((address_space(1))) u32x4_t* gptr;
+    constexpr int R = 5;
+    const int K = g.K, M = g.M;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int KB = K / 128;
+    const int kb0 = (wave * KB) / kStripWaves, kb1 = ((wave + 1) * KB) / kStripWaves;
+    const int nb = kb1 - kb0;
+    const int u = blockIdx.x;
+    const uint32_t loff0 = (uint32_t)((lane >> 4) * K * 2 + 16 * (lane & 15));
+    const uint32_t loff1 = loff0 + (uint32_t)(4 * K * 2);
+    const char* h0 = reinterpret_cast<const char*>(g.w0) + (long)16 * u * K * 2;
+    const char* h1 = h0 + (long)8 * K * 2;
+    const char* dummy = reinterpret_cast<const char*>(g.act);
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(g.act);
+    struct Chunk {
+        uint4 v[4];
+        uint4 x[4][MT];
+        uint32_t keep;
+    };
+    // chunk b of the wave's range: 16 rows x 128 elements of weights and the X fragments of the same
+    // 128 elements; past the range the weights come from the activations and are masked
+    auto load = [&](Chunk& ck, int b) {
+        const bool live = b < nb;
+        const char* a0 = live ? h0 + (long)(kb0 + b) * 256 : dummy;
+        const char* a1 = live ? h1 + (long)(kb0 + b) * 256 : dummy;
+        ck.v[0] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((gptr)(a0 + loff0)));
+        ck.v[1] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((gptr)(a0 + loff1)));
+        ck.v[2] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((gptr)(a1 + loff0)));
+        ck.v[3] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((gptr)(a1 + loff1)));
+        ck.keep = live ? 0xFFFFFFFFu : 0u;
+        const int kb = live ? kb0 + b : (nb > 0 ? kb1 - 1 : 0);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = min(16 * mt + (lane & 15), M - 1);
+            const uint16_t* p = A + (long)m * g.act_ld + (long)kb * 128 + 8 * (lane >> 4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ck.x[s][mt] = *reinterpret_cast<const uint4*>(p + 32 * s);
+        }
+    };
+    constexpr int kSlabs = kStripWaves * kStripSlab, kRed = kStripWaves * MT * 1024;
+    __shared__ __align__(16) unsigned char lds[kSlabs > kRed ? kSlabs : kRed];
+    unsigned char* slab = lds + wave * kStripSlab;
+    float4_t acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    auto consume = [&](const Chunk& ck) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 v = ck.v[i];
+            const uint32_t kp = ck.keep;
+            *reinterpret_cast<uint4*>(slab + (4 * i + (lane >> 4)) * kStripRowB + 16 * (lane & 15)) =
+                make_uint4(v.x & kp, v.y & kp, v.z & kp, v.w & kp);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            Frag<DT> fa, fx;
+            fa.a = *reinterpret_cast<const uint4*>(slab + (lane & 15) * kStripRowB + 64 * s + 16 * (lane >> 4));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                fx.a = ck.x[s][mt];
+                acc[mt] = frag_mma<DT>(fa, fx, acc[mt]);
+            }
+        }
+    };
+    // the residual values the epilogue adds to, requested before the stream (thread t: rows pair
+    // p = 4 (l / 16) + e of tile mt, l < 32, as in the epilogue below)
+    constexpr int NT = kStripWaves * 64;
+    constexpr int n_items = MT * 32 * 4;
+    constexpr int NIT = (n_items + NT - 1) / NT;
+    float2 xr[NIT];
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+        const int it = min((int)threadIdx.x + k * NT, n_items - 1);
+        const int e = it & 3, l = (it >> 2) & 31, mt = it >> 7;
+        const int m = min(16 * mt + (l & 15), M - 1), f = 16 * u + 4 * (l >> 4) + e;
+        xr[k] = make_float2(g.x[(long)m * g.x_ld + f], g.x[(long)m * g.x_ld + f + 8]);
+    }
+    // the stream: slot of chunk c is c % R (the loop body is R chunks); the loads run R - 1 ahead
+    Chunk ring[R];
+#pragma unroll
+    for (int c = 0; c < R - 1; ++c) load(ring[c], c);
+    for (int c0 = 0; c0 < nb; c0 += R) {
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            if (c0 + t >= nb) break;
+            load(ring[(t + R - 1) % R], c0 + t + R - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(ring[t]);
+        }
+    }
+    __syncthreads();
+    float4_t* red = reinterpret_cast<float4_t*>(lds);  // [wave][mt][lane]
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * 64 + lane] = acc[mt];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+        const int it = threadIdx.x + k * NT;
+        const int e = it & 3, l = (it >> 2) & 31, mt = it >> 7;
+        const int m = 16 * mt + (l & 15);
+        if (it >= n_items || m >= M) continue;
+        float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < kStripWaves; ++w) {
+            v0 += red[(w * MT + mt) * 64 + l][e];
+            v1 += red[(w * MT + mt) * 64 + l + 32][e];
+        }
+        const int f = 16 * u + 4 * (l >> 4) + e;
+        g.x[(long)m * g.x_ld + f] = xr[k].x + v0;
+        g.x[(long)m * g.x_ld + f + 8] = xr[k].y + v1;
     }
 }
 

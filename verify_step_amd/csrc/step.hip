@@ -162,6 +162,7 @@ struct Plan {
     bool ksplit_qkv, ksplit_gu;  // the q/k/v and gate/up products too (their epilogues after the sums)
     bool ksplit_lm;              // the LM head too (logits and argmax partials after the sums)
     bool strip_qkv, strip_gu;    // q/k/v, gate/up through the full-reduction strip GEMM (epilogue in-kernel)
+    bool strip_o, strip_down;    // the residual products through its one-unit variant (8..16 rows)
     int ks_slices;  // most slices of one of them (sizes the partial sums)
     bool gemv;      // the row-streaming path serves every product of the step
     bool merge_in_o; // the output product's prologue merges the key splits (no merge kernel)
@@ -294,6 +295,11 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
         const bool base = p->dt != VS_F32 && !p->gemv && d->M >= 8 && d->M <= 64 && p->D % 128 == 0;
         p->strip_qkv = base && p->Dh % 16 == 0 && strip_ok((long)(p->H + 2 * p->Hkv) * p->Dh / 16, kStripUnitsQkv);
         p->strip_gu = base && p->F % 8 == 0 && strip_ok(p->F / 8, kStripUnitsGu);
+        // the residual products: one unit per workgroup, up to 16 rows (one row tile; every CU reads
+        // all of X, which past 16 rows outweighs its share of the weights)
+        const bool base_r = base && d->M <= 16 && p->D % 16 == 0 && strip_ok(p->D / 16, 1);
+        p->strip_o = base_r && (p->H * p->Dh) % 128 == 0;
+        p->strip_down = base_r && p->F % 128 == 0;
     }
     p->ksplit_lm = p->ksplit && d->M_log > 0;
     const long n_qkv = (long)(p->H + 2 * p->Hkv) * p->Dh, n_gu = 2L * p->F;
@@ -387,6 +393,16 @@ void launch_strip(int kind, const GemmArgs& g, hipStream_t s) {
                 if constexpr (U <= strip_max_units(4)) launch1(kind, gemm_strip_kernel<DT, 4, EPI, U>, grid, block, 0, s, g);
                 break;
         }
+    }
+}
+
+// x += W a through the one-unit strip GEMM (8..16 rows: one row tile), one workgroup per 16 features.
+template <int DT>
+void launch_strip_resid(int kind, const GemmArgs& g, hipStream_t s) {
+    if constexpr (DT == F32) {
+        return;  // fp16 / bf16 only (the plan never selects this for fp32 models)
+    } else {
+        launch1(kind, gemm_strip_resid_kernel<DT, 1>, dim3(g.n_tiles), dim3(kStripWaves * 64), 0, s, g);
     }
 }
 
@@ -720,7 +736,9 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             o.n_tiles = (p.D + 15) / 16;
             o.x = x;
             o.x_ld = p.D;
-            if (p.ksplit) {
+            if (p.strip_o) {
+                launch_strip_resid<DT>(VS_KERNEL_OPROJ, o, s);
+            } else if (p.ksplit) {
                 launch_resid_ksplit<DT>(VS_KERNEL_OPROJ, lw.wo, p.D, p.H * p.Dh, attn, p.H * p.Dh, p.M, x, p.D, ksp, s,
                                         lw.ffn_norm, eps, xn);
                 xn_ready = true;
@@ -790,7 +808,9 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             dn.n_tiles = (p.D + 15) / 16;
             dn.x = x;
             dn.x_ld = p.D;
-            if (p.ksplit && l + 1 < p.L) {
+            if (p.strip_down) {
+                launch_strip_resid<DT>(VS_KERNEL_DOWN, dn, s);
+            } else if (p.ksplit && l + 1 < p.L) {
                 launch_resid_ksplit<DT>(VS_KERNEL_DOWN, lw.wd, p.D, p.F, hmid, p.F, p.M, x, p.D, ksp, s,
                                         w->layers[l + 1].attn_norm, eps, xn);
                 xn_ready = true;
