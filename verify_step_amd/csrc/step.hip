@@ -16,6 +16,7 @@
 #include "error.h"
 #include "gemm.h"
 #include "gemm_big.h"
+#include "gemm_tile.h"
 #include "gemm_ksplit.h"
 #include "gemm_strip.h"
 #include "gemv.h"
@@ -163,6 +164,7 @@ struct Plan {
     bool ksplit_lm;              // the LM head too (logits and argmax partials after the sums)
     bool strip_qkv, strip_gu;    // q/k/v, gate/up through the full-reduction strip GEMM (epilogue in-kernel)
     bool strip_o, strip_down;    // the residual products through its one-unit variant (8..16 rows)
+    int tile_slices;             // > 1: more than 64 rows, residual products split K over this many slices
     int ks_slices;  // most slices of one of them (sizes the partial sums)
     bool gemv;      // the row-streaming path serves every product of the step
     bool merge_in_o; // the output product's prologue merges the key splits (no merge kernel)
@@ -301,6 +303,17 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
         p->strip_o = base_r && (p->H * p->Dh) % 128 == 0;
         p->strip_down = base_r && p->F % 128 == 0;
     }
+    // more than 64 rows (the pipelined tile GEMM): the residual products have D / 256 feature blocks
+    // x ceil(M / 128) row blocks of workgroups, too few for the CUs at prompt-chunk sizes; their
+    // reduction is then split into slices to make about one workgroup per CU (at most 8 slices, each
+    // at least one 64-element step). Measured at 7B widths and 576 rows (O / down): 1 slice 92 / 218 us,
+    // 2 slices 48 / 115, 3 slices 41 / 87, 4 slices 56 / 124.
+    p->tile_slices = 1;
+    if (p->dt != VS_F32 && d->M > 64 && p->D % 16 == 0 && (p->H * p->Dh) % kTileK == 0 && p->F % kTileK == 0) {
+        const long wgs = (long)((p->D / 16 + 15) / 16) * ((d->M + kTileRowsM - 1) / kTileRowsM);
+        const int nk = std::min(p->H * p->Dh, p->F) / kTileK;
+        p->tile_slices = (int)std::max<long>(1, std::min<long>({8L, (long)kNumCUs / wgs, (long)nk}));
+    }
     p->ksplit_lm = p->ksplit && d->M_log > 0;
     const long n_qkv = (long)(p->H + 2 * p->Hkv) * p->Dh, n_gu = 2L * p->F;
     long ks_floats = std::max<long>((long)p->ks_slices * p->D,
@@ -329,7 +342,8 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->off_part = take(M * p->H * p->n_splits * part_stride(p->Dh) * 4);
     p->off_xf = take(ML * p->D * p->esz);
     p->off_lmpart = take(ML * p->n_lm_parts * sizeof(ArgPart));
-    p->off_ksp = take(p->ksplit || p->ksplit_qkv ? (size_t)ks_floats * M * 4 : 4);
+    if (p->tile_slices > 1) ks_floats = std::max<long>(ks_floats, (long)p->tile_slices * p->D);
+    p->off_ksp = take(p->ksplit || p->ksplit_qkv || p->tile_slices > 1 ? (size_t)ks_floats * M * 4 : 4);
     p->total = o;
     return vs_ok();
 }
@@ -424,6 +438,37 @@ void launch_resid_ksplit(int kind, const void* w, int N, int K, const void* act,
     }
 }
 
+// The pipelined tile GEMM takes a product when its reduction is whole 64-element steps and its weight
+// segments whole 16-row blocks (q/k/v: whole 32-row tiles of each head); the LM head keeps the LDS-tiled
+// GEMM (its epilogue folds argmax partials per 16-feature tile).
+template <int EPI>
+bool tile_ok(const GemmArgs& g) {
+    if (EPI == EPI_LOGITS || g.K % kTileK != 0 || g.n0 % 16 != 0) return false;
+    if (EPI == EPI_QKV) return g.head_dim % 32 == 0 && g.n1 % 16 == 0 && g.n2 % 16 == 0;
+    return true;
+}
+
+// x += W a for more than 64 rows through the tile GEMM, the reduction split into `slices` slices whose
+// partial sums are added in slice order; with a gain the same reduction writes RMSNorm(x) * gain to y.
+template <int DT>
+void launch_resid_tile(int kind, const GemmArgs& g, int slices, float* part, hipStream_t s, const void* gain = nullptr,
+                       float eps = 0.f, void* y = nullptr) {
+    if constexpr (DT == F32) {
+        return;  // fp16 / bf16 only (the plan never selects this for fp32 models)
+    } else {
+        launchn(kind, gemm_tile_kernel<DT, EPI_RESID>, dim3(tile_grid(g.n_tiles, EPI_RESID, slices, g.M)), dim3(256), 0,
+                s, g, slices, part);
+        if (gain) {
+            launchn(kind, resid_norm_kernel<DT>, dim3(g.M), dim3(1024), 0, s, g.x, (const float*)part, slices, g.M, g.n0,
+                    gain, eps, y);
+        } else {
+            const long groups = (long)g.M * ((g.n0 + 3) / 4);
+            launchn(kind, resid_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, g.x, g.x_ld,
+                    (const float*)part, slices, g.M, g.n0);
+        }
+    }
+}
+
 template <int DT, int EPI>
 void launch_gemm(int kind, const GemmArgs& g, hipStream_t s) {
     const int M = g.M;
@@ -431,6 +476,11 @@ void launch_gemm(int kind, const GemmArgs& g, hipStream_t s) {
     if constexpr (DT != F32) {
         // more than 64 rows (a prompt chunk): LDS-tiled MFMA GEMM, eight paired (or two single) feature
         // tiles x 128 rows per workgroup
+        if (M > 64 && tile_ok<EPI>(g)) {
+            launchn(kind, gemm_tile_kernel<DT, EPI>, dim3(tile_grid(g.n_tiles, EPI, 1, M)), dim3(256), 0, s, g, 1,
+                    (float*)nullptr);
+            return;
+        }
         if (M > 64 && g.K % kBigK == 0) {
             constexpr int T = big_tiles(EPI);
             const dim3 grid((M + kBigRows - 1) / kBigRows, (g.n_tiles + T - 1) / T);
@@ -738,6 +788,9 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             o.x_ld = p.D;
             if (p.strip_o) {
                 launch_strip_resid<DT>(VS_KERNEL_OPROJ, o, s);
+            } else if (p.tile_slices > 1 && tile_ok<EPI_RESID>(o)) {
+                launch_resid_tile<DT>(VS_KERNEL_OPROJ, o, p.tile_slices, ksp, s, lw.ffn_norm, eps, xn);
+                xn_ready = true;
             } else if (p.ksplit) {
                 launch_resid_ksplit<DT>(VS_KERNEL_OPROJ, lw.wo, p.D, p.H * p.Dh, attn, p.H * p.Dh, p.M, x, p.D, ksp, s,
                                         lw.ffn_norm, eps, xn);
@@ -810,6 +863,13 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             dn.x_ld = p.D;
             if (p.strip_down) {
                 launch_strip_resid<DT>(VS_KERNEL_DOWN, dn, s);
+            } else if (p.tile_slices > 1 && tile_ok<EPI_RESID>(dn)) {
+                if (l + 1 < p.L) {
+                    launch_resid_tile<DT>(VS_KERNEL_DOWN, dn, p.tile_slices, ksp, s, w->layers[l + 1].attn_norm, eps, xn);
+                    xn_ready = true;
+                } else {
+                    launch_resid_tile<DT>(VS_KERNEL_DOWN, dn, p.tile_slices, ksp, s);
+                }
             } else if (p.ksplit && l + 1 < p.L) {
                 launch_resid_ksplit<DT>(VS_KERNEL_DOWN, lw.wd, p.D, p.F, hmid, p.F, p.M, x, p.D, ksp, s,
                                         w->layers[l + 1].attn_norm, eps, xn);
