@@ -2,10 +2,11 @@
 
 The shape: Llama 3.1 8B's widths ([KV Cache] section 03 lists it with 32 query heads over 8 K/V heads;
 section 04 defines grouped-query attention: each K/V head serves a group of 4 query heads), d_model
-4096, head_dim 128, MLP 14336, vocabulary 128256, bf16 weights and K/V, 32 layers. Two steps of
+4096, head_dim 128, MLP 14336, vocabulary 128256, bf16 weights and K/V, 32 layers. Three steps of
 different launch shapes: 16 sequences x 1 row (the 16-feature tile products; grouped heads through the
-matrix-core attention) and 8 sequences x 5 verify rows with fused acceptance (split-K products). The
-contexts are uniform in 128..4096, with pages scattered through a shuffled pool.
+matrix-core attention), 32 sequences x 1 row (split-K products; 256 (sequence, K/V head) pairs, so the
+grouped heads go through the VALU attention's four-head workgroups) and 8 sequences x 5 verify rows with
+fused acceptance. The contexts are uniform in 128..4096, with pages scattered through a shuffled pool.
 
 Rows are independent, so two sampled sequences per step are run by the oracle alone: their logits,
 greedy tokens and every K/V row they wrote in all 32 layers. The other sequences' pages hold
@@ -42,7 +43,7 @@ def env():
     w_cpu = W.make_weights(dims, SEED_W)
     model = GpuModel(dims, weights_cpu=w_cpu)
     max_blocks = -(-(CTX_HI + 5) // 16)
-    n_pages = 16 * max_blocks + 16
+    n_pages = 32 * max_blocks + 16
     pool = GpuPool(dims, n_pages)
     pool.view().normal_()  # pages of unsampled sequences keep arbitrary values
     ids = vs.kv_alloc(pool.handle, n_pages)
@@ -53,7 +54,7 @@ def env():
     pool.close()
 
 
-@pytest.mark.parametrize("B,K", [(16, 1), (8, 5)])
+@pytest.mark.parametrize("B,K", [(16, 1), (32, 1), (8, 5)])
 def test_8b_gqa_32_layers_sampled(env, B, K):
     dims, w_cpu, model, pool, max_blocks = env
     free0 = vs.kv_num_free(pool.handle)

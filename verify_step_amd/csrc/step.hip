@@ -242,7 +242,12 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
         // each page run as MFMA tiles of 16: HG heads of one K/V group (the largest power of two up to
         // 16 dividing the group) x 16 / HG rows
         const int group = m->n_heads / m->n_kv_heads;
-        p->attn_mfma = m->dtype != VS_F32 && m->head_dim == kAmDh && (d->max_rows >= 2 || group >= 2);
+        // One-row sequences with grouped heads take the matrix cores only while (sequence, K/V head)
+        // pairs are fewer than the CUs: with more, the VALU kernel's four-head workgroups stream K/V
+        // faster (measured at 8B widths, bf16, 64 decode rows, contexts 128..4096: 4.48 against 4.92 ms
+        // of attention per step; at one row the matrix cores win, 0.48 against 0.53 ms).
+        p->attn_mfma = m->dtype != VS_F32 && m->head_dim == kAmDh &&
+                       (d->max_rows >= 2 || (group >= 2 && (long)d->B * m->n_kv_heads < kNumCUs));
         // rows differ between sequences (a prompt chunk among decode rows): the one-row sequences,
         // which would fill one of the 16 states, go to the VALU kernel, whose one-state workgroups
         // stream K/V faster
