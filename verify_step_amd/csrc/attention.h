@@ -61,6 +61,15 @@ struct AttnArgs {
 __host__ __device__ constexpr int part_stride(int dh) { return dh + 4; }
 constexpr int kPartO = 4;  // offset of o in a split's statistics
 
+// c + a.lo * b.lo + a.hi * b.hi over two packed 16-bit values, fp32 accumulation
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    if constexpr (DT == F16)
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+    else
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 // o / l; a row with no visible key (l = 0, only if the block table is cut short) gives 0
 __device__ __forceinline__ float safe_div(float o, float l) { return l > 0.f ? o / l : 0.f; }
 
@@ -68,6 +77,7 @@ template <int DT, int DH, int RMAX, int NW, int HG, int KVT = DT>  // KVT: the c
 __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
     constexpr int DPL = DH / 16;  // dims per lane
     constexpr int NS = RMAX * HG;  // online-softmax states: (row, head) pairs
+    constexpr bool kDot2 = (DT == F16 || DT == BF16) && KVT == DT;  // scores by packed 16-bit dot products
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -99,7 +109,11 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
         const int nr = min(RMAX, R - rg);
         const int n_pages = min((ctx + rg + nr + T - 1) / T, a.max_blocks);
         const int p_end = min(p_begin + a.split_pages, n_pages);
+        // q: with a 16-bit cache of the model's type, raw pairs for the packed dot products (the
+        // products of two 16-bit values are exact in fp32; the scale is applied to the summed score);
+        // otherwise widened and prescaled
         float qr[NS][DPL];
+        uint32_t qw[NS][DPL / 2];
         float o[NS][DPL];
         float m[NS], l[NS];
 #pragma unroll
@@ -109,10 +123,15 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
             l[st] = 0.f;
 #pragma unroll
             for (int e = 0; e < DPL; ++e) o[st][e] = 0.f;
-            if (i < nr) {
-                load_widen<DT, DPL>(reinterpret_cast<const char*>(a.q) +
-                                        ((long)(r0 + rg + i) * QLD + (long)(h0 + j) * DH + c * DPL) * St<DT>::bytes,
-                                    qr[st]);
+            const char* qp = reinterpret_cast<const char*>(a.q) +
+                             ((long)(r0 + rg + (i < nr ? i : 0)) * QLD + (long)(h0 + j) * DH + c * DPL) * St<DT>::bytes;
+            if constexpr (kDot2) {
+                RawVec<DT, DPL> qv;
+                load_raw<DT, DPL>(qv, qp);
+#pragma unroll
+                for (int w = 0; w < DPL / 2; ++w) qw[st][w] = i < nr ? qv.w[w] : 0u;
+            } else if (i < nr) {
+                load_widen<DT, DPL>(qp, qr[st]);
 #pragma unroll
                 for (int e = 0; e < DPL; ++e) qr[st][e] *= a.scale_log2;
             } else {
@@ -141,9 +160,15 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     float d = 0.f;
+                    if constexpr (kDot2) {
 #pragma unroll
-                    for (int e = 0; e < DPL; ++e) d += qr[st][e] * raw_at<KVT, DPL>(kk[u], e);
-                    d = row16_sum(d);  // the 16 lanes of a key slot hold its 16 dim chunks
+                        for (int w = 0; w < DPL / 2; ++w) d = dot2<DT>(qw[st][w], kk[u].w[w], d);
+                        d = row16_sum(d) * a.scale_log2;  // the 16 lanes of a key slot hold its 16 dim chunks
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < DPL; ++e) d += qr[st][e] * raw_at<KVT, DPL>(kk[u], e);
+                        d = row16_sum(d);
+                    }
                     const int kp = p * T + 4 * u + g;
                     sc[u] = (kp <= qpos) ? d : -INFINITY;
                 }
