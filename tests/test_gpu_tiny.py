@@ -418,10 +418,12 @@ def test_tiny_validation_word_flags_bad_inputs(dtype):
     rows = alloc_rows(pool, [20, 9])
     flags = torch.zeros(1, dtype=torch.int32, device="cuda")
 
-    def step(tokens, bt_patch=None, ctx=(19, 8)):
+    def step(tokens, bt_patch=None, ctx=(19, 8), ctx_patch=None):
         sb = make_step(model, pool, [SeqSpec(ctx[0], [tokens[0]]), SeqSpec(ctx[1], [tokens[1]])], rows, max_blocks=4)
         if bt_patch is not None:
             sb.block_tables[bt_patch[0], bt_patch[1]] = bt_patch[2]
+        if ctx_patch is not None:  # a context length the caller got wrong (the step treats it as 0)
+            sb.ctx_len[ctx_patch[0]] = ctx_patch[1]
         flags.zero_()
         sb.desc.error_flags = flags.data_ptr()
         run_step(model, sb)
@@ -435,4 +437,5 @@ def test_tiny_validation_word_flags_bad_inputs(dtype):
     assert step([3, 4], bt_patch=(0, 1, pool.num_pages + 3)) == vs.VS_STEP_BAD_PAGE  # row 0 reads page 1
     assert step([3, 4], bt_patch=(1, 2, pool.num_pages + 3)) == 0  # past row 1's pages: never read
     assert step([dims.vocab, 4], bt_patch=(1, 0, -2)) == vs.VS_STEP_BAD_TOKEN | vs.VS_STEP_BAD_PAGE
+    assert step([3, 4], ctx_patch=(1, -3)) == vs.VS_STEP_BAD_BATCH
     pool.close()
