@@ -162,7 +162,8 @@ struct Plan {
     bool ksplit;  // residual products through the split-K tile GEMM
     bool ksplit_qkv, ksplit_gu;  // the q/k/v and gate/up products too (their epilogues after the sums)
     bool ksplit_lm;              // the LM head too (logits and argmax partials after the sums)
-    bool strip_qkv, strip_gu;    // q/k/v, gate/up through the full-reduction strip GEMM (epilogue in-kernel)
+    bool strip_qkv;              // q/k/v through the full-reduction strip GEMM (epilogue in-kernel)
+    int strip_gu;                // gate/up through it: its units per workgroup (6 or 7), 0 when not
     bool strip_o, strip_down;    // the residual products through its one-unit variant (8..16 rows)
     int tile_slices;             // > 1: more than 64 rows, residual products split K over this many slices
     int ks_slices;  // most slices of one of them (sizes the partial sums)
@@ -301,7 +302,10 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
         };
         const bool base = p->dt != VS_F32 && !p->gemv && d->M >= 8 && d->M <= 64 && p->D % 128 == 0;
         p->strip_qkv = base && p->Dh % 16 == 0 && strip_ok((long)(p->H + 2 * p->Hkv) * p->Dh / 16, kStripUnitsQkv);
-        p->strip_gu = base && p->F % 8 == 0 && strip_ok(p->F / 8, kStripUnitsGu);
+        p->strip_gu = !(base && p->F % 8 == 0) ? 0
+                      : strip_ok(p->F / 8, kStripUnitsGu)     ? kStripUnitsGu
+                      : strip_ok(p->F / 8, kStripUnitsGuWide) ? kStripUnitsGuWide
+                                                                : 0;
         // the residual products: one unit per workgroup, up to 16 rows (one row tile; every CU reads
         // all of X, which past 16 rows outweighs its share of the weights)
         const bool base_r = base && d->M <= 16 && p->D % 16 == 0 && strip_ok(p->D / 16, 1);
@@ -833,7 +837,10 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             gu.h_ld = p.F;
             if (p.strip_gu) {
                 gu.n_tiles = p.F / 8;
-                launch_strip<DT, EPI_SWIGLU, kStripUnitsGu>(VS_KERNEL_GATEUP, gu, s);
+                if (p.strip_gu == kStripUnitsGuWide)
+                    launch_strip<DT, EPI_SWIGLU, kStripUnitsGuWide>(VS_KERNEL_GATEUP, gu, s);
+                else
+                    launch_strip<DT, EPI_SWIGLU, kStripUnitsGu>(VS_KERNEL_GATEUP, gu, s);
             } else if (p.ksplit_gu) {
                 const int slices = launch_ksplit<DT>(VS_KERNEL_GATEUP, lw.wg, lw.wu, lw.wu, p.F, p.F, 2 * p.F, p.D, xn,
                                                      p.D, p.M, ksp, s);
