@@ -38,6 +38,7 @@ constexpr int kStripSlab = 16 * kStripRowB;   // one wave's slab
 // 6; the 8B-GQA widths' 1792 gate/up units -> 256 workgroups of 7).
 __host__ __device__ constexpr int strip_max_units(int MT) { return 7; }
 constexpr int kStripUnitsQkv = 3;
+constexpr int kStripUnitsQkvNarrow = 2;
 constexpr int kStripUnitsGu = 6;
 constexpr int kStripUnitsGuWide = 7;
 
@@ -85,7 +86,7 @@ struct StripChunk {
 
 template <int DT, int MT, int EPI, int U>
 __global__ void __launch_bounds__(kStripWaves * 64, 1) gemm_strip_kernel(GemmArgs g) {
-    static_assert(U == 3 || U == 6 || U == 7, "the chunk ring is laid out for 3, 6 or 7 units");
+    static_assert(U == 2 || U == 3 || U == 6 || U == 7, "the chunk ring is laid out for 2, 3, 6 or 7 units");
     typedef const __attribute__((address_space(1))) u32x4_t* gptr;
     const int K = g.K, M = g.M;
     const int lane = threadIdx.x & 63;
@@ -187,7 +188,7 @@ __global__ void __launch_bounds__(kStripWaves * 64, 1) gemm_strip_kernel(GemmArg
     // fills the ring a whole number of times, so every slot index below is a constant. (Measured on
     // 7B widths: three X buffers with a deeper ring, or A fragments loaded straight from memory without
     // the slab, both ran slower.)
-    constexpr int R = U == 7 ? 7 : 6;  // a pair of blocks (2 U chunks) fills the ring a whole number of times
+    constexpr int R = U == 7 ? 7 : U == 2 ? 4 : 6;  // a pair of blocks (2 U chunks) fills the ring a whole number of times
     constexpr int AHEAD = R - 1 < U ? R - 1 : U;
     constexpr int XJ = U - AHEAD;
     StripChunk ring[R];

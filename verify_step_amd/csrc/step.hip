@@ -162,7 +162,8 @@ struct Plan {
     bool ksplit;  // residual products through the split-K tile GEMM
     bool ksplit_qkv, ksplit_gu;  // the q/k/v and gate/up products too (their epilogues after the sums)
     bool ksplit_lm;              // the LM head too (logits and argmax partials after the sums)
-    bool strip_qkv;              // q/k/v through the full-reduction strip GEMM (epilogue in-kernel)
+    int strip_qkv;               // q/k/v through the full-reduction strip GEMM (epilogue in-kernel): units per
+                                 // workgroup (3 or 2), 0 when not
     int strip_gu;                // gate/up through it: its units per workgroup (6 or 7), 0 when not
     bool strip_o, strip_down;    // the residual products through its one-unit variant (8..16 rows)
     int tile_slices;             // > 1: more than 64 rows, residual products split K over this many slices
@@ -301,7 +302,15 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
             return U <= strip_max_units(MT) && wgs <= kNumCUs && wgs * 100 >= 85L * kNumCUs;
         };
         const bool base = p->dt != VS_F32 && !p->gemv && d->M >= 8 && d->M <= 64 && p->D % 128 == 0;
-        p->strip_qkv = base && p->Dh % 16 == 0 && strip_ok((long)(p->H + 2 * p->Hkv) * p->Dh / 16, kStripUnitsQkv);
+        // q/k/v units that do not fill whole three-unit workgroups (the 8B-GQA widths: 384 units) may go two
+        // to a workgroup on 75 % of the CUs up to 48 rows (8 x 5 verify rows: 19.6 against 21.3 us per layer
+        // for split-K + its rotary reduction; at 64 rows 25.2 against 24.5, so split-K stays there)
+        const long qkv_units = (long)(p->H + 2 * p->Hkv) * p->Dh / 16;
+        const bool narrow_ok = MT <= 3 && (qkv_units + 1) / 2 <= kNumCUs && (qkv_units + 1) / 2 * 100 >= 70L * kNumCUs;
+        p->strip_qkv = !(base && p->Dh % 16 == 0)           ? 0
+                       : strip_ok(qkv_units, kStripUnitsQkv) ? kStripUnitsQkv
+                       : narrow_ok                           ? kStripUnitsQkvNarrow
+                                                             : 0;
         p->strip_gu = !(base && p->F % 8 == 0) ? 0
                       : strip_ok(p->F / 8, kStripUnitsGu)     ? kStripUnitsGu
                       : strip_ok(p->F / 8, kStripUnitsGuWide) ? kStripUnitsGuWide
@@ -747,7 +756,10 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
             q.layer = l;
             if (p.strip_qkv) {
                 q.n_tiles = (p.H + 2 * p.Hkv) * p.Dh / 16;
-                launch_strip<DT, EPI_QKV, kStripUnitsQkv>(VS_KERNEL_QKV, q, s);
+                if (p.strip_qkv == kStripUnitsQkvNarrow)
+                    launch_strip<DT, EPI_QKV, kStripUnitsQkvNarrow>(VS_KERNEL_QKV, q, s);
+                else
+                    launch_strip<DT, EPI_QKV, kStripUnitsQkv>(VS_KERNEL_QKV, q, s);
             } else if (p.ksplit_qkv) {
                 const int N = q.n0 + q.n1 + q.n2;
                 const int slices = launch_ksplit<DT>(VS_KERNEL_QKV, lw.wq, lw.wk, lw.wv, q.n0, q.n1, N, p.D, xn, p.D,
