@@ -332,7 +332,9 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
         const int nk = std::min(p->H * p->Dh, p->F) / kTileK;
         p->tile_slices = (int)std::max<long>(1, std::min<long>({8L, (long)kNumCUs / wgs, (long)nk}));
     }
-    p->ksplit_lm = p->ksplit && d->M_log > 0;
+    // the LM head goes by its own rows: 17..64 logit rows through split-K also in a longer step (a prompt
+    // chunk beside 64 decode rows), where the 16-feature tiles took 155 us per step
+    p->ksplit_lm = p->dt != VS_F32 && !p->gemv && d->M_log > 0 && d->M_log <= 64 && (p->ksplit || d->M_log > 16);
     const long n_qkv = (long)(p->H + 2 * p->Hkv) * p->Dh, n_gu = 2L * p->F;
     long ks_floats = std::max<long>((long)p->ks_slices * p->D,
                                     std::max((long)ks_shape(n_qkv, p->D, d->M).slices * n_qkv,
@@ -361,7 +363,7 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->off_xf = take(ML * p->D * p->esz);
     p->off_lmpart = take(ML * p->n_lm_parts * sizeof(ArgPart));
     if (p->tile_slices > 1) ks_floats = std::max<long>(ks_floats, (long)p->tile_slices * p->D);
-    p->off_ksp = take(p->ksplit || p->ksplit_qkv || p->tile_slices > 1 ? (size_t)ks_floats * M * 4 : 4);
+    p->off_ksp = take(p->ksplit || p->ksplit_qkv || p->ksplit_lm || p->tile_slices > 1 ? (size_t)ks_floats * M * 4 : 4);
     p->total = o;
     return vs_ok();
 }
