@@ -436,9 +436,47 @@ def other_workload(args):
         "weight_stream": weight_stream(dims, kt, n_rf),
         "attention": attention_stream(kt, n_rf, kv_read + M * kvpt),
     }
+    if not args.no_cpu_baseline:
+        if kv8:
+            result["cpu_baseline"] = {"value": None, "unit": "rows/s", "kind": "oracle",
+                                      "sample": "not run: the oracle's 8-bit cache path is timed on the 16-bit shapes"}
+        else:
+            if chunk:  # two decode rows of the step and the first 16 rows of its prompt chunk
+                sample, label = [(ctxs[0], K), (ctxs[1], K), (0, 16)], "2 decode rows + 16 prompt-chunk rows"
+            elif K > 1:  # one sequence's verify rows
+                sample, label = [(ctxs[0], K)], f"1 sequence x {K} verify rows at context {ctxs[0]}"
+            elif B > 1:  # two sequences of the batch
+                sample, label = [(ctxs[0], 1), (ctxs[1], 1)], f"2 of the {B} sequences (contexts {ctxs[0]}, {ctxs[1]})"
+            else:
+                sample, label = [(ctxs[0], 1)], f"1 decode row at context {ctxs[0]}"
+            result["cpu_baseline"] = other_cpu_baseline(dims, 1000 * wl + 1, sample, label)
     if args.copy_calibration:
         copy_calibration()
     print(json.dumps(result), flush=True)
+
+
+def other_cpu_baseline(dims, seed, sample, label):
+    """The oracle, as it stands, on a bounded sample of a workload's rows (the whole step would take many
+    minutes on the host): the sampled sequences, each with its context and rows, in one oracle step on the
+    same weights; reported as rows per second. Cached K/V are zeros (the oracle's time does not depend on
+    them)."""
+    import torch
+
+    import oracle
+    from synth import workloads as W
+
+    log(f"cpu baseline: one oracle step over {label}")
+    w_cpu = W.make_weights(dims, seed)
+    seqs = []
+    for ctx, n in sample:
+        kv = torch.zeros(dims.n_layers, 2, ctx + n, dims.n_kv_heads, dims.head_dim, dtype=dims.torch_dtype)
+        seqs.append(oracle.SeqState(kv, ctx, [1 + 7 * i for i in range(n)]))
+    rows = sum(n for _, n in sample)
+    t0 = time.perf_counter()
+    oracle.decode_step(dims, w_cpu, seqs)
+    dt = time.perf_counter() - t0
+    return {"value": round(rows / dt, 5), "unit": "rows/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"{label}, {dims.name} {dims.dtype} (float64 PyTorch CPU oracle): {rows} rows in {dt:.1f} s"}
 
 
 SAMPLE_WORKLOADS = {
