@@ -404,7 +404,9 @@ def other_workload(args):
         rows.append(vs.kv_append(pool.handle, [], max_blocks, 0, chunk))
         specs.append(SeqSpec(0, W.token_ids(1000 * wl + 3, 999, chunk, dims.vocab), want_logits=False))
     g0 = [0] * len(specs) if K > 1 else None
-    sb = make_step(model, pool, specs, rows, max_blocks=max_blocks, want_logits_tensor=False, g0=g0)
+    # sequences on one shared prefix form a prefix group (the prefix's pages read once for the group)
+    groups = [(16 * p, 16, 1024 // 16) for p in range(B // 16)] if ctx_rule == "prefix" else None
+    sb = make_step(model, pool, specs, rows, max_blocks=max_blocks, want_logits_tensor=False, g0=g0, groups=groups)
     stream = torch.cuda.current_stream().cuda_stream
 
     def step():
@@ -423,6 +425,8 @@ def other_workload(args):
     M = sum(len(s.tokens) for s in specs)
     kvpt = 2 * dims.n_layers * dims.n_kv_heads * dims.head_dim * dims.kv_elem_bytes
     kv_read = sum(s.ctx + len(s.tokens) for s in specs) * kvpt  # logical K/V bytes the attention reads
+    if groups:  # a prefix group's shared pages are read once for all of its sequences
+        kv_read -= sum((n - 1) * pages * 16 for _, n, pages in groups) * kvpt
     step_bytes = streamed_weight_bytes(dims) + kv_read + M * kvpt
     n_rf = min(args.steps, ROOFLINE_STEPS)
     kt = kernel_times(vs, step, n_rf, 8 * dims.n_layers)
@@ -432,6 +436,7 @@ def other_workload(args):
         "step_bytes": step_bytes, "step_TBps": round(step_bytes / (ms * 1e-3) / 1e12, 4),
         "step_frac_of_hbm_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "contexts": [min(ctxs), max(ctxs)], "prompt_chunk_rows": chunk, "model_shape": dims.name,
+        "prefix_groups": [list(g) for g in groups] if groups else None,
         "kv_cache": dims.kv_type,
         "weight_stream": weight_stream(dims, kt, n_rf),
         "attention": attention_stream(kt, n_rf, kv_read + M * kvpt),
@@ -601,8 +606,8 @@ def weight_stream(dims, kt, n_steps):
 
 
 def attention_stream(kt, n_steps, kv_bytes):
-    """Logical K/V bytes per step (every cached key and value the step's rows attend to, plus the rows
-    written) over the attention and merge kernels' time per step."""
+    """Logical K/V bytes per step (every cached key and value the step's rows attend to, a prefix group's
+    shared pages once, plus the rows written) over the attention and merge kernels' time per step."""
     us = (sum(kt["attn"]["launch_us"]) + sum(kt["merge"]["launch_us"])) / n_steps
     gbps = kv_bytes / (us * 1e-6) / 1e9
     return {"kv_bytes_per_step": int(kv_bytes), "us_per_step": round(us, 2), "achieved": round(gbps, 1),

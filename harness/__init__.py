@@ -137,7 +137,9 @@ class StepBuffers:
 
 
 def make_step(model: GpuModel, pool: GpuPool, seqs: list[SeqSpec], rows: list[list[int]], max_blocks: int | None = None,
-              want_logits_tensor: bool = True, g0: list[int] | None = None, device: str = "cuda") -> StepBuffers:
+              want_logits_tensor: bool = True, g0: list[int] | None = None, device: str = "cuda",
+              groups: list[tuple[int, int, int]] | None = None) -> StepBuffers:
+    """One step's device buffers. groups: shared-prefix groups (first sequence, sequences, prefix pages)."""
     d = model.dims
     B = len(seqs)
     q_start = [0]
@@ -167,6 +169,14 @@ def make_step(model: GpuModel, pool: GpuPool, seqs: list[SeqSpec], rows: list[li
     desc = vs.vs_batch_desc(B, M, len(logit_rows), max(len(s.tokens) for s in seqs), max_ctx, max_blocks,
                             pool.handle, bufs["q_start"].data_ptr(), bufs["ctx_len"].data_ptr(),
                             bufs["tokens"].data_ptr(), bufs["logit_rows"].data_ptr() if logit_rows else None)
+    keep = []
+    if groups:
+        gt = torch.tensor(groups, dtype=torch.int32).t().contiguous().to(device)  # rows: seq0, n, pages
+        keep.append(gt)
+        desc.n_prefix_groups = len(groups)
+        desc.max_group_size = max(g[1] for g in groups)
+        desc.max_group_pages = max(g[2] for g in groups)
+        desc.group_seq0, desc.group_n, desc.group_pages = gt[0].data_ptr(), gt[1].data_ptr(), gt[2].data_ptr()
     ws_bytes = vs.decode_step_workspace_bytes(desc, model_desc(d))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
     extra = {}
@@ -178,7 +188,7 @@ def make_step(model: GpuModel, pool: GpuPool, seqs: list[SeqSpec], rows: list[li
                          extra["g0"].data_ptr() if extra else None,
                          extra["accept_len"].data_ptr() if extra else None,
                          extra["bonus"].data_ptr() if extra else None)
-    return StepBuffers(desc=desc, out=out, logits=logits, ws=ws, ws_bytes=ws_bytes, **bufs, **extra)
+    return StepBuffers(desc=desc, out=out, logits=logits, ws=ws, ws_bytes=ws_bytes, **bufs, **extra, keep=keep)
 
 
 def run_step(model: GpuModel, sb: StepBuffers, stream: torch.cuda.Stream | None = None) -> None:

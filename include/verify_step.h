@@ -248,6 +248,22 @@ typedef struct vs_batch_desc {
                                   with the clamped values. The caller zeroes the word beforehand and
                                   reads it after the stream reaches the step; any bit set means
                                   the step's outputs are not valid (treat as VS_ERR_INVALID). */
+    /* Shared-prefix groups, a hint (n_prefix_groups = 0: none). Group g is the sequences
+       group_seq0[g] .. group_seq0[g] + group_n[g] - 1, each bringing exactly one row, whose block
+       tables hold the same first group_pages[g] page ids (a prefix found with kv_prefix_lookup or
+       shared with kv_share: [KV Cache] section 05, "Prefix caching", the shared blocks stored
+       once) and whose contexts cover those pages (ctx_len >= 16 * group_pages[g]). The step then
+       reads those pages once per group for all of the group's rows, and each sequence's own pages
+       after them, the two parts merged as key splits are ([KV Cache] section 07). The groups are
+       used for fp16 / bf16 models with head_dim 128 and ignored otherwise; with error_flags set,
+       a group whose rows or block tables break these conditions raises VS_STEP_BAD_BATCH (the
+       results of its rows are then not valid). Groups are disjoint. */
+    int32_t n_prefix_groups;    /* >= 0 (host) */
+    int32_t max_group_size;     /* >= every group_n[g] (host) */
+    int32_t max_group_pages;    /* >= every group_pages[g] (host) */
+    const int32_t* group_seq0;  /* device [n_prefix_groups], or NULL when there are none */
+    const int32_t* group_n;     /* device [n_prefix_groups], each >= 1 */
+    const int32_t* group_pages; /* device [n_prefix_groups], each >= 1 */
 } vs_batch_desc;
 
 #define VS_STEP_BAD_TOKEN 1
@@ -276,7 +292,14 @@ vs_status decode_step_workspace_bytes(const vs_batch_desc* desc, const vs_model_
  * RMSNorm, gate/up product with SwiGLU, down product + residual; final RMSNorm
  * and LM head on the logit rows, with the per-row argmax and top-2 gap.
  * block_tables: device [B][max_blocks] int32 page ids. ws: device workspace of
- * at least decode_step_workspace_bytes. */
+ * at least decode_step_workspace_bytes. Work is queued on `stream` in order; in
+ * a step that mixes one-row sequences with longer ones, or has prefix groups,
+ * one attention kernel per layer runs on a second stream the library keeps per
+ * device (default priority), forked from `stream` and joined back into it by
+ * events before the next work on `stream`, so the step still completes in
+ * `stream`'s order and may be captured into a graph. The second stream is
+ * made by the first such step on a device whose stream is not being captured;
+ * until then the kernels run one after the other on `stream`. */
 vs_status decode_step(const vs_batch_desc* desc, const int32_t* block_tables, const vs_weights* weights,
                       const vs_step_out* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -292,7 +315,8 @@ vs_status decode_step(const vs_batch_desc* desc, const int32_t* block_tables, co
  * at 64 rows does not). Every call on one GPU shares that GPU's array:
  * calls that overlap on one GPU (two streams, two threads) race and give
  * undefined results; calls serialised on one stream are safe. Nothing in the
- * array needs to start at zero. The current device must be the stream's. */
+ * array needs to start at zero. The current device must be the stream's.
+ * Every kernel runs on `stream` (no second stream is made or used). */
 #define VS_NOALLOC_SCRATCH_BYTES (96u << 20)
 vs_status decode_step_noalloc(const vs_batch_desc* desc, const int32_t* block_tables, const vs_weights* weights,
                               const vs_step_out* out, hipStream_t stream);

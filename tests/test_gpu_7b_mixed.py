@@ -13,6 +13,8 @@ the tile (MFMA) path.
 Checked against the oracle on one sampled decode sequence per prefix and on
 the whole chunk: logits, greedy tokens, and every K/V row written (the
 chunk's 512 rows in all 32 layers). The shared prefix pages must be untouched.
+The step runs twice: with each prompt's 16 sequences named as a prefix group
+(their 64 shared pages read once per group and head) and without groups.
 Through 32 layers the bound of a row is the stated tolerance or twice the
 distance between the oracle's float64 and fp32 realisations, whichever is
 larger.
@@ -102,21 +104,33 @@ def test_7b_shared_prefixes_and_prompt_chunk():
                                               dtype=dims.torch_dtype), 0, list(chunk_tok), want_logits=False))
     order.append(B_dec)
 
-    _say("7B fp16 mixed: GPU step, M = 576")
-    sb = make_step(model, pool, specs, rows, max_blocks=max_blocks)
-    vs.decode_step(sb.desc, sb.block_tables, model.w, sb.out, sb.ws, sb.ws_bytes,
-                   torch.cuda.current_stream().cuda_stream)
-    torch.cuda.synchronize()
+    # each prompt's 16 sequences form a prefix group over its 64 pages; the step runs with the groups
+    # (the prefixes read once per group) and without them, the same K/V rows written by both
+    groups = [(p * PER_PREFIX, PER_PREFIX, PREFIX // 16) for p in range(N_PREFIX)]
+    runs = {}
+    for label, g in (("prefix groups", groups), ("no groups", None)):
+        _say(f"7B fp16 mixed: GPU step, M = 576, {label}")
+        sb = make_step(model, pool, specs, rows, max_blocks=max_blocks, groups=g)
+        flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+        sb.desc.error_flags = flags.data_ptr()
+        vs.decode_step(sb.desc, sb.block_tables, model.w, sb.out, sb.ws, sb.ws_bytes,
+                       torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert int(flags.item()) == 0, f"{label}: validation word {int(flags.item())}"
+        runs[label] = sb
     _say("7B fp16 mixed: oracle on the sampled sequences and the chunk")
     states32 = [oracle.SeqState(st.kv.clone(), st.ctx, list(st.tokens), st.want_logits) for st in states]
     ref = oracle.decode_step(dims, w_cpu, states)
     alt = oracle.decode_step(dims, w_cpu, states32, compute="f32")
     tol = TOL[dims.dtype]
-    am = sb.argmax[:B_dec + CHUNK].cpu().tolist()
     ties = TieLog()
+    for label, sb in runs.items():
+        am = sb.argmax[:B_dec + CHUNK].cpu().tolist()
+        for j, b in enumerate(order[:-1]):
+            check_rows([sb.logits[b].cpu()], [ref.logits[j]], tol, f"{label}: decode seq {b} logits", [alt.logits[j]])
+            ties.check(am[b], ref.argmax[j], ref.logits[j], ref.gap[j], f"{label}: decode seq {b}", alt.logits[j])
+        assert all(a == -1 for a in am[B_dec:]), "chunk rows carry no logits"
     for j, b in enumerate(order[:-1]):
-        check_rows([sb.logits[b].cpu()], [ref.logits[j]], tol, f"decode seq {b} logits", [alt.logits[j]])
-        ties.check(am[b], ref.argmax[j], ref.logits[j], ref.gap[j], f"decode seq {b}", alt.logits[j])
         c = specs[b].ctx
         got = pool.read(rows[b], c, c + 1).double()
         want = states[j].kv[:, :, c:c + 1].double()
@@ -124,7 +138,6 @@ def test_7b_shared_prefixes_and_prompt_chunk():
         err = (got - want).abs().amax(dim=(3, 4)) / want.abs().amax(dim=(3, 4))
         bound = (2 * (want32 - want).abs().amax(dim=(3, 4)) / want.abs().amax(dim=(3, 4))).clamp(min=tol)
         assert bool((err <= bound).all()), f"decode seq {b} K/V rows: worst error / bound {float((err / bound).max()):.3f}"
-    assert all(a == -1 for a in am[B_dec:]), "chunk rows carry no logits"
     got = pool.read(crow, 0, CHUNK).double()  # [layer][2][512][heads][dim]
     want = states[-1].kv.double()
     want32 = states32[-1].kv.double()

@@ -64,7 +64,9 @@ class vs_batch_desc(Structure):
     _fields_ = [("B", c_int32), ("M", c_int32), ("M_log", c_int32), ("max_rows", c_int32), ("max_ctx", c_int32),
                 ("max_blocks", c_int32), ("pool", c_void_p), ("q_start", c_void_p), ("ctx_len", c_void_p),
                 ("tokens", c_void_p), ("logit_rows", c_void_p), ("ctx_advance", c_void_p),
-                ("error_flags", c_void_p)]
+                ("error_flags", c_void_p), ("n_prefix_groups", c_int32), ("max_group_size", c_int32),
+                ("max_group_pages", c_int32), ("group_seq0", c_void_p), ("group_n", c_void_p),
+                ("group_pages", c_void_p)]
 
 
 class vs_step_out(Structure):

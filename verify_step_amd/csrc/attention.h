@@ -10,7 +10,8 @@
 // tile outputs).
 //
 // With a single split the workgroup's state is final: it writes the attention
-// output itself (o / l in the storage type) and no merge is needed.
+// output itself (o / l in the storage type) and no merge is needed (with
+// shared-prefix groups: a row outside any group whose own pages form one split).
 // One workgroup of NW waves per (split, head, sequence, row-group block). Wave w takes pages
 // w, w+NW, ... of the split. A prompt chunk's rows are spread over row-group blocks, so its
 // row groups run in parallel. Lane l owns dims [(l%16)*DH/16, +DH/16) of key slot
@@ -55,6 +56,28 @@ struct AttnArgs {
     void* out;         // [M][n_heads*DH] storage type
     int rows_lo, rows_hi;  // a workgroup serves only sequences of rows_lo..rows_hi rows (a step that mixes
                            // one-row and longer sequences runs each kind through its own kernel)
+    // Shared-prefix groups ([KV Cache] section 05, prefix caching: one copy of a common prefix's pages
+    // serves several sequences). A grouped sequence (one row, seq_gp[b] = gp > 0) has the key splits
+    // [0, n_pre_splits) over its group's gp prefix pages, computed once for the whole group by the
+    // matrix-core kernel's group blocks, and the splits [n_pre_splits, n_splits) over its own pages
+    // gp .. n_pages - 1. Any other sequence has only the splits [n_pre_splits, n_splits), over all its
+    // pages (split_pages each): the workgroups of a plain launch take split n_pre_splits + blockIdx.x,
+    // and the merge skips the first n_pre_splits splits of such rows. seq_gp = nullptr: no groups
+    // (n_pre_splits = 0).
+    const int* seq_gp;       // [B] prefix pages read by the sequence's group (0: not grouped)
+    const int* seq_group;    // [B] the sequence's group (-1: none)
+    const int* group_seq0;   // [n_groups] first sequence of each group (consecutive sequences)
+    const int* group_n;      // [n_groups] sequences in each group
+    const int* group_pages;  // [n_groups] prefix pages of each group
+    int n_pre_splits, pre_split_pages;
+    int gz_blocks;     // the matrix-core kernel's grid z blocks [0, gz_blocks) are group blocks
+    int gz_per_group;  // group blocks per group (16 / HG sequences each)
+    const int* row_seq;  // [M] each row's sequence (read by the merge kernel with groups)
+    // The matrix-core kernel's work list (nullptr: none): its plain block z - gz_blocks takes the unit
+    // items[z - gz_blocks] = (sequence, first row of the row group) if below *n_items, else nothing;
+    // without a list it takes sequence z % B and every rg_blocks-th row group from z / B on.
+    const int2* items;
+    const int* n_items;
 };
 
 // One split's statistics: m, l, two unused floats (so o starts 16-byte aligned), o[dh].
@@ -70,6 +93,21 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
         return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// The pages [p_begin, p_end) of key split s >= n_pre_splits of a sequence with n_pages pages: the plain
+// splits of split_pages pages, or, for a grouped sequence (gp prefix pages), its own pages gp .. n_pages - 1
+// cut evenly over the splits after the prefix splits.
+__device__ __forceinline__ void split_range(const AttnArgs& a, int s, int gp, int n_pages, int& p_begin, int& p_end) {
+    if (gp > 0) {
+        const int ss = a.n_splits - a.n_pre_splits;
+        const int sp = (max(n_pages - gp, 0) + ss - 1) / ss;
+        p_begin = gp + (s - a.n_pre_splits) * sp;
+        p_end = min(p_begin + sp, n_pages);
+    } else {
+        p_begin = (s - a.n_pre_splits) * a.split_pages;
+        p_end = min(p_begin + a.split_pages, n_pages);
+    }
+}
+
 // o / l; a row with no visible key (l = 0, only if the block table is cut short) gives 0
 __device__ __forceinline__ float safe_div(float o, float l) { return l > 0.f ? o / l : 0.f; }
 
@@ -83,7 +121,7 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
     const int g = lane >> 4;  // key slot within a group of four
     const int c = lane & 15;  // dim chunk
-    const int s = blockIdx.x, h0 = blockIdx.y * HG;  // query heads h0 .. h0 + HG - 1 share K/V head hk
+    const int s = a.n_pre_splits + blockIdx.x, h0 = blockIdx.y * HG;  // query heads h0 .. h0 + HG - 1 share K/V head hk
     const int b = blockIdx.z % a.B, rgb = blockIdx.z / a.B;
     const int group = a.n_heads / a.n_kv_heads;
     const int hk = h0 / group;
@@ -91,9 +129,9 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
     const int r0 = min(max(a.q_start[b], 0), a.M);
     const int R = min(max(a.q_start[b + 1] - r0, 0), a.M - r0);
     if (R < a.rows_lo || R > a.rows_hi) return;  // another kernel's sequence
+    const int gp = a.seq_gp ? a.seq_gp[b] : 0;  // a grouped sequence: its prefix splits come from the group
     const int ctx = max(a.ctx_len[b], 0);
     const int T = a.page_tokens;
-    const int p_begin = s * a.split_pages;
 
     const int* bt = a.block_tables + (long)b * a.max_blocks;
     const long kofs = (long)a.layer * a.layer_elems + (long)hk * T * DH + (long)c * DPL;
@@ -108,7 +146,8 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
     for (int rg = rgb * RMAX; rg < R; rg += a.rg_blocks * RMAX) {
         const int nr = min(RMAX, R - rg);
         const int n_pages = min((ctx + rg + nr + T - 1) / T, a.max_blocks);
-        const int p_end = min(p_begin + a.split_pages, n_pages);
+        int p_begin, p_end;
+        split_range(a, s, gp, n_pages, p_begin, p_end);
         // q: with a 16-bit cache of the model's type, raw pairs for the packed dot products (the
         // products of two 16-bit values are exact in fp32; the scale is applied to the summed score);
         // otherwise widened and prescaled
@@ -278,7 +317,7 @@ __global__ void __launch_bounds__(NW * 64) attn_split_kernel(AttnArgs a) {
                     os += f * wst[w][i][2 + d];
                 }
             }
-            if (a.n_splits == 1) {  // the only split: the state is final
+            if (gp == 0 && a.n_splits - a.n_pre_splits == 1) {  // the row's only split: the state is final
                 store_round<DT>(a.out, (long)row * a.n_heads * DH + (long)h * DH + d, safe_div(os, ls));
             } else {
                 float* dst = a.part + (((long)row * a.n_heads + h) * a.n_splits + s) * part_stride(DH);
@@ -304,9 +343,13 @@ __global__ void __launch_bounds__(DH) attn_merge_kernel(AttnArgs a) {
     __shared__ float sm[kMaxSplits], sw[kMaxSplits];
     __shared__ float s_red[DH / 64];
     const int row = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-    const int ns = min(a.n_splits, kMaxSplits);
+    // with prefix groups, a row outside any group has no prefix splits; with one split left, the
+    // attention kernel stored its output itself
+    const int s0 = a.seq_gp && a.seq_gp[a.row_seq[row]] == 0 ? a.n_pre_splits : 0;
+    const int ns = min(a.n_splits - s0, kMaxSplits);
+    if (ns == 1) return;
     constexpr int SD = part_stride(DH);
-    const float* src = a.part + ((long)row * a.n_heads + h) * a.n_splits * SD;
+    const float* src = a.part + (((long)row * a.n_heads + h) * a.n_splits + s0) * SD;
     float mx = -INFINITY;
     for (int sp = d; sp < ns; sp += DH) {
         sm[sp] = src[(long)sp * SD];

@@ -93,6 +93,40 @@ __device__ __forceinline__ uint4 widen8(uint2 w) {
                       widen2<DT, KVT, true>(w.y));
 }
 
+// The matrix-core kernel's work list: every row group (R rows from the first row of the sequence on) of
+// every sequence of rows_lo..rows_hi rows, as (sequence, first row within it), in sequence order and within
+// a sequence last group first (a causal pass's last group reads the most pages: the longest units start
+// first); *n_items the count, at most cap (one workgroup, blocks of 1024 sequences, an exclusive scan per
+// block).
+__global__ void __launch_bounds__(1024) attn_items_kernel(const int* q_start, int B, int M, int R, int rows_lo,
+                                                          int rows_hi, int2* items, int cap, int* n_items) {
+    __shared__ int sc[1024];
+    const int tid = threadIdx.x;
+    int base = 0;
+    for (int b0 = 0; b0 < B; b0 += 1024) {
+        const int b = b0 + tid;
+        int n = 0;
+        if (b < B) {
+            const int r0 = min(max(q_start[b], 0), M);
+            const int rn = min(max(q_start[b + 1] - r0, 0), M - r0);
+            if (rn >= rows_lo && rn <= rows_hi) n = (rn + R - 1) / R;
+        }
+        sc[tid] = n;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan (Hillis-Steele)
+            const int v = tid >= off ? sc[tid - off] : 0;
+            __syncthreads();
+            sc[tid] += v;
+            __syncthreads();
+        }
+        const int at = base + sc[tid] - n;
+        for (int k = 0; k < n && at + k < cap; ++k) items[at + k] = make_int2(b, (n - 1 - k) * R);
+        base += sc[1023];
+        __syncthreads();
+    }
+    if (tid == 0) *n_items = min(base, cap);
+}
+
 // Two waves per SIMD (at most 256 registers, no scratch): with one page in flight per wave, a
 // decode step's few states leave the kernel bound by load latency, and the second resident
 // workgroup is what hides it.
@@ -103,15 +137,50 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, kq = lane >> 4;
-    const int s = blockIdx.x, h0 = blockIdx.y * HG;
-    const int b = blockIdx.z % a.B, rgb = blockIdx.z / a.B;
+    const int h0 = blockIdx.y * HG;
     const int hk = h0 / (a.n_heads / a.n_kv_heads);
-    const int r0 = min(max(a.q_start[b], 0), a.M);
-    const int Rn = min(max(a.q_start[b + 1] - r0, 0), a.M - r0);
-    if (Rn < a.rows_lo || Rn > a.rows_hi) return;  // another kernel's sequence
-    const int ctx = max(a.ctx_len[b], 0);
     const int T = a.page_tokens;
-    const int p_begin = s * a.split_pages;
+    // A group block (blockIdx.z < gz_blocks) takes R sequences of one shared-prefix group as its row
+    // slots (each one row, at its own position) and the prefix splits [0, n_pre_splits) of its prefix
+    // pages, read through the block table of the group's first sequence (every member's table holds
+    // the same prefix page ids, checked before: a member that fails the check has seq_group -1 and
+    // takes the plain path). Any other block takes row groups of one sequence, as below, and the key
+    // split n_pre_splits + blockIdx.x.
+    const bool grp = (int)blockIdx.z < a.gz_blocks;
+    int s = blockIdx.x, b, rgb, rg_step, r0, Rn, ctx, gp, gi = 0, j0 = 0, gn = 0;
+    if (grp) {
+        if (s >= a.n_pre_splits) return;
+        rg_step = R;
+        gi = blockIdx.z / a.gz_per_group;
+        j0 = (blockIdx.z % a.gz_per_group) * R;
+        gn = a.group_n[gi];
+        b = min(max(a.group_seq0[gi], 0), a.B - 1);
+        rgb = 0;
+        r0 = 0;
+        Rn = 1;  // one pass over the row slots
+        ctx = 0;
+        gp = min(max(a.group_pages[gi], 0), a.max_blocks);
+    } else {
+        s += a.n_pre_splits;
+        if (s >= a.n_splits) return;
+        const int z = blockIdx.z - a.gz_blocks;
+        if (a.items) {  // one unit of the work list
+            if (z >= *a.n_items) return;
+            const int2 it = a.items[z];
+            b = min(max(it.x, 0), a.B - 1);
+            rgb = max(it.y, 0) / R;
+            rg_step = 1 << 30;
+        } else {
+            b = z % a.B;
+            rgb = z / a.B;
+            rg_step = a.rg_blocks * R;
+        }
+        r0 = min(max(a.q_start[b], 0), a.M);
+        Rn = min(max(a.q_start[b + 1] - r0, 0), a.M - r0);
+        if (Rn < a.rows_lo || Rn > a.rows_hi) return;  // another kernel's sequence
+        gp = a.seq_gp ? a.seq_gp[b] : 0;  // a grouped sequence: its prefix splits come from the group blocks
+        ctx = max(a.ctx_len[b], 0);
+    }
     const int* bt = a.block_tables + (long)b * a.max_blocks;
     const long kofs = (long)a.layer * a.layer_elems + (long)hk * T * DH;
     const long vofs = kofs + (long)a.n_kv_heads * T * DH;
@@ -123,17 +192,43 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
     __shared__ __align__(16) uint16_t pt[kAmWaves][2][16 * kAmPLd];  // P hi / lo, [state][key]
     __shared__ __align__(16) uint16_t vt[kAmWaves][16 * kAmVLd];     // V page, [key][dim]
     __shared__ float wst[kAmWaves][16][DH + 2];                      // per-wave (m, l, o) of each state
+    __shared__ int srow[R], spos[R];  // each row slot's q / output row (-1: none) and position
 
-    for (int rg = rgb * R; rg < Rn; rg += a.rg_blocks * R) {
-        const int nr = min(R, Rn - rg);
-        const int n_pages = min((ctx + rg + nr + T - 1) / T, a.max_blocks);
-        const int p_end = min(p_begin + a.split_pages, n_pages);
+    for (int rg = rgb * R; rg < Rn; rg += rg_step) {
+        if (tid < R) {
+            int row = -1, pos = 0;
+            if (grp) {
+                const int seq = a.group_seq0[gi] + j0 + tid;
+                if (j0 + tid < gn && seq >= 0 && seq < a.B && a.seq_group[seq] == gi) {
+                    row = min(max(a.q_start[seq], 0), a.M - 1);
+                    pos = max(a.ctx_len[seq], 0);
+                }
+            } else if (rg + tid < Rn) {
+                row = r0 + rg + tid;
+                pos = ctx + rg + tid;
+            }
+            srow[tid] = row;
+            spos[tid] = pos;
+        }
+        __syncthreads();
+        int p_begin, p_end;
+        if (grp) {
+            bool any = false;
+#pragma unroll
+            for (int i = 0; i < R; ++i) any |= srow[i] >= 0;
+            p_begin = s * a.pre_split_pages;
+            p_end = any ? min(p_begin + a.pre_split_pages, gp) : p_begin;
+        } else {
+            const int nr = min(R, Rn - rg);
+            split_range(a, s, gp, min((ctx + rg + nr + T - 1) / T, a.max_blocks), p_begin, p_end);
+        }
         // q fragments (A operand of the scores): state l16, dims 8 kq + 32 step
         uint4 qf[4];
         {
             const int i = l16 / HG, j = l16 % HG;
-            const bool ok = i < nr;
-            const long qrow = (long)(r0 + rg + (ok ? i : 0)) * QLD + (long)(h0 + j) * DH + 8 * kq;
+            const int row = srow[i];
+            const bool ok = row >= 0;
+            const long qrow = (long)(ok ? row : 0) * QLD + (long)(h0 + j) * DH + 8 * kq;
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const uint4 v = *reinterpret_cast<const uint4*>(qb + qrow + 32 * st);
@@ -146,8 +241,8 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = (4 * kq + r) / HG;
-            sv[r] = i < nr;
-            qpos[r] = ctx + rg + i;
+            sv[r] = srow[i] >= 0;
+            qpos[r] = spos[i];
         }
         float m[4], l[4];
         float4_t o[8];
@@ -253,10 +348,13 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
             for (int t = 0; t < 8; ++t) wst[wave][st][2 + 16 * t + l16] = o[t][r];
         }
         __syncthreads();
+        // a row with one key split (no group, one plain split) is final here; the merge kernel skips it
+        const bool single = !grp && gp == 0 && a.n_splits - a.n_pre_splits == 1;
         // merge the waves in wave order; thread t takes (state, dim) pairs of the valid states
-        for (int idx = tid; idx < nr * HG * DH; idx += kAmWaves * 64) {
+        for (int idx = tid; idx < 16 * DH; idx += kAmWaves * 64) {
             const int st = idx / DH, d = idx % DH;
-            const int row = r0 + rg + st / HG, h = h0 + st % HG;
+            const int row = srow[st / HG], h = h0 + st % HG;
+            if (row < 0) continue;
             float mx = -INFINITY;
 #pragma unroll
             for (int w = 0; w < kAmWaves; ++w) mx = fmaxf(mx, wst[w][st][0]);
@@ -271,7 +369,7 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
                     os += f * wst[w][st][2 + d];
                 }
             }
-            if (a.n_splits == 1) {
+            if (single) {
                 store_round<DT>(a.out, (long)row * a.n_heads * DH + (long)h * DH + d, safe_div(os, ls));
             } else {
                 float* dst = a.part + (((long)row * a.n_heads + h) * a.n_splits + s) * part_stride(DH);

@@ -25,6 +25,8 @@ struct PrepArgs {
     int max_blocks, num_pages, page_tokens;
     long page_elems;
     int* error_flags;  // optional: validation bits (VS_STEP_BAD_*)
+    int* seq_group;    // optional [B]: set to -1 (no shared-prefix group), and seq_gp to 0
+    int* seq_gp;
 };
 
 // One workgroup (256 threads) per row r: its sequence and position, the rotary
@@ -54,6 +56,12 @@ __global__ void __launch_bounds__(256) prep_embed_kernel(PrepArgs p) {
                 off = (long)page * p.page_elems + (long)(pos % p.page_tokens) * p.head_dim;
         }
         p.row_kvoff[r] = off;
+    }
+    if (p.seq_group) {
+        for (long b = (long)r * blockDim.x + tid; b < p.B; b += (long)gridDim.x * blockDim.x) {
+            p.seq_group[b] = -1;
+            p.seq_gp[b] = 0;
+        }
     }
     __syncthreads();
     const int pos = s_pos;
@@ -99,6 +107,61 @@ __global__ void __launch_bounds__(256) prep_embed_kernel(PrepArgs p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) xr[e] = v[e];
     }
+}
+
+// Shared-prefix groups ([KV Cache] section 05, prefix caching): one workgroup per group admits each
+// member sequence whose block table holds the group's first sequence's prefix page ids (valid pages),
+// which brings exactly one row and whose context covers the prefix: seq_group[seq] = g (the first group
+// to claim a sequence keeps it), seq_gp[seq] = the prefix pages. A member that fails a check keeps
+// seq_group -1 and is attended over all its own pages; with error_flags, the failure sets
+// VS_STEP_BAD_BATCH (4).
+struct GroupArgs {
+    const int* group_seq0;
+    const int* group_n;
+    const int* group_pages;
+    int max_group_size, max_group_pages;
+    const int* q_start;
+    const int* ctx_len;
+    const int* block_tables;
+    int B, max_blocks, num_pages, page_tokens;
+    int* seq_group;
+    int* seq_gp;
+    int* error_flags;
+};
+
+__global__ void __launch_bounds__(256) prefix_group_kernel(GroupArgs a) {
+    const int g = blockIdx.x, tid = threadIdx.x;
+    const int seq0 = a.group_seq0[g], n = a.group_n[g], gp = a.group_pages[g];
+    __shared__ int bad[256];
+    const bool ok_group = seq0 >= 0 && n >= 1 && n <= a.max_group_size && (long)seq0 + n <= a.B && gp >= 1 &&
+                          gp <= a.max_group_pages && gp <= a.max_blocks;
+    if (!ok_group) {
+        if (tid == 0 && a.error_flags) atomicOr(a.error_flags, 4);
+        return;
+    }
+    const int* bt0 = a.block_tables + (long)seq0 * a.max_blocks;
+    int flag = 0;
+    for (int c = 0; c < n; c += 256) {
+        const int cnt = min(256, n - c);
+        bad[tid] = 0;
+        __syncthreads();
+        for (long idx = tid; idx < (long)cnt * gp; idx += 256) {
+            const int i = (int)(idx / gp), j = (int)(idx % gp);
+            const int pg = bt0[j];
+            if (pg < 0 || pg >= a.num_pages || a.block_tables[(long)(seq0 + c + i) * a.max_blocks + j] != pg) bad[i] = 1;
+        }
+        __syncthreads();
+        if (tid < cnt) {
+            const int seq = seq0 + c + tid;
+            bool ok = !bad[tid] && a.q_start[seq + 1] - a.q_start[seq] == 1 &&
+                      (long)a.ctx_len[seq] >= (long)a.page_tokens * gp;
+            if (ok) ok = atomicCAS(&a.seq_group[seq], -1, g) == -1;
+            if (ok) a.seq_gp[seq] = gp;
+            else flag = 4;
+        }
+        __syncthreads();
+    }
+    if (flag && a.error_flags) atomicOr(a.error_flags, flag);
 }
 
 // y[r] = round(x[src] / sqrt(mean(x[src]^2) + eps) * gain), src = map ? map[r] : r

@@ -89,6 +89,43 @@ void launchn(int kind, void (*kern)(P...), dim3 grid, dim3 block, size_t lds, hi
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// A second stream per device (default priority) for attention work beside the caller's stream: the
+// one-row sequences' VALU kernel beside the matrix-core kernel, forked from and joined back into the
+// caller's stream by events. It is made on the first step on the device whose stream is not under
+// graph capture (until then the two kernels run one after the other). The fork / join sequence of one
+// step holds the device's lock, so steps on several host threads never wait on each other's events.
+constexpr int kMaxAuxDevices = 64;
+struct AuxStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    std::mutex mu;
+};
+AuxStream g_aux[kMaxAuxDevices];
+std::mutex g_aux_make;
+
+AuxStream* aux_stream(hipStream_t s) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxAuxDevices) return nullptr;
+    AuxStream& a = g_aux[dev];
+    std::lock_guard<std::mutex> lk(g_aux_make);
+    if (a.s) return &a;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+        if (f) (void)hipEventDestroy(f);
+        (void)hipStreamDestroy(st);
+        return nullptr;
+    }
+    a.fork = f;
+    a.join = j;
+    a.s = st;
+    return &a;
+}
+
 // The chip: 256 CUs of 160 KB LDS (MI355X).
 constexpr int kNumCUs = 256;
 constexpr int kLdsPerCu = 160 * 1024;
@@ -159,6 +196,14 @@ struct Plan {
     bool attn_mfma;  // matrix-core attention: up to 16 (row, head) states per workgroup
     bool attn_mixed;  // matrix-core attention for sequences of 2+ rows, the VALU kernel for one-row ones
     int attn_hg1;     // head group of the VALU kernel's one-row sequences
+    // shared-prefix groups: the matrix-core kernel's group blocks (head groups of grp_hg heads) take each
+    // group's prefix pages once, over the first n_pre_splits key splits
+    bool groups;
+    int grp_hg, n_pre_splits, pre_split_pages, gz_per_group, gz_blocks;
+    // the matrix-core kernel's blocks go by a work list of (sequence, row group) units when the plain
+    // grid (every sequence x rg_blocks) would be mostly empty: a prompt chunk beside many decode rows
+    bool attn_items;
+    int items_cap;
     bool ksplit;  // residual products through the split-K tile GEMM
     bool ksplit_qkv, ksplit_gu;  // the q/k/v and gate/up products too (their epilogues after the sums)
     bool ksplit_lm;              // the LM head too (logits and argmax partials after the sums)
@@ -171,6 +216,8 @@ struct Plan {
     bool gemv;      // the row-streaming path serves every product of the step
     bool merge_in_o; // the output product's prologue merges the key splits (no merge kernel)
     int n_lm_parts; // argmax partials per logit row
+    size_t off_grp;  // seq_group[B], seq_gp[B]
+    size_t off_items, off_n_items;
     size_t off_row_seq, off_row_pos, off_kvoff, off_rope, off_x, off_xn, off_q, off_attn, off_h, off_part, off_xf, off_lmpart,
         off_ksp;
     size_t total;
@@ -263,10 +310,30 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
             p->attn_waves = kAmWaves;
         }
     }
+    // shared-prefix groups: used for fp16 / bf16 models with head_dim 128 (the matrix-core kernel's group
+    // blocks), ignored otherwise
+    if (d->n_prefix_groups < 0) return vs_fail(VS_ERR_INVALID, "n_prefix_groups must be >= 0");
+    p->groups = d->n_prefix_groups > 0 && m->dtype != VS_F32 && m->head_dim == kAmDh && d->M > 0;
+    p->grp_hg = 1;
+    p->n_pre_splits = p->pre_split_pages = p->gz_per_group = p->gz_blocks = 0;
+    if (p->groups) {
+        if (!d->group_seq0 || !d->group_n || !d->group_pages || d->max_group_size < 1 || d->max_group_pages < 1 ||
+            d->n_prefix_groups > d->B || d->max_group_size > d->B || d->max_group_pages > d->max_blocks)
+            return vs_fail(VS_ERR_INVALID,
+                           "prefix groups need device arrays, 1 <= n_prefix_groups <= B, 1 <= max_group_size <= B, "
+                           "1 <= max_group_pages <= max_blocks");
+        const int group = m->n_heads / m->n_kv_heads;
+        while (p->grp_hg < 16 && group % (2 * p->grp_hg) == 0) p->grp_hg *= 2;
+        const int per_block = 16 / p->grp_hg;  // sequences per group block
+        p->gz_per_group = (d->max_group_size + per_block - 1) / per_block;
+        const long gz = (long)d->n_prefix_groups * p->gz_per_group;
+        if (gz + d->B > 65535) return vs_fail(VS_ERR_INVALID, "too many prefix-group blocks (groups x ceil(max_group_size / 16 x HG) + B > 65535)");
+        p->gz_blocks = (int)gz;
+    }
     const int max_pages = (d->max_ctx + kPageTokens - 1) / kPageTokens;
     // row groups of a sequence go to separate workgroups (a prompt chunk's groups run in parallel)
     const int rg_needed = (d->max_rows + p->rmax - 1) / p->rmax;
-    p->rg_blocks = (int)std::max<long>(1, std::min<long>(rg_needed, 65535L / d->B));
+    p->rg_blocks = (int)std::max<long>(1, std::min<long>(rg_needed, (65535L - p->gz_blocks) / d->B));
     const long pairs = (long)d->B * (m->n_heads / p->attn_hg) * p->rg_blocks;  // workgroups per split
     const long wgs_target = p->attn_mfma          ? kAttnTargetWgsMfma
                             : p->attn_waves == 8 ? kAttnTargetWaves / 8
@@ -275,10 +342,31 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
                                        std::max<long>(1, (wgs_target + pairs - 1) / pairs));
     p->split_pages = (max_pages + ns - 1) / ns;
     p->n_splits = (max_pages + p->split_pages - 1) / p->split_pages;
+    if (p->groups) {
+        // the prefix splits, ahead of the others: about one workgroup per CU over the group blocks, at
+        // least two pages per wave
+        const long gwgs = (long)p->gz_blocks * (m->n_heads / p->grp_hg);
+        p->n_pre_splits = (int)std::min<long>(std::max(1, d->max_group_pages / (2 * kAmWaves)),
+                                              std::max<long>(1, (kAttnTargetWgsMfma + gwgs - 1) / gwgs));
+        p->pre_split_pages = (d->max_group_pages + p->n_pre_splits - 1) / p->n_pre_splits;
+        p->n_splits += p->n_pre_splits;
+    }
+    p->attn_items = false;
+    p->items_cap = 0;
+    if (p->attn_mfma) {
+        // units: at most ceil(rows / R) per sequence of rows_lo+ rows
+        const int R = 16 / p->attn_hg, lo = p->attn_mixed ? 2 : 1;
+        const long nq = std::min<long>(d->B, std::max(d->M, 1) / lo);
+        const long cap = ((long)d->M + (R - 1) * nq + R - 1) / R;
+        if ((long)d->B * p->rg_blocks > 2 * cap && cap <= 65535L - p->gz_blocks) {
+            p->attn_items = true;
+            p->items_cap = (int)std::max<long>(cap, 1);
+        }
+    }
     // the row-streaming GEMV serves steps of up to kGemvMaxRows rows (beyond, the products' VALU work
     // outgrows the weight stream); RMSNorm-input products stage all of X, plain-input ones may phase it
     p->gemv = d->M <= kGemvMaxRows && (size_t)std::max(d->M, 1) * p->D * p->esz <= kGemvMaxLds;
-    p->merge_in_o = p->gemv && p->n_splits > 1 && p->n_splits <= kMergeMaxSplits;
+    p->merge_in_o = p->gemv && p->n_splits > 1 && p->n_splits <= kMergeMaxSplits && !p->groups;
     p->n_lm_parts = p->gemv ? (p->V + gemv_units_per_wg(p->V) - 1) / gemv_units_per_wg(p->V) : (p->V + 15) / 16;
     // 17..64 rows in fp16 / bf16: the weight products split K over workgroups, the X slice staged
     // once per workgroup in LDS (up to 16 rows the 16-feature tiles read no more activation bytes
@@ -350,6 +438,9 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
         o = align256(o + std::max<size_t>(bytes, 4));
         return at;
     };
+    p->off_grp = take(p->groups ? 2 * (size_t)d->B * 4 : 4);
+    p->off_items = take((size_t)std::max(p->items_cap, 1) * 8);
+    p->off_n_items = take(4);
     p->off_row_seq = take(M * 4);
     p->off_row_pos = take(M * 4);
     p->off_kvoff = take(M * 8);
@@ -554,7 +645,7 @@ void launch_gemv(int kind, GemvArgs g, hipStream_t s, int units_per_wg = 0) {
 // needs none; the output GEMV can merge them in its prologue).
 template <int DT, int DH, int KVT>
 void launch_attention_kv(const AttnArgs& a, int B, int M, int rmax, int hg, bool merge_kernel, hipStream_t s) {
-    dim3 grid(a.n_splits, a.n_heads / hg, B * a.rg_blocks);
+    dim3 grid(a.n_splits - a.n_pre_splits, a.n_heads / hg, B * a.rg_blocks);
     const int nw = attn_waves(rmax * hg, DT);
     dim3 block(nw * 64);
     auto go = [&](auto kern) { launch1(VS_KERNEL_ATTN, kern, grid, block, 0, s, a); };
@@ -580,10 +671,13 @@ void launch_attention_kv(const AttnArgs& a, int B, int M, int rmax, int hg, bool
 
 // The cache's storage type picks the K/V loads: the model's type, or (fp16 / bf16 models with
 // head_dim 128) an 8-bit float.
-// Matrix-core attention: grid (splits, head groups of HG, sequences x row-group blocks).
+// Matrix-core attention: grid (splits, head groups of HG, prefix-group blocks + plain blocks); z_seq = 0
+// launches the group blocks alone.
 template <int DT, int KVT>
-void launch_attention_mfma(const AttnArgs& a, int B, int hg, hipStream_t s) {
-    const dim3 grid(a.n_splits, a.n_heads / hg, B * a.rg_blocks), block(kAmWaves * 64);
+void launch_attention_mfma(const AttnArgs& a, int z_seq, int hg, hipStream_t s) {
+    const int ss = a.n_splits - a.n_pre_splits;
+    const int nx = z_seq == 0 ? a.n_pre_splits : a.gz_blocks > 0 ? std::max(a.n_pre_splits, ss) : ss;
+    const dim3 grid(nx, a.n_heads / hg, a.gz_blocks + z_seq), block(kAmWaves * 64);
     switch (hg) {
         case 1: launch1(VS_KERNEL_ATTN, attn_mfma_kernel<DT, 1, KVT>, grid, block, 0, s, a); break;
         case 2: launch1(VS_KERNEL_ATTN, attn_mfma_kernel<DT, 2, KVT>, grid, block, 0, s, a); break;
@@ -593,34 +687,61 @@ void launch_attention_mfma(const AttnArgs& a, int B, int hg, hipStream_t s) {
     }
 }
 
+// The attention kernels of one layer; two of them (the matrix-core kernel and the VALU kernel of the
+// one-row sequences, or the group blocks and the VALU kernel) take disjoint rows and key splits, so with
+// a second stream the second runs beside the first.
+template <int DT, int KVT>
+void launch_attention_kvt(const AttnArgs& a, const Plan& p, hipStream_t s, AuxStream* aux) {
+    constexpr int DH = kAmDh;
+    const bool two = p.attn_mfma ? p.attn_mixed : p.groups;
+    std::unique_lock<std::mutex> lk;
+    hipStream_t s2 = s;
+    if (two && aux) {
+        lk = std::unique_lock<std::mutex>(aux->mu);
+        (void)hipEventRecord(aux->fork, s);
+        (void)hipStreamWaitEvent(aux->s, aux->fork, 0);
+        s2 = aux->s;
+    }
+    if (p.attn_mfma) {
+        if (p.attn_mixed) {  // the one-row sequences: one-row groups of the VALU kernel, same splits
+            AttnArgs av = a;
+            av.rows_hi = 1;
+            av.rg_blocks = 1;
+            av.items = nullptr;
+            launch_attention_kv<DT, DH, KVT>(av, p.B, p.M, 1, p.attn_hg1, false, s2);
+        }
+        // the matrix cores take the prefix-group blocks and the sequences of 2+ rows (all, unless mixed)
+        AttnArgs am = a;
+        if (p.attn_mixed) am.rows_lo = 2;
+        launch_attention_mfma<DT, KVT>(am, p.attn_items ? p.items_cap : p.B * p.rg_blocks, p.attn_hg, s);
+    } else {
+        if (p.groups) launch_attention_mfma<DT, KVT>(a, 0, p.grp_hg, s2);  // the group blocks alone
+        launch_attention_kv<DT, DH, KVT>(a, p.B, p.M, p.rmax, p.attn_hg, false, s);
+    }
+    if (s2 != s) {
+        (void)hipEventRecord(aux->join, s2);
+        (void)hipStreamWaitEvent(s, aux->join, 0);
+    }
+}
+
 template <int DT, int DH>
-void launch_attention(const AttnArgs& a, int B, int M, int rmax, int hg, int kv_dt, bool merge_kernel, bool mfma,
-                      hipStream_t s, bool mixed = false, int hg1 = 1) {
+void launch_attention(const AttnArgs& a, const Plan& p, int kv_dt, hipStream_t s, AuxStream* aux) {
+    const bool merge_kernel = !p.merge_in_o;
     if constexpr (DT != F32 && DH == kAmDh) {
-        if (mfma) {
-            AttnArgs am = a;
-            if (mixed) am.rows_lo = 2;
-            if (kv_dt == E4M3) launch_attention_mfma<DT, E4M3>(am, B, hg, s);
-            else if (kv_dt == E5M2) launch_attention_mfma<DT, E5M2>(am, B, hg, s);
-            else launch_attention_mfma<DT, DT>(am, B, hg, s);
-            if (mixed) {  // the one-row sequences: one-row groups of the VALU kernel, same splits
-                AttnArgs av = a;
-                av.rows_hi = 1;
-                av.rg_blocks = 1;
-                if (kv_dt == E4M3) launch_attention_kv<DT, DH, E4M3>(av, B, M, 1, hg1, false, s);
-                else if (kv_dt == E5M2) launch_attention_kv<DT, DH, E5M2>(av, B, M, 1, hg1, false, s);
-                else launch_attention_kv<DT, DH, DT>(av, B, M, 1, hg1, false, s);
-            }
+        if (p.attn_mfma || p.groups) {
+            if (kv_dt == E4M3) launch_attention_kvt<DT, E4M3>(a, p, s, aux);
+            else if (kv_dt == E5M2) launch_attention_kvt<DT, E5M2>(a, p, s, aux);
+            else launch_attention_kvt<DT, DT>(a, p, s, aux);
             if (merge_kernel && a.n_splits > 1)
-                launch1(VS_KERNEL_MERGE, attn_merge_kernel<DT, DH>, dim3(M, a.n_heads), dim3(DH), 0, s, a);
+                launch1(VS_KERNEL_MERGE, attn_merge_kernel<DT, DH>, dim3(p.M, a.n_heads), dim3(DH), 0, s, a);
             return;
         }
     }
     if constexpr (DT != F32 && DH == 128) {
-        if (kv_dt == E4M3) return launch_attention_kv<DT, DH, E4M3>(a, B, M, rmax, hg, merge_kernel, s);
-        if (kv_dt == E5M2) return launch_attention_kv<DT, DH, E5M2>(a, B, M, rmax, hg, merge_kernel, s);
+        if (kv_dt == E4M3) return launch_attention_kv<DT, DH, E4M3>(a, p.B, p.M, p.rmax, p.attn_hg, merge_kernel, s);
+        if (kv_dt == E5M2) return launch_attention_kv<DT, DH, E5M2>(a, p.B, p.M, p.rmax, p.attn_hg, merge_kernel, s);
     }
-    launch_attention_kv<DT, DH, DT>(a, B, M, rmax, hg, merge_kernel, s);
+    launch_attention_kv<DT, DH, DT>(a, p.B, p.M, p.rmax, p.attn_hg, merge_kernel, s);
 }
 
 // Common epilogue fields of both product paths.
@@ -646,7 +767,7 @@ void fill_epilogue(A& g, const Plan& p, const vs_batch_desc* d, const int32_t* b
 
 template <int DT>
 vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, const vs_weights* w,
-                   const vs_step_out* out, char* ws, hipStream_t s) {
+                   const vs_step_out* out, char* ws, hipStream_t s, bool allow_aux) {
     const vs_pool_desc* pg = vs_pool_geometry(d->pool);
     int* row_seq = reinterpret_cast<int*>(ws + p.off_row_seq);
     int* row_pos = reinterpret_cast<int*>(ws + p.off_row_pos);
@@ -685,7 +806,30 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     pa.page_tokens = kPageTokens;
     pa.page_elems = (long)(kv_page_bytes(pg) / kv_elem_bytes(pg->dtype));
     pa.error_flags = d->error_flags;
+    int* seq_group = reinterpret_cast<int*>(ws + p.off_grp);
+    int* seq_gp = seq_group + p.B;
+    pa.seq_group = p.groups ? seq_group : nullptr;
+    pa.seq_gp = p.groups ? seq_gp : nullptr;
     hipLaunchKernelGGL((prep_embed_kernel<DT>), dim3(p.M), dim3(256), 0, s, pa);
+    if (p.groups) {
+        GroupArgs ga;
+        ga.group_seq0 = d->group_seq0;
+        ga.group_n = d->group_n;
+        ga.group_pages = d->group_pages;
+        ga.max_group_size = d->max_group_size;
+        ga.max_group_pages = d->max_group_pages;
+        ga.q_start = d->q_start;
+        ga.ctx_len = d->ctx_len;
+        ga.block_tables = bt;
+        ga.B = p.B;
+        ga.max_blocks = d->max_blocks;
+        ga.num_pages = pg->num_pages;
+        ga.page_tokens = kPageTokens;
+        ga.seq_group = seq_group;
+        ga.seq_gp = seq_gp;
+        ga.error_flags = d->error_flags;
+        hipLaunchKernelGGL(prefix_group_kernel, dim3(d->n_prefix_groups), dim3(256), 0, s, ga);
+    }
 
     GemvArgs gv = {};
     fill_epilogue(gv, p, d, bt, pg, row_seq, row_pos, rope_cs, row_kvoff);
@@ -720,6 +864,26 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.Dh));
     a.part = part;
     a.out = attn;
+    a.row_seq = row_seq;
+    AuxStream* aux = allow_aux && ((p.attn_mfma && p.attn_mixed) || p.groups) ? aux_stream(s) : nullptr;
+    if (p.attn_items) {
+        a.items = reinterpret_cast<int2*>(ws + p.off_items);
+        a.n_items = reinterpret_cast<int*>(ws + p.off_n_items);
+        hipLaunchKernelGGL(attn_items_kernel, dim3(1), dim3(1024), 0, s, d->q_start, p.B, p.M, 16 / p.attn_hg,
+                           p.attn_mixed ? 2 : 0, 0x7fffffff, reinterpret_cast<int2*>(ws + p.off_items), p.items_cap,
+                           reinterpret_cast<int*>(ws + p.off_n_items));
+    }
+    if (p.groups) {
+        a.seq_gp = seq_gp;
+        a.seq_group = seq_group;
+        a.group_seq0 = d->group_seq0;
+        a.group_n = d->group_n;
+        a.group_pages = d->group_pages;
+        a.n_pre_splits = p.n_pre_splits;
+        a.pre_split_pages = p.pre_split_pages;
+        a.gz_blocks = p.gz_blocks;
+        a.gz_per_group = p.gz_per_group;
+    }
 
     // the split-K residual products hand the next RMSNorm's output over in xn (fused into their
     // partial-sum reduction): the norm ahead of the next product is then already done
@@ -775,11 +939,8 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
         }
 
         a.layer = l;
-        if (p.Dh == 128)
-            launch_attention<DT, 128>(a, p.B, p.M, p.rmax, p.attn_hg, pg->dtype, !p.merge_in_o, p.attn_mfma, s,
-                                      p.attn_mixed, p.attn_hg1);
-        else
-            launch_attention<DT, 64>(a, p.B, p.M, p.rmax, p.attn_hg, pg->dtype, !p.merge_in_o, p.attn_mfma, s);
+        if (p.Dh == 128) launch_attention<DT, 128>(a, p, pg->dtype, s, aux);
+        else launch_attention<DT, 64>(a, p, pg->dtype, s, aux);
 
         // x += W_o attn
         if (p.gemv) {
@@ -1000,12 +1161,14 @@ vs_status check_step(const vs_batch_desc* desc, const int32_t* block_tables, con
     return vs_ok();
 }
 
+// allow_aux: the step may make and use the device's second stream (the allocation-free entry point
+// keeps to the caller's stream)
 vs_status run_checked(const Plan& p, const vs_batch_desc* desc, const int32_t* block_tables,
-                      const vs_weights* weights, const vs_step_out* out, char* w, hipStream_t stream) {
+                      const vs_weights* weights, const vs_step_out* out, char* w, hipStream_t stream, bool allow_aux) {
     switch (p.dt) {
-        case VS_F32: return run_step<F32>(p, desc, block_tables, weights, out, w, stream);
-        case VS_F16: return run_step<F16>(p, desc, block_tables, weights, out, w, stream);
-        default: return run_step<BF16>(p, desc, block_tables, weights, out, w, stream);
+        case VS_F32: return run_step<F32>(p, desc, block_tables, weights, out, w, stream, allow_aux);
+        case VS_F16: return run_step<F16>(p, desc, block_tables, weights, out, w, stream, allow_aux);
+        default: return run_step<BF16>(p, desc, block_tables, weights, out, w, stream, allow_aux);
     }
 }
 
@@ -1018,7 +1181,7 @@ extern "C" vs_status decode_step(const vs_batch_desc* desc, const int32_t* block
     if (st != VS_OK || p.M == 0) return st;
     if (!ws || ws_bytes < p.total)
         return vs_fail(VS_ERR_SHAPE, "decode_step: workspace needs " + std::to_string(p.total) + " bytes");
-    return run_checked(p, desc, block_tables, weights, out, static_cast<char*>(ws), stream);
+    return run_checked(p, desc, block_tables, weights, out, static_cast<char*>(ws), stream, true);
 }
 
 // ---- the allocation-free variant: the workspace is a device array of the library itself -------
@@ -1064,7 +1227,7 @@ extern "C" vs_status decode_step_noalloc(const vs_batch_desc* desc, const int32_
     void* ws = nullptr;
     st = scratch_for_current_device(&ws);
     if (st != VS_OK) return st;
-    return run_checked(p, desc, block_tables, weights, out, static_cast<char*>(ws), stream);
+    return run_checked(p, desc, block_tables, weights, out, static_cast<char*>(ws), stream, false);
 }
 
 extern "C" vs_status verify_accept(int32_t B, const int32_t* q_start, const int32_t* drafts, const int32_t* g0,
