@@ -196,6 +196,7 @@ struct Plan {
     bool attn_mfma;  // matrix-core attention: up to 16 (row, head) states per workgroup
     bool attn_mixed;  // matrix-core attention for sequences of 2+ rows, the VALU kernel for one-row ones
     int attn_hg1;     // head group of the VALU kernel's one-row sequences
+    int attn_nw1;     // waves per VALU workgroup of one (row, head) state: 4 or 8
     // shared-prefix groups: the matrix-core kernel's group blocks (head groups of grp_hg heads) take each
     // group's prefix pages once, over the first n_pre_splits key splits
     bool groups;
@@ -351,6 +352,13 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
         p->pre_split_pages = (d->max_group_pages + p->n_pre_splits - 1) / p->n_pre_splits;
         p->n_splits += p->n_pre_splits;
     }
+    // one-state VALU workgroups (decode rows, one head each): four waves, each with twice the pages,
+    // when the launch has no more workgroups than CUs or its sequences are grouped (few own pages
+    // after the prefix); eight otherwise. Measured (7B): batch 1 at context 2048, 2.869 -> 2.846 ms per
+    // step; batch 8, contexts 128..4096, 4.364 -> 4.309; 64 decode rows on shared prefixes + a 512-row
+    // chunk, 17.06 -> 16.64; batch 64 (2048 workgroups of about 130 pages) 14.13 with eight waves
+    // against 14.61 with four.
+    p->attn_nw1 = (long)d->B * m->n_heads * (p->n_splits - p->n_pre_splits) <= kNumCUs || p->groups ? 4 : 8;
     p->attn_items = false;
     p->items_cap = 0;
     if (p->attn_mfma) {
@@ -644,13 +652,16 @@ void launch_gemv(int kind, GemvArgs g, hipStream_t s, int units_per_wg = 0) {
 // The split pass, then the merge kernel unless the splits are merged elsewhere (one split
 // needs none; the output GEMV can merge them in its prologue).
 template <int DT, int DH, int KVT>
-void launch_attention_kv(const AttnArgs& a, int B, int M, int rmax, int hg, bool merge_kernel, hipStream_t s) {
+void launch_attention_kv(const AttnArgs& a, int B, int M, int rmax, int hg, bool merge_kernel, hipStream_t s, int nw1) {
     dim3 grid(a.n_splits - a.n_pre_splits, a.n_heads / hg, B * a.rg_blocks);
-    const int nw = attn_waves(rmax * hg, DT);
+    const int nw = rmax * hg == 1 ? nw1 : attn_waves(rmax * hg, DT);
     dim3 block(nw * 64);
     auto go = [&](auto kern) { launch1(VS_KERNEL_ATTN, kern, grid, block, 0, s, a); };
     switch (hg * 16 + rmax) {
-        case 16 + 1: go(attn_split_kernel<DT, DH, 1, 8, 1, KVT>); break;
+        case 16 + 1:
+            if (nw == 4) go(attn_split_kernel<DT, DH, 1, 4, 1, KVT>);
+            else go(attn_split_kernel<DT, DH, 1, 8, 1, KVT>);
+            break;
         case 16 + 2:
             if (nw == 8) go(attn_split_kernel<DT, DH, 2, DT == F32 ? 4 : 8, 1, KVT>);
             else go(attn_split_kernel<DT, DH, 2, 4, 1, KVT>);
@@ -708,7 +719,7 @@ void launch_attention_kvt(const AttnArgs& a, const Plan& p, hipStream_t s, AuxSt
             av.rows_hi = 1;
             av.rg_blocks = 1;
             av.items = nullptr;
-            launch_attention_kv<DT, DH, KVT>(av, p.B, p.M, 1, p.attn_hg1, false, s2);
+            launch_attention_kv<DT, DH, KVT>(av, p.B, p.M, 1, p.attn_hg1, false, s2, p.attn_nw1);
         }
         // the matrix cores take the prefix-group blocks and the sequences of 2+ rows (all, unless mixed)
         AttnArgs am = a;
@@ -716,7 +727,7 @@ void launch_attention_kvt(const AttnArgs& a, const Plan& p, hipStream_t s, AuxSt
         launch_attention_mfma<DT, KVT>(am, p.attn_items ? p.items_cap : p.B * p.rg_blocks, p.attn_hg, s);
     } else {
         if (p.groups) launch_attention_mfma<DT, KVT>(a, 0, p.grp_hg, s2);  // the group blocks alone
-        launch_attention_kv<DT, DH, KVT>(a, p.B, p.M, p.rmax, p.attn_hg, false, s);
+        launch_attention_kv<DT, DH, KVT>(a, p.B, p.M, p.rmax, p.attn_hg, false, s, p.attn_nw1);
     }
     if (s2 != s) {
         (void)hipEventRecord(aux->join, s2);
@@ -738,10 +749,12 @@ void launch_attention(const AttnArgs& a, const Plan& p, int kv_dt, hipStream_t s
         }
     }
     if constexpr (DT != F32 && DH == 128) {
-        if (kv_dt == E4M3) return launch_attention_kv<DT, DH, E4M3>(a, p.B, p.M, p.rmax, p.attn_hg, merge_kernel, s);
-        if (kv_dt == E5M2) return launch_attention_kv<DT, DH, E5M2>(a, p.B, p.M, p.rmax, p.attn_hg, merge_kernel, s);
+        if (kv_dt == E4M3)
+            return launch_attention_kv<DT, DH, E4M3>(a, p.B, p.M, p.rmax, p.attn_hg, merge_kernel, s, p.attn_nw1);
+        if (kv_dt == E5M2)
+            return launch_attention_kv<DT, DH, E5M2>(a, p.B, p.M, p.rmax, p.attn_hg, merge_kernel, s, p.attn_nw1);
     }
-    launch_attention_kv<DT, DH, DT>(a, p.B, p.M, p.rmax, p.attn_hg, merge_kernel, s);
+    launch_attention_kv<DT, DH, DT>(a, p.B, p.M, p.rmax, p.attn_hg, merge_kernel, s, p.attn_nw1);
 }
 
 // Common epilogue fields of both product paths.
