@@ -70,8 +70,9 @@ struct AttnArgs {
     const int* group_n;      // [n_groups] sequences in each group
     const int* group_pages;  // [n_groups] prefix pages of each group
     int n_pre_splits, pre_split_pages;
-    int gz_blocks;     // the matrix-core kernel's grid z blocks [0, gz_blocks) are group blocks
-    int gz_per_group;  // group blocks per group (16 / HG sequences each)
+    int gz_blocks;     // the matrix-core kernel's grid z blocks [0, gz_blocks) are group blocks: (block of
+                       // 16 / HG sequences of a group) x n_pre_splits + prefix split
+    int gz_per_group;  // blocks of 16 / HG sequences per group
     const int* row_seq;  // [M] each row's sequence (read by the merge kernel with groups)
     // The matrix-core kernel's work list (nullptr: none): its plain block z - gz_blocks takes the unit
     // items[z - gz_blocks] = (sequence, first row of the row group) if below *n_items, else nothing;

@@ -141,18 +141,20 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
     const int hk = h0 / (a.n_heads / a.n_kv_heads);
     const int T = a.page_tokens;
     // A group block (blockIdx.z < gz_blocks) takes R sequences of one shared-prefix group as its row
-    // slots (each one row, at its own position) and the prefix splits [0, n_pre_splits) of its prefix
-    // pages, read through the block table of the group's first sequence (every member's table holds
+    // slots (each one row, at its own position) and one of the prefix splits [0, n_pre_splits) of its
+    // prefix pages, read through the block table of the group's first sequence (every member's table holds
     // the same prefix page ids, checked before: a member that fails the check has seq_group -1 and
     // takes the plain path). Any other block takes row groups of one sequence, as below, and the key
     // split n_pre_splits + blockIdx.x.
     const bool grp = (int)blockIdx.z < a.gz_blocks;
     int s = blockIdx.x, b, rgb, rg_step, r0, Rn, ctx, gp, gi = 0, j0 = 0, gn = 0;
-    if (grp) {
-        if (s >= a.n_pre_splits) return;
+    if (grp) {  // z = (group block) x n_pre_splits + prefix split; blocks past x = 0 are not needed
+        if (s > 0) return;
+        s = blockIdx.z % a.n_pre_splits;
+        const int gz = blockIdx.z / a.n_pre_splits;
         rg_step = R;
-        gi = blockIdx.z / a.gz_per_group;
-        j0 = (blockIdx.z % a.gz_per_group) * R;
+        gi = gz / a.gz_per_group;
+        j0 = (gz % a.gz_per_group) * R;
         gn = a.group_n[gi];
         b = min(max(a.group_seq0[gi], 0), a.B - 1);
         rgb = 0;
