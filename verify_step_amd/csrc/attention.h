@@ -74,6 +74,10 @@ struct AttnArgs {
                        // 16 / HG sequences of a group) x n_pre_splits + prefix split
     int gz_per_group;  // blocks of 16 / HG sequences per group
     const int* row_seq;  // [M] each row's sequence (read by the merge kernel with groups)
+    // The merge kernel's rows: merge_rows[0 .. *merge_count) (the grouped rows, when every other row
+    // has a single split and was stored by the attention kernel), or nullptr: block x is row x.
+    const int* merge_rows;
+    const int* merge_count;
     // The matrix-core kernel's work list (nullptr: none): its plain block z - gz_blocks takes the unit
     // items[z - gz_blocks] = (sequence, first row of the row group) if below *n_items, else nothing;
     // without a list it takes sequence z % B and every rg_blocks-th row group from z / B on.
@@ -343,7 +347,12 @@ __global__ void __launch_bounds__(DH) attn_merge_kernel(AttnArgs a) {
     constexpr int kMaxSplits = 1024;
     __shared__ float sm[kMaxSplits], sw[kMaxSplits];
     __shared__ float s_red[DH / 64];
-    const int row = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    int row = blockIdx.x;
+    if (a.merge_rows) {
+        if (row >= *a.merge_count) return;
+        row = a.merge_rows[row];
+    }
+    const int h = blockIdx.y, d = threadIdx.x;
     // with prefix groups, a row outside any group has no prefix splits; with one split left, the
     // attention kernel stored its output itself
     const int s0 = a.seq_gp && a.seq_gp[a.row_seq[row]] == 0 ? a.n_pre_splits : 0;

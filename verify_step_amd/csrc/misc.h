@@ -27,6 +27,7 @@ struct PrepArgs {
     int* error_flags;  // optional: validation bits (VS_STEP_BAD_*)
     int* seq_group;    // optional [B]: set to -1 (no shared-prefix group), and seq_gp to 0
     int* seq_gp;
+    int* merge_count;  // optional: set to 0 (the rows the group check lists for the merge kernel)
 };
 
 // One workgroup (256 threads) per row r: its sequence and position, the rotary
@@ -62,6 +63,7 @@ __global__ void __launch_bounds__(256) prep_embed_kernel(PrepArgs p) {
             p.seq_group[b] = -1;
             p.seq_gp[b] = 0;
         }
+        if (r == 0 && tid == 0) *p.merge_count = 0;
     }
     __syncthreads();
     const int pos = s_pos;
@@ -112,9 +114,10 @@ __global__ void __launch_bounds__(256) prep_embed_kernel(PrepArgs p) {
 // Shared-prefix groups ([KV Cache] section 05, prefix caching): one workgroup per group admits each
 // member sequence whose block table holds the group's first sequence's prefix page ids (valid pages),
 // which brings exactly one row and whose context covers the prefix: seq_group[seq] = g (the first group
-// to claim a sequence keeps it), seq_gp[seq] = the prefix pages. A member that fails a check keeps
-// seq_group -1 and is attended over all its own pages; with error_flags, the failure sets
-// VS_STEP_BAD_BATCH (4).
+// to claim a sequence keeps it), seq_gp[seq] = the prefix pages, and its row goes on the list of rows
+// the merge kernel combines (merge_rows, *merge_count, in no fixed order; each row's merge is the same
+// wherever it sits). A member that fails a check keeps seq_group -1 and is attended over all its own
+// pages; with error_flags, the failure sets VS_STEP_BAD_BATCH (4).
 struct GroupArgs {
     const int* group_seq0;
     const int* group_n;
@@ -126,6 +129,9 @@ struct GroupArgs {
     int B, max_blocks, num_pages, page_tokens;
     int* seq_group;
     int* seq_gp;
+    int* merge_rows;   // [B]
+    int* merge_count;
+    int M;
     int* error_flags;
 };
 
@@ -156,8 +162,12 @@ __global__ void __launch_bounds__(256) prefix_group_kernel(GroupArgs a) {
             bool ok = !bad[tid] && a.q_start[seq + 1] - a.q_start[seq] == 1 &&
                       (long)a.ctx_len[seq] >= (long)a.page_tokens * gp;
             if (ok) ok = atomicCAS(&a.seq_group[seq], -1, g) == -1;
-            if (ok) a.seq_gp[seq] = gp;
-            else flag = 4;
+            if (ok) {
+                a.seq_gp[seq] = gp;
+                a.merge_rows[atomicAdd(a.merge_count, 1)] = min(max(a.q_start[seq], 0), a.M - 1);
+            } else {
+                flag = 4;
+            }
         }
         __syncthreads();
     }

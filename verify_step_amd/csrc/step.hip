@@ -217,7 +217,7 @@ struct Plan {
     bool gemv;      // the row-streaming path serves every product of the step
     bool merge_in_o; // the output product's prologue merges the key splits (no merge kernel)
     int n_lm_parts; // argmax partials per logit row
-    size_t off_grp;  // seq_group[B], seq_gp[B]
+    size_t off_grp;  // seq_group[B], seq_gp[B], merge_rows[B], merge_count
     size_t off_items, off_n_items;
     size_t off_row_seq, off_row_pos, off_kvoff, off_rope, off_x, off_xn, off_q, off_attn, off_h, off_part, off_xf, off_lmpart,
         off_ksp;
@@ -451,7 +451,7 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
         o = align256(o + std::max<size_t>(bytes, 4));
         return at;
     };
-    p->off_grp = take(p->groups ? 2 * (size_t)d->B * 4 : 4);
+    p->off_grp = take(p->groups ? (3 * (size_t)d->B + 1) * 4 : 4);  // seq_group, seq_gp, merge_rows, count
     p->off_items = take((size_t)std::max(p->items_cap, 1) * 8);
     p->off_n_items = take(4);
     p->off_row_seq = take(M * 4);
@@ -748,7 +748,8 @@ void launch_attention(const AttnArgs& a, const Plan& p, int kv_dt, hipStream_t s
             else if (kv_dt == E5M2) launch_attention_kvt<DT, E5M2>(a, p, s, aux);
             else launch_attention_kvt<DT, DT>(a, p, s, aux);
             if (merge_kernel && a.n_splits > 1)
-                launch1(VS_KERNEL_MERGE, attn_merge_kernel<DT, DH>, dim3(p.M, a.n_heads), dim3(DH), 0, s, a);
+                launch1(VS_KERNEL_MERGE, attn_merge_kernel<DT, DH>, dim3(a.merge_rows ? p.B : p.M, a.n_heads),
+                        dim3(DH), 0, s, a);
             return;
         }
     }
@@ -825,8 +826,11 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
     pa.error_flags = d->error_flags;
     int* seq_group = reinterpret_cast<int*>(ws + p.off_grp);
     int* seq_gp = seq_group + p.B;
+    int* merge_rows = seq_gp + p.B;
+    int* merge_count = merge_rows + p.B;
     pa.seq_group = p.groups ? seq_group : nullptr;
     pa.seq_gp = p.groups ? seq_gp : nullptr;
+    pa.merge_count = p.groups ? merge_count : nullptr;
     hipLaunchKernelGGL((prep_embed_kernel<DT>), dim3(p.M), dim3(256), 0, s, pa);
     if (p.groups) {
         GroupArgs ga;
@@ -844,6 +848,9 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
         ga.page_tokens = kPageTokens;
         ga.seq_group = seq_group;
         ga.seq_gp = seq_gp;
+        ga.merge_rows = merge_rows;
+        ga.merge_count = merge_count;
+        ga.M = p.M;
         ga.error_flags = d->error_flags;
         hipLaunchKernelGGL(prefix_group_kernel, dim3(d->n_prefix_groups), dim3(256), 0, s, ga);
     }
@@ -900,6 +907,10 @@ vs_status run_step(const Plan& p, const vs_batch_desc* d, const int32_t* bt, con
         a.pre_split_pages = p.pre_split_pages;
         a.gz_blocks = p.gz_blocks;
         a.gz_per_group = p.gz_per_group;
+        if (p.n_splits - p.n_pre_splits == 1) {  // only the grouped rows have splits to merge
+            a.merge_rows = merge_rows;
+            a.merge_count = merge_count;
+        }
     }
 
     // the split-K residual products hand the next RMSNorm's output over in xn (fused into their
