@@ -5,12 +5,16 @@
 // ([KV Cache] section 06, chunked prefill: the rows of a prompt chunk go
 // through the same weight products as the decode rows of their step; at
 // hundreds of rows the product is a dense contraction and the matrix cores
-// set its pace). A workgroup of four waves owns 256 weight rows x 128 batch
-// rows; each wave multiplies 128 weight rows (eight 16-row blocks) by 64 batch
-// rows (four 16-row tiles) with MFMA 16x16x32, 32 accumulators of four floats.
-// The q/k/v and gate/up products pair their blocks the way their epilogues
-// need (rotary halves; the gate and up rows of the same features), so a wave
-// holds four whole output tiles of those products, eight of the others.
+// set its pace). A workgroup of eight waves owns 256 weight rows x 128 batch
+// rows; each wave multiplies 64 weight rows (four 16-row blocks) by 64 batch
+// rows (four 16-row tiles) with MFMA 16x16x32, 16 accumulators of four floats.
+// Two waves share each SIMD, so one wave's LDS and barrier waits are covered
+// by the other's matrix work (with four waves of 128 x 64 the matrix cores
+// were busy about 38 % of the time; a probe on LDS data alone reached 43 % at
+// one wave per SIMD). The q/k/v and gate/up products pair their blocks the way
+// their epilogues need (rotary halves; the gate and up rows of the same
+// features), so a wave holds two whole output tiles of those products, four
+// of the others.
 //
 // Both operands go straight from global memory into LDS (gfx950's LDS-direct
 // loads, 16 bytes a lane) in 64-element steps of the reduction, through a ring
@@ -47,14 +51,16 @@ namespace vs {
 constexpr int kTileK = 64;                 // reduction elements per stage
 constexpr int kTileRowB = kTileK * 2;      // bytes of one staged row
 constexpr int kTileStages = 3;             // LDS stages (two in flight while one is multiplied)
-constexpr int kTileTN = 8;                 // 16-row weight blocks per wave
+constexpr int kTileWN = 4, kTileWM = 2;    // waves along the features and along the batch rows
+constexpr int kTileWaves = kTileWN * kTileWM;
+constexpr int kTileTN = 4;                 // 16-row weight blocks per wave
 constexpr int kTileTM = 4;                 // 16-row batch tiles per wave
-constexpr int kTileRowsN = 2 * kTileTN * 16;  // weight rows per workgroup (two waves along the features)
-constexpr int kTileRowsM = 2 * kTileTM * 16;  // batch rows per workgroup (two waves along the rows)
+constexpr int kTileRowsN = kTileWN * kTileTN * 16;  // weight rows per workgroup
+constexpr int kTileRowsM = kTileWM * kTileTM * 16;  // batch rows per workgroup
 
 // epilogue tiles (the skinny GEMM's tiling) per workgroup
 __host__ __device__ constexpr int tile_tiles_per_wg(int EPI) {
-    return (EPI == EPI_QKV || EPI == EPI_SWIGLU) ? kTileTN : 2 * kTileTN;
+    return (EPI == EPI_QKV || EPI == EPI_SWIGLU) ? kTileWN * kTileTN / 2 : kTileWN * kTileTN;
 }
 // workgroups of a launch: 8 x ceil(column blocks / 8) x row blocks (the padding ones return at once)
 __host__ __device__ inline int tile_grid(int n_tiles, int EPI, int n_slices, int M) {
@@ -66,16 +72,17 @@ __host__ __device__ inline int tile_grid(int n_tiles, int EPI, int n_slices, int
 // n_slices > 1 (EPI_RESID only): slice s of the reduction writes its sums to part[s][m][n] (n < g.n0)
 // instead of adding them to x.
 template <int DT, int EPI>
-__global__ void __launch_bounds__(256, 1) gemm_tile_kernel(GemmArgs g, int n_slices, float* part) {
+__global__ void __launch_bounds__(kTileWaves * 64, 1) gemm_tile_kernel(GemmArgs g, int n_slices, float* part) {
     constexpr bool PAIRED = EPI == EPI_QKV || EPI == EPI_SWIGLU;
     constexpr int TPG = tile_tiles_per_wg(EPI);
     constexpr int BN = kTileRowsN, BM = kTileRowsM;
-    constexpr int A_PER = BN / 8 / 4, B_PER = BM / 8 / 4;  // LDS-direct loads (8 rows each) per wave and stage
+    constexpr int A_PER = BN / 8 / kTileWaves, B_PER = BM / 8 / kTileWaves;  // LDS-direct loads (8 rows each) per wave and stage
+    static_assert(A_PER % 2 == 0 && A_PER + B_PER == 6, "whole 16-row weight blocks per wave; six loads per stage");
     constexpr int STAGE_B = (BN + BM) * kTileRowB;          // bytes of one stage: weight rows, then batch rows
     __shared__ __align__(1024) unsigned char lds[kTileStages * STAGE_B];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wn = wave & 1, wm = wave >> 1;  // this wave's weight half and row half
+    const int wn = wave % kTileWN, wm = wave / kTileWN;  // this wave's weight quarter and row half
 
     // workgroup -> (column block, row block): column block c = 8 (r / row blocks) + L % 8
     const int L = blockIdx.x, r = L >> 3;
@@ -91,14 +98,14 @@ __global__ void __launch_bounds__(256, 1) gemm_tile_kernel(GemmArgs g, int n_sli
 
     // Loads. Row group j (rows 8 j .. 8 j + 7 of an operand tile) is one load: lane l fills LDS row
     // 8 j + l / 8, slot l % 8, with chunk (l % 8) ^ ((4 j + l / 16) % 8) of that row. Wave w loads weight
-    // groups 8 w .. 8 w + 7 (16-row blocks 4 w .. 4 w + 3: block bases are wave-uniform) and batch groups
-    // 4 w .. 4 w + 3. Batch rows past M read row M - 1 (never stored); weight rows are whole 16-row
+    // groups 4 w .. 4 w + 3 (16-row blocks 2 w, 2 w + 1: block bases are wave-uniform) and batch groups
+    // 2 w, 2 w + 1. Batch rows past M read row M - 1 (never stored); weight rows are whole 16-row
     // blocks of valid rows (the host checks the segment sizes).
     const int lr = lane >> 3, ls = lane & 7;
     const char* abase[A_PER / 2];  // per 16-row block of the wave
 #pragma unroll
     for (int i = 0; i < A_PER / 2; ++i) {
-        const int blk = 4 * wave + i;
+        const int blk = (A_PER / 2) * wave + i;
         const int t = min(t0 + (PAIRED ? blk / 2 : blk), last_tile);
         const TileMap tm = tile_map<EPI>(g, t);
         const bool second = PAIRED && (blk & 1);
@@ -117,7 +124,7 @@ __global__ void __launch_bounds__(256, 1) gemm_tile_kernel(GemmArgs g, int n_sli
     uint32_t boff[B_PER];
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) {
-        const int j = 4 * wave + i;
+        const int j = B_PER * wave + i;
         const int m = min(m0 + 8 * j + lr, g.M - 1);
         boff[i] = (uint32_t)((m * g.act_ld + 8 * (ls ^ ((4 * j + (lane >> 4)) & 7))) * 2);
     }
@@ -133,15 +140,16 @@ __global__ void __launch_bounds__(256, 1) gemm_tile_kernel(GemmArgs g, int n_sli
     };
 #pragma clang diagnostic pop
     // step j of the slice into stage buffer sb (past the end: the last step again, never multiplied);
-    // A_PER + B_PER = 12 loads per wave
+    // A_PER + B_PER = 6 loads per wave
     auto issue = [&](int j, int sb) {
         const long ko = (long)min(j, nkb - 1) * kTileRowB;
         const uint32_t base = lds0 + (uint32_t)(sb * STAGE_B);
 #pragma unroll
         for (int i = 0; i < A_PER; ++i)
-            dma(abase[i / 2] + ko, (i & 1) ? aoff1 : aoff0, base + (uint32_t)((8 * wave + i) * 1024));
+            dma(abase[i / 2] + ko, (i & 1) ? aoff1 : aoff0, base + (uint32_t)((A_PER * wave + i) * 1024));
 #pragma unroll
-        for (int i = 0; i < B_PER; ++i) dma(act + ko, boff[i], base + (uint32_t)(BN * kTileRowB + (4 * wave + i) * 1024));
+        for (int i = 0; i < B_PER; ++i)
+            dma(act + ko, boff[i], base + (uint32_t)(BN * kTileRowB + (B_PER * wave + i) * 1024));
     };
 
     float4_t acc[kTileTN][kTileTM];
@@ -173,7 +181,7 @@ __global__ void __launch_bounds__(256, 1) gemm_tile_kernel(GemmArgs g, int n_sli
     };
 
     // The ring: step k sits in stage buffer k % 3. Before step k is multiplied the wave waits until at
-    // most one step's loads (12) are outstanding, i.e. its own loads of step k have landed, and the
+    // most one step's loads (6) are outstanding, i.e. its own loads of step k have landed, and the
     // barrier then covers every wave's; the same barrier frees the buffer of step k - 1, which takes
     // step k + 2.
     issue(0, 0);
@@ -183,7 +191,7 @@ __global__ void __launch_bounds__(256, 1) gemm_tile_kernel(GemmArgs g, int n_sli
         for (int u = 0; u < kTileStages; ++u) {
             const int k = k0 + u;
             if (k >= nkb) break;
-            asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+            asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
             __syncthreads();
             issue(k + 2, (u + 2) % kTileStages);
             compute(u);

@@ -580,7 +580,7 @@ void launch_resid_tile(int kind, const GemmArgs& g, int slices, float* part, hip
     if constexpr (DT == F32) {
         return;  // fp16 / bf16 only (the plan never selects this for fp32 models)
     } else {
-        launchn(kind, gemm_tile_kernel<DT, EPI_RESID>, dim3(tile_grid(g.n_tiles, EPI_RESID, slices, g.M)), dim3(256), 0,
+        launchn(kind, gemm_tile_kernel<DT, EPI_RESID>, dim3(tile_grid(g.n_tiles, EPI_RESID, slices, g.M)), dim3(kTileWaves * 64), 0,
                 s, g, slices, part);
         if (gain) {
             launchn(kind, resid_norm_kernel<DT>, dim3(g.M), dim3(1024), 0, s, g.x, (const float*)part, slices, g.M, g.n0,
@@ -601,7 +601,7 @@ void launch_gemm(int kind, const GemmArgs& g, hipStream_t s) {
         // more than 64 rows (a prompt chunk): LDS-tiled MFMA GEMM, eight paired (or two single) feature
         // tiles x 128 rows per workgroup
         if (M > 64 && tile_ok<EPI>(g)) {
-            launchn(kind, gemm_tile_kernel<DT, EPI>, dim3(tile_grid(g.n_tiles, EPI, 1, M)), dim3(256), 0, s, g, 1,
+            launchn(kind, gemm_tile_kernel<DT, EPI>, dim3(tile_grid(g.n_tiles, EPI, 1, M)), dim3(kTileWaves * 64), 0, s, g, 1,
                     (float*)nullptr);
             return;
         }
