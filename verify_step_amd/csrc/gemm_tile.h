@@ -5,16 +5,18 @@
 // ([KV Cache] section 06, chunked prefill: the rows of a prompt chunk go
 // through the same weight products as the decode rows of their step; at
 // hundreds of rows the product is a dense contraction and the matrix cores
-// set its pace). A workgroup of eight waves owns 256 weight rows x 128 batch
-// rows; each wave multiplies 64 weight rows (four 16-row blocks) by 64 batch
-// rows (four 16-row tiles) with MFMA 16x16x32, 16 accumulators of four floats.
-// Two waves share each SIMD, so one wave's LDS and barrier waits are covered
-// by the other's matrix work (with four waves of 128 x 64 the matrix cores
-// were busy about 38 % of the time; a probe on LDS data alone reached 43 % at
-// one wave per SIMD). The q/k/v and gate/up products pair their blocks the way
-// their epilogues need (rotary halves; the gate and up rows of the same
-// features), so a wave holds two whole output tiles of those products, four
-// of the others.
+// set its pace). A workgroup of sixteen waves owns 256 weight rows x 128 batch
+// rows; each wave multiplies 32 weight rows (two 16-row blocks) by 64 batch
+// rows (four 16-row tiles) with MFMA 16x16x32, 8 accumulators of four floats.
+// Four waves share each SIMD, so one wave's LDS and barrier waits are covered
+// by the others' matrix work. Measured on the 576-row 7B step (the four
+// products per step): four waves of 128 x 64, 11.0 ms (the matrix cores busy
+// about 38 % of the time; a probe on LDS data alone reached 43 % at one wave
+// per SIMD); eight waves of 64 x 64, 10.86 ms; sixteen waves of 64 x 32 or
+// 32 x 64, 10.58 and 10.56 ms. The q/k/v and gate/up products pair their
+// blocks the way their epilogues need (rotary halves; the gate and up rows of
+// the same features), so a wave holds one whole output tile of those
+// products, two of the others.
 //
 // Both operands go straight from global memory into LDS (gfx950's LDS-direct
 // loads, 16 bytes a lane) in 64-element steps of the reduction, through a ring
@@ -51,9 +53,9 @@ namespace vs {
 constexpr int kTileK = 64;                 // reduction elements per stage
 constexpr int kTileRowB = kTileK * 2;      // bytes of one staged row
 constexpr int kTileStages = 3;             // LDS stages (two in flight while one is multiplied)
-constexpr int kTileWN = 4, kTileWM = 2;    // waves along the features and along the batch rows
+constexpr int kTileWN = 8, kTileWM = 2;    // waves along the features and along the batch rows
 constexpr int kTileWaves = kTileWN * kTileWM;
-constexpr int kTileTN = 4;                 // 16-row weight blocks per wave
+constexpr int kTileTN = 2;                 // 16-row weight blocks per wave
 constexpr int kTileTM = 4;                 // 16-row batch tiles per wave
 constexpr int kTileRowsN = kTileWN * kTileTN * 16;  // weight rows per workgroup
 constexpr int kTileRowsM = kTileWM * kTileTM * 16;  // batch rows per workgroup
@@ -77,12 +79,12 @@ __global__ void __launch_bounds__(kTileWaves * 64, 1) gemm_tile_kernel(GemmArgs 
     constexpr int TPG = tile_tiles_per_wg(EPI);
     constexpr int BN = kTileRowsN, BM = kTileRowsM;
     constexpr int A_PER = BN / 8 / kTileWaves, B_PER = BM / 8 / kTileWaves;  // LDS-direct loads (8 rows each) per wave and stage
-    static_assert(A_PER % 2 == 0 && A_PER + B_PER == 6, "whole 16-row weight blocks per wave; six loads per stage");
+    static_assert(A_PER % 2 == 0 && B_PER >= 1, "whole 16-row weight blocks and 8-row batch groups per wave");
     constexpr int STAGE_B = (BN + BM) * kTileRowB;          // bytes of one stage: weight rows, then batch rows
     __shared__ __align__(1024) unsigned char lds[kTileStages * STAGE_B];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wn = wave % kTileWN, wm = wave / kTileWN;  // this wave's weight quarter and row half
+    const int wn = wave % kTileWN, wm = wave / kTileWN;  // this wave's weight block and row block
 
     // workgroup -> (column block, row block): column block c = 8 (r / row blocks) + L % 8
     const int L = blockIdx.x, r = L >> 3;
@@ -98,8 +100,8 @@ __global__ void __launch_bounds__(kTileWaves * 64, 1) gemm_tile_kernel(GemmArgs 
 
     // Loads. Row group j (rows 8 j .. 8 j + 7 of an operand tile) is one load: lane l fills LDS row
     // 8 j + l / 8, slot l % 8, with chunk (l % 8) ^ ((4 j + l / 16) % 8) of that row. Wave w loads weight
-    // groups 4 w .. 4 w + 3 (16-row blocks 2 w, 2 w + 1: block bases are wave-uniform) and batch groups
-    // 2 w, 2 w + 1. Batch rows past M read row M - 1 (never stored); weight rows are whole 16-row
+    // groups A_PER w .. A_PER w + A_PER - 1 (whole 16-row blocks: block bases are wave-uniform) and batch
+    // groups B_PER w .. B_PER w + B_PER - 1. Batch rows past M read row M - 1 (never stored); weight rows are whole 16-row
     // blocks of valid rows (the host checks the segment sizes).
     const int lr = lane >> 3, ls = lane & 7;
     const char* abase[A_PER / 2];  // per 16-row block of the wave
@@ -140,7 +142,7 @@ __global__ void __launch_bounds__(kTileWaves * 64, 1) gemm_tile_kernel(GemmArgs 
     };
 #pragma clang diagnostic pop
     // step j of the slice into stage buffer sb (past the end: the last step again, never multiplied);
-    // A_PER + B_PER = 6 loads per wave
+    // A_PER + B_PER loads per wave
     auto issue = [&](int j, int sb) {
         const long ko = (long)min(j, nkb - 1) * kTileRowB;
         const uint32_t base = lds0 + (uint32_t)(sb * STAGE_B);
@@ -181,7 +183,7 @@ __global__ void __launch_bounds__(kTileWaves * 64, 1) gemm_tile_kernel(GemmArgs 
     };
 
     // The ring: step k sits in stage buffer k % 3. Before step k is multiplied the wave waits until at
-    // most one step's loads (6) are outstanding, i.e. its own loads of step k have landed, and the
+    // most one step's loads (A_PER + B_PER) are outstanding, i.e. its own loads of step k have landed, and the
     // barrier then covers every wave's; the same barrier frees the buffer of step k - 1, which takes
     // step k + 2.
     issue(0, 0);
@@ -191,7 +193,7 @@ __global__ void __launch_bounds__(kTileWaves * 64, 1) gemm_tile_kernel(GemmArgs 
         for (int u = 0; u < kTileStages; ++u) {
             const int k = k0 + u;
             if (k >= nkb) break;
-            asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(A_PER + B_PER) : "memory");
             __syncthreads();
             issue(k + 2, (u + 2) % kTileStages);
             compute(u);
@@ -200,7 +202,7 @@ __global__ void __launch_bounds__(kTileWaves * 64, 1) gemm_tile_kernel(GemmArgs 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the ring's last loads (past the end) have landed
 
     // ---- epilogues: the wave's output tiles ----
-    const int mg = im * 2 + wm;  // row group of 64 rows
+    const int mg = im * kTileWM + wm;  // row group of 16 kTileTM rows
     if (n_slices > 1) {
         if constexpr (EPI == EPI_RESID) {
             const int nl0 = kq * 4;
@@ -211,7 +213,7 @@ __global__ void __launch_bounds__(kTileWaves * 64, 1) gemm_tile_kernel(GemmArgs 
                 const int n = 16 * t + nl0;
 #pragma unroll
                 for (int i = 0; i < kTileTM; ++i) {
-                    const int m = mg * 64 + i * 16 + l16;
+                    const int m = mg * 16 * kTileTM + i * 16 + l16;
                     if (m >= g.M) continue;
                     float* dst = part + ((long)sl * g.M + m) * g.n0 + n;
                     if (n + 3 < g.n0) {
@@ -236,7 +238,7 @@ __global__ void __launch_bounds__(kTileWaves * 64, 1) gemm_tile_kernel(GemmArgs 
         long koff[kTileTM];
 #pragma unroll
         for (int i = 0; i < kTileTM; ++i) {
-            mrow[i] = mg * 64 + i * 16 + l16;
+            mrow[i] = mg * 16 * kTileTM + i * 16 + l16;
             koff[i] = g.row_kvoff[min(mrow[i], g.M - 1)];
         }
         TileMap tms[TPW];
