@@ -10,9 +10,10 @@
 // rows (four 16-row tiles) with MFMA 16x16x32, 8 accumulators of four floats.
 // Four waves share each SIMD, so one wave's LDS and barrier waits are covered
 // by the others' matrix work. Measured on the 576-row 7B step (the four
-// products per step): four waves of 128 x 64, 11.0 ms (the matrix cores busy
-// about 38 % of the time; a probe on LDS data alone reached 43 % at one wave
-// per SIMD); eight waves of 64 x 64, 10.86 ms; sixteen waves of 64 x 32 or
+// products per step by dispatch events, the residual products' slice sums
+// included): four waves of 128 x 64, 11.97 ms (the matrix cores busy about
+// 38 % of the time; a probe on LDS data alone reached 43 % at one wave per
+// SIMD); eight waves of 64 x 64, 10.86 ms; sixteen waves of 64 x 32 or
 // 32 x 64, 10.58 and 10.56 ms. The q/k/v and gate/up products pair their
 // blocks the way their epilogues need (rotary halves; the gate and up rows of
 // the same features), so a wave holds one whole output tile of those
