@@ -130,7 +130,9 @@ __global__ void __launch_bounds__(1024) attn_items_kernel(const int* q_start, in
 // Two waves per SIMD (at most 256 registers, no scratch): with one page in flight per wave, a
 // decode step's few states leave the kernel bound by load latency, and the second resident
 // workgroup is what hides it.
-template <int DT, int HG, int KVT>
+// EXT: group blocks, grouped sequences (seq_gp) and the work list may be present; without it the kernel
+// takes plain blocks only (every sequence x row-group block) and none of that code is compiled in.
+template <int DT, int HG, int KVT, bool EXT>
 __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a) {
     constexpr int DH = kAmDh;
     constexpr int R = 16 / HG;  // rows per group
@@ -146,7 +148,7 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
     // the same prefix page ids, checked before: a member that fails the check has seq_group -1 and
     // takes the plain path). Any other block takes row groups of one sequence, as below, and the key
     // split n_pre_splits + blockIdx.x.
-    const bool grp = (int)blockIdx.z < a.gz_blocks;
+    const bool grp = EXT && (int)blockIdx.z < a.gz_blocks;
     int s = blockIdx.x, b, rgb, rg_step, r0, Rn, ctx, gp, gi = 0, j0 = 0, gn = 0;
     if (grp) {  // z = (group block) x n_pre_splits + prefix split; blocks past x = 0 are not needed
         if (s > 0) return;
@@ -163,10 +165,12 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
         ctx = 0;
         gp = min(max(a.group_pages[gi], 0), a.max_blocks);
     } else {
-        s += a.n_pre_splits;
-        if (s >= a.n_splits) return;
-        const int z = blockIdx.z - a.gz_blocks;
-        if (a.items) {  // one unit of the work list
+        if constexpr (EXT) {
+            s += a.n_pre_splits;
+            if (s >= a.n_splits) return;
+        }
+        const int z = blockIdx.z - (EXT ? a.gz_blocks : 0);
+        if (EXT && a.items) {  // one unit of the work list
             if (z >= *a.n_items) return;
             const int2 it = a.items[z];
             b = min(max(it.x, 0), a.B - 1);
@@ -180,7 +184,7 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
         r0 = min(max(a.q_start[b], 0), a.M);
         Rn = min(max(a.q_start[b + 1] - r0, 0), a.M - r0);
         if (Rn < a.rows_lo || Rn > a.rows_hi) return;  // another kernel's sequence
-        gp = a.seq_gp ? a.seq_gp[b] : 0;  // a grouped sequence: its prefix splits come from the group blocks
+        gp = EXT && a.seq_gp ? a.seq_gp[b] : 0;  // a grouped sequence: its prefix splits come from the group blocks
         ctx = max(a.ctx_len[b], 0);
     }
     const int* bt = a.block_tables + (long)b * a.max_blocks;
@@ -194,25 +198,25 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
     __shared__ __align__(16) uint16_t pt[kAmWaves][2][16 * kAmPLd];  // P hi / lo, [state][key]
     __shared__ __align__(16) uint16_t vt[kAmWaves][16 * kAmVLd];     // V page, [key][dim]
     __shared__ float wst[kAmWaves][16][DH + 2];                      // per-wave (m, l, o) of each state
-    __shared__ int srow[R], spos[R];  // each row slot's q / output row (-1: none) and position
+    __shared__ int srow[R], spos[R];  // a group block's row slots: q / output row (-1: none) and position
 
     for (int rg = rgb * R; rg < Rn; rg += rg_step) {
-        if (tid < R) {
-            int row = -1, pos = 0;
-            if (grp) {
+        if (grp) {  // the member sequences' rows and positions (group blocks only: a plain block's follow from rg)
+            if (tid < R) {
+                int row = -1, pos = 0;
                 const int seq = a.group_seq0[gi] + j0 + tid;
                 if (j0 + tid < gn && seq >= 0 && seq < a.B && a.seq_group[seq] == gi) {
                     row = min(max(a.q_start[seq], 0), a.M - 1);
                     pos = max(a.ctx_len[seq], 0);
                 }
-            } else if (rg + tid < Rn) {
-                row = r0 + rg + tid;
-                pos = ctx + rg + tid;
+                srow[tid] = row;
+                spos[tid] = pos;
             }
-            srow[tid] = row;
-            spos[tid] = pos;
+            __syncthreads();
         }
-        __syncthreads();
+        // row slot i's q / output row (-1: none) and its position
+        auto slot_row = [&](int i) { return grp ? srow[i] : rg + i < Rn ? r0 + rg + i : -1; };
+        auto slot_pos = [&](int i) { return grp ? spos[i] : ctx + rg + i; };
         int p_begin, p_end;
         if (grp) {
             bool any = false;
@@ -228,9 +232,9 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
         uint4 qf[4];
         {
             const int i = l16 / HG, j = l16 % HG;
-            const int row = srow[i];
+            const int row = slot_row(i);
             const bool ok = row >= 0;
-            const long qrow = (long)(ok ? row : 0) * QLD + (long)(h0 + j) * DH + 8 * kq;
+            const long qrow = (long)(ok ? row : max(slot_row(0), 0)) * QLD + (long)(h0 + j) * DH + 8 * kq;
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const uint4 v = *reinterpret_cast<const uint4*>(qb + qrow + 32 * st);
@@ -243,8 +247,8 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = (4 * kq + r) / HG;
-            sv[r] = srow[i] >= 0;
-            qpos[r] = spos[i];
+            sv[r] = slot_row(i) >= 0;
+            qpos[r] = slot_pos(i);
         }
         float m[4], l[4];
         float4_t o[8];
@@ -353,9 +357,10 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
         // a row with one key split (no group, one plain split) is final here; the merge kernel skips it
         const bool single = !grp && gp == 0 && a.n_splits - a.n_pre_splits == 1;
         // merge the waves in wave order; thread t takes (state, dim) pairs of the valid states
-        for (int idx = tid; idx < 16 * DH; idx += kAmWaves * 64) {
+        const int n_st = grp ? 16 : min(R, Rn - rg) * HG;  // a plain block's valid states come first
+        for (int idx = tid; idx < n_st * DH; idx += kAmWaves * 64) {
             const int st = idx / DH, d = idx % DH;
-            const int row = srow[st / HG], h = h0 + st % HG;
+            const int row = slot_row(st / HG), h = h0 + st % HG;
             if (row < 0) continue;
             float mx = -INFINITY;
 #pragma unroll

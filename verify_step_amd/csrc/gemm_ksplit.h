@@ -377,30 +377,31 @@ __global__ void __launch_bounds__(256) resid_reduce_kernel(float* __restrict__ x
 // workgroups, so every thread keeps its four features' partial sums of all slices in flight at
 // once; the mean of squares is summed in a fixed order (per thread, then per wave, then over the
 // waves in order). D must be a multiple of 4.
-template <int DT>
+// The sum over slices of four features' partials (src: slice 0's, the slices plane floats apart), in
+// slice order: JB slices' loads at a time, all issued before the first add (the slice index is clamped
+// instead of branched around, so none of them waits for another).
+template <int JB>
+__device__ __forceinline__ float4_t ks_slice_sum4(const float* src, long plane, int n_slices) {
+    float4_t s = (float4_t){0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < n_slices; s0 += JB) {
+        float4_t v[JB];
+#pragma unroll
+        for (int j = 0; j < JB; ++j) v[j] = *reinterpret_cast<const float4_t*>(src + min(s0 + j, n_slices - 1) * plane);
+#pragma unroll
+        for (int j = 0; j < JB; ++j)
+            if (s0 + j < n_slices) s = s0 + j == 0 ? v[j] : s + v[j];
+    }
+    return s;
+}
+
+template <int DT, int JB>  // JB: slices' loads issued at a time (4: up to four slices; 12 otherwise)
 __global__ void __launch_bounds__(1024) resid_norm_kernel(float* __restrict__ x, const float* __restrict__ part,
                                                           int n_slices, int M, int D, const void* gain, float eps,
                                                           void* y) {
     const int m = blockIdx.x, tid = threadIdx.x;
     const long plane = (long)M * D;
     float* xr = x + (long)m * D;
-    // the sum over slices of four features' partials; twelve slices' loads at a time, all issued
-    // before the first add (the slice index is clamped instead of branched around, so none of them
-    // waits for another)
-    auto slice_sum4 = [&](int k) {
-        const float* src = part + (long)m * D + k;
-        float4_t s = (float4_t){0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < n_slices; s0 += 12) {
-            float4_t v[12];
-#pragma unroll
-            for (int j = 0; j < 12; ++j)
-                v[j] = *reinterpret_cast<const float4_t*>(src + min(s0 + j, n_slices - 1) * plane);
-#pragma unroll
-            for (int j = 0; j < 12; ++j)
-                if (s0 + j < n_slices) s = s0 + j == 0 ? v[j] : s + v[j];
-        }
-        return s;
-    };
+    auto slice_sum4 = [&](int k) { return ks_slice_sum4<JB>(part + (long)m * D + k, plane, n_slices); };
     __shared__ float wsum[16];
     auto row_inv = [&](float ss) {
 #pragma unroll

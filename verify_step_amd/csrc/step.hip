@@ -451,9 +451,6 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
         o = align256(o + std::max<size_t>(bytes, 4));
         return at;
     };
-    p->off_grp = take(p->groups ? (3 * (size_t)d->B + 1) * 4 : 4);  // seq_group, seq_gp, merge_rows, count
-    p->off_items = take((size_t)std::max(p->items_cap, 1) * 8);
-    p->off_n_items = take(4);
     p->off_row_seq = take(M * 4);
     p->off_row_pos = take(M * 4);
     p->off_kvoff = take(M * 8);
@@ -468,6 +465,9 @@ vs_status make_plan(const vs_batch_desc* d, const vs_model_desc* m, Plan* p) {
     p->off_lmpart = take(ML * p->n_lm_parts * sizeof(ArgPart));
     if (p->tile_slices > 1) ks_floats = std::max<long>(ks_floats, (long)p->tile_slices * p->D);
     p->off_ksp = take(p->ksplit || p->ksplit_qkv || p->ksplit_lm || p->tile_slices > 1 ? (size_t)ks_floats * M * 4 : 4);
+    p->off_grp = take(p->groups ? (3 * (size_t)d->B + 1) * 4 : 4);  // seq_group, seq_gp, merge_rows, count
+    p->off_items = take((size_t)std::max(p->items_cap, 1) * 8);
+    p->off_n_items = take(4);
     p->total = o;
     return vs_ok();
 }
@@ -553,7 +553,8 @@ void launch_resid_ksplit(int kind, const void* w, int N, int K, const void* act,
     } else {
     const int slices = launch_ksplit<DT>(kind, w, w, w, N, 0, N, K, act, act_ld, M, part, s);
     if (gain) {
-        launchn(kind, resid_norm_kernel<DT>, dim3(M), dim3(1024), 0, s, x, part, slices, M, N, gain, eps, y);
+        if (slices <= 4) launchn(kind, resid_norm_kernel<DT, 4>, dim3(M), dim3(1024), 0, s, x, part, slices, M, N, gain, eps, y);
+        else launchn(kind, resid_norm_kernel<DT, 12>, dim3(M), dim3(1024), 0, s, x, part, slices, M, N, gain, eps, y);
     } else {
         const long groups = (long)M * ((N + 3) / 4);
         launchn(kind, resid_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, x, x_ld,
@@ -583,8 +584,8 @@ void launch_resid_tile(int kind, const GemmArgs& g, int slices, float* part, hip
         launchn(kind, gemm_tile_kernel<DT, EPI_RESID>, dim3(tile_grid(g.n_tiles, EPI_RESID, slices, g.M)), dim3(kTileWaves * 64), 0,
                 s, g, slices, part);
         if (gain) {
-            launchn(kind, resid_norm_kernel<DT>, dim3(g.M), dim3(1024), 0, s, g.x, (const float*)part, slices, g.M, g.n0,
-                    gain, eps, y);
+            auto rn = slices <= 4 ? resid_norm_kernel<DT, 4> : resid_norm_kernel<DT, 12>;
+            launchn(kind, rn, dim3(g.M), dim3(1024), 0, s, g.x, (const float*)part, slices, g.M, g.n0, gain, eps, y);
         } else {
             const long groups = (long)g.M * ((g.n0 + 3) / 4);
             launchn(kind, resid_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, g.x, g.x_ld,
@@ -693,12 +694,15 @@ template <int DT, int KVT>
 void launch_attention_mfma(const AttnArgs& a, int z_seq, int hg, hipStream_t s) {
     const int nx = z_seq == 0 ? 1 : a.n_splits - a.n_pre_splits;  // the group blocks carry their split in z
     const dim3 grid(nx, a.n_heads / hg, a.gz_blocks + z_seq), block(kAmWaves * 64);
+    // the kernel with group blocks, grouped sequences and the work list compiled in only where used
+    const bool ext = a.gz_blocks > 0 || a.items || a.seq_gp;
+    auto go = [&](auto plain, auto full) { launch1(VS_KERNEL_ATTN, ext ? full : plain, grid, block, 0, s, a); };
     switch (hg) {
-        case 1: launch1(VS_KERNEL_ATTN, attn_mfma_kernel<DT, 1, KVT>, grid, block, 0, s, a); break;
-        case 2: launch1(VS_KERNEL_ATTN, attn_mfma_kernel<DT, 2, KVT>, grid, block, 0, s, a); break;
-        case 4: launch1(VS_KERNEL_ATTN, attn_mfma_kernel<DT, 4, KVT>, grid, block, 0, s, a); break;
-        case 8: launch1(VS_KERNEL_ATTN, attn_mfma_kernel<DT, 8, KVT>, grid, block, 0, s, a); break;
-        default: launch1(VS_KERNEL_ATTN, attn_mfma_kernel<DT, 16, KVT>, grid, block, 0, s, a); break;
+        case 1: go(attn_mfma_kernel<DT, 1, KVT, false>, attn_mfma_kernel<DT, 1, KVT, true>); break;
+        case 2: go(attn_mfma_kernel<DT, 2, KVT, false>, attn_mfma_kernel<DT, 2, KVT, true>); break;
+        case 4: go(attn_mfma_kernel<DT, 4, KVT, false>, attn_mfma_kernel<DT, 4, KVT, true>); break;
+        case 8: go(attn_mfma_kernel<DT, 8, KVT, false>, attn_mfma_kernel<DT, 8, KVT, true>); break;
+        default: go(attn_mfma_kernel<DT, 16, KVT, false>, attn_mfma_kernel<DT, 16, KVT, true>); break;
     }
 }
 
