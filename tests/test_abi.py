@@ -103,6 +103,32 @@ def test_step_rejects_bad_shapes_before_launching(L):
     assert e.value.status == vs.VS_ERR_INVALID
 
 
+def test_prefix_groups_checked_on_the_host(L):
+    """Shared-prefix groups in the batch descriptor: an fp16 / bf16 model with head_dim 128 plans them (the
+    workspace grows by the group bookkeeping) and rejects inconsistent ones with VS_ERR_INVALID before any
+    device call; an fp32 model or head_dim 64 ignores them."""
+    fake = 4096  # non-null stand-ins for the device arrays (nothing is dereferenced on the host)
+    dims = vs.vs_model_desc(256, 2, 2, 128, 512, 1000, 2, vs.VS_F16, 10000.0, 1e-5)
+
+    def desc(n_groups=1, size=4, pages=3, arrays=True, B=5, max_blocks=8):
+        d = vs.vs_batch_desc(B, B, B, 1, 100, max_blocks, None, None, None, None, None)
+        d.n_prefix_groups, d.max_group_size, d.max_group_pages = n_groups, size, pages
+        if arrays:
+            d.group_seq0, d.group_n, d.group_pages = fake, fake, fake
+        return d
+
+    plain = vs.decode_step_workspace_bytes(desc(n_groups=0), dims)
+    assert vs.decode_step_workspace_bytes(desc(), dims) > plain
+    for bad in (desc(arrays=False), desc(size=6), desc(n_groups=6), desc(pages=9), desc(size=0), desc(n_groups=-1)):
+        with pytest.raises(vs.VSError) as e:
+            vs.decode_step_workspace_bytes(bad, dims)
+        assert e.value.status == vs.VS_ERR_INVALID
+    for other in (vs.vs_model_desc(256, 2, 2, 128, 512, 1000, 2, vs.VS_F32, 10000.0, 1e-5),
+                  vs.vs_model_desc(256, 4, 4, 64, 512, 1000, 2, vs.VS_F16, 10000.0, 1e-5)):
+        assert vs.decode_step_workspace_bytes(desc(arrays=False, size=6), other) == \
+            vs.decode_step_workspace_bytes(desc(n_groups=0), other)
+
+
 def test_verify_accept_rejects_null(L):
     with pytest.raises(vs.VSError):
         vs.verify_accept(3, None, None, None, None, None, None, 0)
