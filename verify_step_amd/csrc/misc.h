@@ -257,10 +257,69 @@ __global__ void __launch_bounds__(256) argmax_accept_kernel(const ArgPart* parts
             if (logit_rows[mid] < r0) lo = mid + 1;
             else hi = mid;
         }
+        int hi2 = lo, top = M_log;  // the sequence's logit rows are logit_rows[lo .. hi2)
+        while (hi2 < top) {
+            const int mid = (hi2 + top) >> 1;
+            if (logit_rows[mid] < r1) hi2 = mid + 1;
+            else top = mid;
+        }
         __syncthreads();  // the defaults above land before the values below
-        for (int j = lo; j < M_log; ++j) {
+        if (hi2 - lo >= 2) {
+            // several logit rows (a verify pass): up to eight rows at a time, every thread combining its
+            // tiles of all of them, so the rows' partials are requested together; the combine is exact in
+            // any order (largest value, lowest index on ties, second value)
+            constexpr int RB = 8;
+            __shared__ float bv1[RB][4], bv2[RB][4];
+            __shared__ int bi1[RB][4];
+            const int wave = threadIdx.x >> 6;
+            for (int j0 = lo; j0 < hi2; j0 += RB) {
+                const int nr = min(RB, hi2 - j0);
+                float v1[RB], v2[RB];
+                int i1[RB];
+#pragma unroll
+                for (int q = 0; q < RB; ++q) {
+                    v1[q] = v2[q] = -INFINITY;
+                    i1[q] = 0x7FFFFFFF;
+                }
+                // every load unconditional (rows past the pass's last re-read it, and are never written):
+                // with a branch around a load the compiler waits for each before issuing the next
+                for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) {
+                    ArgPart p[RB];
+#pragma unroll
+                    for (int q = 0; q < RB; ++q) p[q] = parts[(long)(j0 + min(q, nr - 1)) * n_tiles + t];
+#pragma unroll
+                    for (int q = 0; q < RB; ++q) argpart_combine(v1[q], i1[q], v2[q], p[q].v1, p[q].i1, p[q].v2);
+                }
+#pragma unroll
+                for (int q = 0; q < RB; ++q) {
+#pragma unroll
+                    for (int mask = 32; mask >= 1; mask >>= 1) {
+                        const float o1 = shfl_xor(v1[q], mask);
+                        const int oi = shfl_xor(i1[q], mask);
+                        const float o2 = shfl_xor(v2[q], mask);
+                        argpart_combine(v1[q], i1[q], v2[q], o1, oi, o2);
+                    }
+                    if ((threadIdx.x & 63) == 0) {
+                        bv1[q][wave] = v1[q];
+                        bi1[q][wave] = i1[q];
+                        bv2[q][wave] = v2[q];
+                    }
+                }
+                __syncthreads();
+                if (threadIdx.x < nr) {
+                    const int q = threadIdx.x;
+                    float a1 = bv1[q][0], a2 = bv2[q][0];
+                    int ai = bi1[q][0];
+                    for (int w = 1; w < 4; ++w) argpart_combine(a1, ai, a2, bv1[q][w], bi1[q][w], bv2[q][w]);
+                    const int r = logit_rows[j0 + q];
+                    argmax[r] = ai;
+                    if (gap) gap[r] = a1 - a2;
+                }
+                __syncthreads();  // the rows' argmax land before the acceptance reads them; LDS is free again
+            }
+        }
+        for (int j = lo; j < (hi2 - lo >= 2 ? lo : hi2); ++j) {
             const int r = logit_rows[j];
-            if (r >= r1) break;
             float v1 = -INFINITY, v2 = -INFINITY;
             int i1 = 0x7FFFFFFF;
             for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) {
