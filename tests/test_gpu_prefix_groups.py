@@ -192,3 +192,42 @@ def test_prefix_groups_graph_replays_match_the_eager_step():
         junk = torch.randn(1 << 20, device="cuda")  # other work between the replays
         float(junk.square().sum())
     pool.close()
+
+
+def test_prefix_groups_one_stream_equals_two_streams():
+    """decode_step runs the matrix-core kernel and the VALU kernel of a step with groups on two streams;
+    decode_step_noalloc keeps every kernel on the caller's stream, one after the other. Same kernels, same
+    key splits, so the "chunk" case (fp16) gives the same logits, greedy tokens, gaps and K/V rows bit for
+    bit either way."""
+    _say("prefix groups: one stream (decode_step_noalloc) against two (decode_step)")
+    heads, kvh, prefixes, members, groups = CASES["chunk"]
+    dims = W.ModelDims(f"tiny-dh128-{heads}x{kvh}-2L", heads * 128, heads, kvh, 128, 512, 1000, 2, "f16")
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, ref, seqs_o, pool, rows, ctxs, ks = run_groups(dims, prefixes, members, groups, flags)
+    model = run_groups.model
+    sb = out["groups"][0]
+    n_log, M = int(sb.desc.M_log), sum(ks)
+
+    def outputs():
+        kv = [pool.read(rows[b], ctxs[b], ctxs[b] + ks[b]) for b in range(len(ctxs))]
+        return [sb.logits[:n_log].clone(), sb.argmax[:M].clone(), sb.gap[:M].clone()] + kv
+
+    run_step(model, sb)
+    torch.cuda.synchronize()
+    want = outputs()
+    sb.logits.fill_(float("nan"))
+    sb.argmax.fill_(-7)
+    sb.gap.fill_(float("nan"))
+    for b in range(len(ctxs)):
+        pool.write(rows[b], ctxs[b], torch.zeros(dims.n_layers, 2, ks[b], kvh, 128, dtype=dims.kv_torch_dtype))
+    assert sb.ws_bytes <= vs.VS_NOALLOC_SCRATCH_BYTES
+    vs.decode_step_noalloc(sb.desc, sb.block_tables, model.w, sb.out, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = outputs()
+    for i, (a, c) in enumerate(zip(want, got)):
+        if a.is_floating_point():
+            same = torch.equal(a.contiguous().view(torch.uint8), c.contiguous().view(torch.uint8))
+        else:
+            same = torch.equal(a, c)
+        assert same, f"output {i} differs between one and two streams"
+    pool.close()
