@@ -8,7 +8,8 @@ key splits ([KV Cache] section 07). The result is the same attention as without 
 the step with and without the groups and checks both against the oracle (logits, greedy tokens, the K/V
 rows written).
 
-Tiny models with head_dim 128 (the grouped path's shape), fp16 and bf16, plain and grouped K/V heads.
+Tiny models with head_dim 128 (the grouped path's shape), fp16 and bf16, plain and grouped K/V heads,
+16-bit and 8-bit caches.
 A group may span several of the matrix-core kernel's group blocks (16 / HG sequences each), a group
 member may fail the check (a block table that differs in the prefix, or two rows), and then it is
 attended like any other sequence, with VS_STEP_BAD_BATCH in the validation word.
@@ -120,6 +121,25 @@ def test_prefix_groups_match_the_oracle(dtype, case):
     heads, kvh, prefixes, members, groups = CASES[case]
     _say(f"prefix groups {case} dtype={dtype}")
     dims = W.ModelDims(f"tiny-dh128-{heads}x{kvh}-2L", heads * 128, heads, kvh, 128, 512, 1000, 2, dtype)
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, ref, seqs_o, pool, rows, ctxs, ks = run_groups(dims, prefixes, members, groups, flags)
+    for label, (sb, fl) in out.items():
+        _say(f"  checking the step with {label}")
+        assert fl == 0, f"{label}: validation word {fl}"
+        check_case(dims, sb, ref, seqs_o, pool, rows, ctxs, ks)
+    pool.close()
+
+
+@pytest.mark.parametrize("fmt,dtype,case", [("e4m3", "f16", "mha"), ("e5m2", "bf16", "gqa"), ("e4m3", "bf16", "chunk")])
+def test_prefix_groups_with_an_8bit_cache(fmt, dtype, case):
+    """The same groups over an 8-bit K/V cache ([KV Cache] section 03): the group blocks widen the shared
+    prefix pages exactly as the other attention kernels widen their own. One layer, as the other 8-bit
+    cache tests: the K/V rows a step writes are then a rounding of the embedding's projections, which the
+    check holds to one value of the format (past the first layer they also carry the attention's rounding,
+    and an e5m2 element near zero can move by more than one of its steps)."""
+    heads, kvh, prefixes, members, groups = CASES[case]
+    _say(f"prefix groups {case} dtype={dtype} cache={fmt}")
+    dims = W.ModelDims(f"tiny-dh128-{heads}x{kvh}-1L", heads * 128, heads, kvh, 128, 512, 1000, 1, dtype).with_kv(fmt)
     flags = torch.zeros(1, dtype=torch.int32, device="cuda")
     out, ref, seqs_o, pool, rows, ctxs, ks = run_groups(dims, prefixes, members, groups, flags)
     for label, (sb, fl) in out.items():
