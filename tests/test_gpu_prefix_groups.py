@@ -108,6 +108,9 @@ CASES = {
     "mha-decode": (2, 2, [80], [(0, s, 1) for s in [0, 7, 44, 130, 16, 3]] + [(None, 60, 1)], [(0, 6, 5)]),
     # one group on a 640-token prefix (40 pages): the group blocks cut it into several prefix splits
     "long-prefix": (2, 2, [640], [(0, s, 1) for s in [3, 50, 17, 0]] + [(None, 30, 1)], [(0, 4, 40)]),
+    # three one-row sequences (the row-streaming GEMV path): the merge kernel combines the grouped rows'
+    # splits, where without groups the output product's prologue would
+    "gemv": (2, 2, [64], [(0, s, 1) for s in [5, 20, 1]], [(0, 3, 4)]),
     # a 70-row prompt chunk from position 0 beside 12 grouped decode rows: the matrix-core kernel's plain
     # blocks go by its work list (5 row groups of the chunk) instead of 13 sequences x 5 row-group blocks
     "chunk": (2, 2, [32], [(0, s, 1) for s in [0, 3, 9, 17, 30, 1, 2, 4, 5, 6, 7, 8]] + [(None, 0, 70)],
