@@ -553,8 +553,8 @@ void launch_resid_ksplit(int kind, const void* w, int N, int K, const void* act,
     } else {
     const int slices = launch_ksplit<DT>(kind, w, w, w, N, 0, N, K, act, act_ld, M, part, s);
     if (gain) {
-        if (slices <= 4) launchn(kind, resid_norm_kernel<DT, 4>, dim3(M), dim3(1024), 0, s, x, part, slices, M, N, gain, eps, y);
-        else launchn(kind, resid_norm_kernel<DT, 12>, dim3(M), dim3(1024), 0, s, x, part, slices, M, N, gain, eps, y);
+        auto rn = slices <= 4 ? resid_norm_kernel<DT, 4> : slices <= 12 ? resid_norm_kernel<DT, 12> : resid_norm_kernel<DT, 16>;
+        launchn(kind, rn, dim3(M), dim3(1024), 0, s, x, part, slices, M, N, gain, eps, y);
     } else {
         const long groups = (long)M * ((N + 3) / 4);
         launchn(kind, resid_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, x, x_ld,
