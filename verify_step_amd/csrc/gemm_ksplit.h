@@ -394,7 +394,7 @@ __device__ __forceinline__ float4_t ks_slice_sum4(const float* src, long plane, 
     return s;
 }
 
-template <int DT, int JB>  // JB: slices' loads issued at a time (4: up to four slices; 12 up to twelve; 16 beyond)
+template <int DT, int JB>  // JB: slices' loads issued at a time (4, 12 or 16, whichever fits the slice count)
 __global__ void __launch_bounds__(1024) resid_norm_kernel(float* __restrict__ x, const float* __restrict__ part,
                                                           int n_slices, int M, int D, const void* gain, float eps,
                                                           void* y) {

@@ -553,7 +553,11 @@ void launch_resid_ksplit(int kind, const void* w, int N, int K, const void* act,
     } else {
     const int slices = launch_ksplit<DT>(kind, w, w, w, N, 0, N, K, act, act_ld, M, part, s);
     if (gain) {
-        auto rn = slices <= 4 ? resid_norm_kernel<DT, 4> : slices <= 12 ? resid_norm_kernel<DT, 12> : resid_norm_kernel<DT, 16>;
+        // loads in as few rounds as possible without many clamped (repeated) ones: 4 up to four slices,
+        // 16 for 13..16, 12 otherwise (23 slices: 12 + 11)
+        auto rn = slices <= 4                    ? resid_norm_kernel<DT, 4>
+                  : slices > 12 && slices <= 16 ? resid_norm_kernel<DT, 16>
+                                                 : resid_norm_kernel<DT, 12>;
         launchn(kind, rn, dim3(M), dim3(1024), 0, s, x, part, slices, M, N, gain, eps, y);
     } else {
         const long groups = (long)M * ((N + 3) / 4);
