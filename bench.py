@@ -58,9 +58,18 @@ class HipEvents:
                 arr[i] = e
         self.n = n
 
-    def elapsed_ms(self, i):
+    def elapsed_ms(self, i, j=None):
+        """Launch i's duration; with j, the time from launch i's start to launch j's end (events of one
+        device compare across streams)."""
         ms = ctypes.c_float()
-        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.stop[i])
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.stop[i if j is None else j])
+        assert rc == 0, rc
+        return ms.value
+
+    def start_ms(self, i, j):
+        """The time from launch i's start to launch j's start."""
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.start[i], self.start[j])
         assert rc == 0, rc
         return ms.value
 
@@ -587,7 +596,9 @@ def kernel_times(vs, run_step, n_steps, per_step_cap):
         n = vs.vs_timed_launches()
         vs.vs_time_kernel(0, None, None, 0)
         assert n < cap, f"{kind}: more launches than the event capacity"
-        out[kind] = {"launch_us": [ev.elapsed_ms(i) * 1e3 for i in range(n)]}
+        # each launch's interval from the pass's first start (launches of one kind may overlap on two streams)
+        out[kind] = {"launch_us": [ev.elapsed_ms(i) * 1e3 for i in range(n)],
+                     "interval_us": [(ev.start_ms(0, i) * 1e3, ev.elapsed_ms(0, i) * 1e3) for i in range(n)]}
         ev.close()
     return out
 
@@ -605,10 +616,24 @@ def weight_stream(dims, kt, n_steps):
             "timing": f"dispatch events of every product and slice-reduction launch in {n_steps} eager steps"}
 
 
+def busy_us(intervals):
+    """Length of the union of (start, end) intervals: launches that overlap count once."""
+    total, cur_s, cur_e = 0.0, None, None
+    for a, b in sorted(intervals):
+        if cur_e is None or a > cur_e:
+            if cur_e is not None:
+                total += cur_e - cur_s
+            cur_s, cur_e = a, b
+        else:
+            cur_e = max(cur_e, b)
+    return total + (cur_e - cur_s if cur_e is not None else 0.0)
+
+
 def attention_stream(kt, n_steps, kv_bytes):
     """Logical K/V bytes per step (every cached key and value the step's rows attend to, a prefix group's
-    shared pages once, plus the rows written) over the attention and merge kernels' time per step."""
-    us = (sum(kt["attn"]["launch_us"]) + sum(kt["merge"]["launch_us"])) / n_steps
+    shared pages once, plus the rows written) over the attention and merge kernels' time per step (the
+    union of the attention launches' intervals: two that run at once on two streams count once)."""
+    us = (busy_us(kt["attn"]["interval_us"]) + sum(kt["merge"]["launch_us"])) / n_steps
     gbps = kv_bytes / (us * 1e-6) / 1e9
     return {"kv_bytes_per_step": int(kv_bytes), "us_per_step": round(us, 2), "achieved": round(gbps, 1),
             "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)}
