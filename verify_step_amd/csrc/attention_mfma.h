@@ -62,8 +62,10 @@ __device__ __forceinline__ float4_t mma32(uint4 a, uint4 b, float4_t acc) {
 
 constexpr int kAmWaves = 4;
 constexpr int kAmDh = 128;
-constexpr int kAmPLd = 16 + 4;     // P tile row stride (elements)
-constexpr int kAmVLd = kAmDh + 8;  // V tile row stride (elements)
+constexpr int kAmPLd = 16;  // P tile row stride (elements): a half-wave's transposed read covers the banks once
+// V tile row stride (elements): 288 bytes, so consecutive rows start 8 banks apart and the eight
+// rows of a half-wave's transposed read (32 bytes each) cover the 64 banks once
+constexpr int kAmVLd = kAmDh + 16;
 
 // two 8-bit floats (bytes 0, 1 of a word, or 2, 3 with HI) widened to two storage-type elements packed
 // in one word. Every e4m3 and e5m2 value is exact in fp16 and in bf16, so no rounding is involved:
@@ -195,7 +197,7 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
     constexpr int KB = St<KVT>::bytes;
     const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q);
 
-    __shared__ __align__(16) uint16_t pt[kAmWaves][2][16 * kAmPLd];  // P hi / lo, [state][key]
+    __shared__ __align__(16) uint16_t pt[kAmWaves][2][16 * kAmPLd];  // P hi / lo, [key][state]
     __shared__ __align__(16) uint16_t vt[kAmWaves][16 * kAmVLd];     // V page, [key][dim]
     __shared__ float wst[kAmWaves][16][DH + 2];                      // per-wave (m, l, o) of each state
     __shared__ int srow[R], spos[R];  // a group block's row slots: q / output row (-1: none) and position
@@ -301,24 +303,34 @@ __global__ void __launch_bounds__(kAmWaves * 64, 2) attn_mfma_kernel(AttnArgs a)
 #pragma unroll
                 for (int t = 0; t < 8; ++t) o[t][r] *= alpha;
             }
-            // P as hi + lo storage-type terms, transposed: [state 4 kq + r][key l16]
+            // P as hi + lo storage-type terms, as the lane holds it: [key l16][states 4 kq .. +3], one 8-byte
+            // store per term
+            uint32_t hw[2], lw[2];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint16_t hi = St<DT>::from_f(pr[r]);
-                const uint16_t lo = St<DT>::from_f(pr[r] - St<DT>::to_f(hi));
-                my_p[(4 * kq + r) * kAmPLd + l16] = hi;
-                my_p[16 * kAmPLd + (4 * kq + r) * kAmPLd + l16] = lo;
+            for (int r = 0; r < 4; r += 2) {
+                const uint16_t h0 = St<DT>::from_f(pr[r]), h1 = St<DT>::from_f(pr[r + 1]);
+                const uint16_t l0 = St<DT>::from_f(pr[r] - St<DT>::to_f(h0));
+                const uint16_t l1 = St<DT>::from_f(pr[r + 1] - St<DT>::to_f(h1));
+                hw[r / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                lw[r / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
             }
+            *reinterpret_cast<uint2*>(my_p + l16 * kAmPLd + 4 * kq) = make_uint2(hw[0], hw[1]);
+            *reinterpret_cast<uint2*>(my_p + 16 * kAmPLd + l16 * kAmPLd + 4 * kq) = make_uint2(lw[0], lw[1]);
             __builtin_amdgcn_wave_barrier();  // the wave's LDS writes above come before its reads below
-            const uint2 ph = *reinterpret_cast<const uint2*>(my_p + l16 * kAmPLd + 4 * kq);
-            const uint2 pl = *reinterpret_cast<const uint2*>(my_p + 16 * kAmPLd + l16 * kAmPLd + 4 * kq);
+            // The transposing LDS read (gfx950) hands lane i of each 16-lane group, as element e, element
+            // i % 4 of the 8 bytes that lane 4 e + i / 4 of the group addressed. A operand P[state l16][keys
+            // 4 kq .. +3]: lane (kq, s) addresses [key 4 kq + s / 4][state 4 (s % 4)], so lane (kq, i)
+            // receives [key 4 kq + e][state i] as element e.
+            typedef __attribute__((address_space(3))) short4_t lds_short4;
+            lds_short4* prow = (lds_short4*)(my_p + (4 * kq + (l16 >> 2)) * kAmPLd + 4 * (l16 & 3));
+            const uint2 ph = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(prow));
+            const uint2 pl = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(prow + 16 * kAmPLd / 4));
+            // B operand V[keys 4 kq .. +3][dim 16 t + l16], by the same read: lane (kq, s) addresses
+            // V[4 kq + s / 4][16 t + 4 (s % 4)], and lane (kq, i) receives V[4 kq + e][16 t + i] as element e.
+            lds_short4* vrow = (lds_short4*)(my_v + (4 * kq + (l16 >> 2)) * kAmVLd + 4 * (l16 & 3));
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                // B operand: V[keys 4 kq .. +3][dim 16 t + l16]
-                const int d = 16 * t + l16;
-                const uint32_t v0 = my_v[(4 * kq + 0) * kAmVLd + d], v1 = my_v[(4 * kq + 1) * kAmVLd + d];
-                const uint32_t v2 = my_v[(4 * kq + 2) * kAmVLd + d], v3 = my_v[(4 * kq + 3) * kAmVLd + d];
-                const uint2 vb = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
+                const uint2 vb = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(vrow + 4 * t));
                 o[t] = mma16<DT>(ph, vb, o[t]);
                 o[t] = mma16<DT>(pl, vb, o[t]);
             }
